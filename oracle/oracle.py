@@ -1,0 +1,160 @@
+"""ctypes front end of the CPU oracle (test infrastructure only).
+
+Arrays are numpy arrays. Modes: MODE_F64 (fp64 parameters, gradients and
+moments; the parameter is its own master), MODE_F32 (the same in fp32) and
+MODE_MIXED (bf16 parameters and gradients as uint16 bit patterns, fp32 master,
+m and v). Every step function is functional: it returns new arrays and leaves
+its inputs untouched, as the problem statement's zero_step returns
+(new_param, new_states).
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import build_oracle
+
+MODE_F64, MODE_F32, MODE_MIXED = 0, 1, 2
+_PARAM_DT = {MODE_F64: np.float64, MODE_F32: np.float32, MODE_MIXED: np.uint16}
+_STATE_DT = {MODE_F64: np.float64, MODE_F32: np.float32, MODE_MIXED: np.float32}
+
+_i64, _i32, _dbl, _vp = C.c_int64, C.c_int, C.c_double, C.c_void_p
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _ptr_array(arrs):
+    return (C.c_void_p * len(arrs))(*[a.ctypes.data for a in arrs])
+
+
+class Oracle:
+    def __init__(self, path=None, mutant=0):
+        if path is None:
+            path = build_oracle.lib_path(mutant)
+            if not os.path.exists(path):
+                path = build_oracle.build(mutant)
+        self.path = path
+        lib = C.CDLL(path)
+        self.lib = lib
+        lib.orc_mutant.restype = _i32
+        lib.orc_split_bounds.argtypes = [_i64, _i64, _i64, C.POINTER(_i64), C.POINTER(_i64)]
+        lib.orc_owner.argtypes = [_i64, _i64, _i64]
+        lib.orc_owner.restype = _i64
+        lib.orc_bf16_round.argtypes = [_vp, _vp, _i64]
+        lib.orc_init_states.argtypes = [_i32, _i64, _vp, _vp, _vp, _vp]
+        step_args = [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                     _i64, _dbl, _dbl, _dbl, _dbl, _dbl, _vp]
+        for name in ("orc_zero_step", "orc_full_step"):
+            f = getattr(lib, name)
+            f.argtypes = step_args
+            f.restype = _i32
+        lib.orc_rank_step.argtypes = [_i32, _i64, _i64, _i64] + step_args[3:]
+        lib.orc_rank_step.restype = _i32
+        lib.orc_memory_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _i64, _i32,
+                                         C.POINTER(_i64)]
+        lib.orc_memory_bytes.restype = _i32
+
+    @property
+    def mutant(self):
+        return self.lib.orc_mutant()
+
+    # -- shards ---------------------------------------------------------------
+    def split_bounds(self, n, N, r):
+        a, b = _i64(), _i64()
+        self.lib.orc_split_bounds(n, N, r, C.byref(a), C.byref(b))
+        return a.value, b.value
+
+    def owner(self, n, N, i):
+        return self.lib.orc_owner(n, N, i)
+
+    # -- bf16 -----------------------------------------------------------------
+    def bf16_round(self, x):
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.orc_bf16_round(_ptr(x), _ptr(out), x.size)
+        return out
+
+    # -- states ---------------------------------------------------------------
+    def init_states(self, mode, param):
+        param = np.ascontiguousarray(param, dtype=_PARAM_DT[mode])
+        n = param.size
+        sdt = _STATE_DT[mode]
+        m = np.empty(n, sdt)
+        v = np.empty(n, sdt)
+        master = np.empty(n, np.float32) if mode == MODE_MIXED else None
+        self.lib.orc_init_states(mode, n, _ptr(param), _ptr(master), _ptr(m), _ptr(v))
+        return master, m, v
+
+    # -- steps ----------------------------------------------------------------
+    def _prep(self, mode, param, grads, master, m, v):
+        param = np.ascontiguousarray(param, dtype=_PARAM_DT[mode])
+        grads = [np.ascontiguousarray(g, dtype=_PARAM_DT[mode]) for g in grads]
+        sdt = _STATE_DT[mode]
+        m = np.ascontiguousarray(m, dtype=sdt)
+        v = np.ascontiguousarray(v, dtype=sdt)
+        if master is not None:
+            master = np.ascontiguousarray(master, dtype=np.float32 if mode == MODE_MIXED else sdt)
+        return param, grads, master, m, v
+
+    def _call_full(self, fn, mode, param, grads, master, m, v, t, lr, b1, b2, eps, wd, decay):
+        param, grads, master, m, v = self._prep(mode, param, grads, master, m, v)
+        n, N = param.size, len(grads)
+        for g in grads:
+            assert g.size == n
+        p_out = np.empty_like(param)
+        mst_out = np.empty(n, np.float32) if mode == MODE_MIXED else None
+        m_out, v_out = np.empty_like(m), np.empty_like(v)
+        dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.uint8)
+        rc = fn(mode, n, N, _ptr(param), _ptr_array(grads), _ptr(master), _ptr(m), _ptr(v),
+                _ptr(p_out), _ptr(mst_out), _ptr(m_out), _ptr(v_out), int(t), float(lr),
+                float(b1), float(b2), float(eps), float(wd), _ptr(dec))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return p_out, mst_out, m_out, v_out
+
+    def zero_step(self, mode, param, grads, master, m, v, t, lr, b1=0.9, b2=0.999,
+                  eps=1e-8, wd=0.0, decay=None):
+        """The sharded step over all N workers. Returns (param, master, m, v)."""
+        return self._call_full(self.lib.orc_zero_step, mode, param, grads, master, m, v,
+                               t, lr, b1, b2, eps, wd, decay)
+
+    def full_step(self, mode, param, grads, master, m, v, t, lr, b1=0.9, b2=0.999,
+                  eps=1e-8, wd=0.0, decay=None):
+        """Shard-free Adam on the full vector with the mean gradient."""
+        return self._call_full(self.lib.orc_full_step, mode, param, grads, master, m, v,
+                               t, lr, b1, b2, eps, wd, decay)
+
+    def rank_step(self, mode, N, r, param, chunk_grads, master, m, v, t, lr, b1=0.9,
+                  b2=0.999, eps=1e-8, wd=0.0, decay=None):
+        """Worker r's share: chunk gradients and shard-local master/m/v.
+
+        Returns (full gathered param, master chunk, m chunk, v chunk)."""
+        param, chunk_grads, master, m, v = self._prep(mode, param, chunk_grads, master, m, v)
+        n = param.size
+        a, b = self.split_bounds(n, N, r)
+        c = b - a
+        assert len(chunk_grads) == N
+        for g in chunk_grads:
+            assert g.size == c
+        assert master is not None and master.size == c and m.size == c and v.size == c
+        p_out = np.empty_like(param)
+        mst_out, m_out, v_out = np.empty_like(master), np.empty_like(m), np.empty_like(v)
+        dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.uint8)
+        rc = self.lib.orc_rank_step(mode, n, N, r, _ptr(param), _ptr_array(chunk_grads),
+                                    _ptr(master), _ptr(m), _ptr(v), _ptr(p_out), _ptr(mst_out),
+                                    _ptr(m_out), _ptr(v_out), int(t), float(lr), float(b1),
+                                    float(b2), float(eps), float(wd), _ptr(dec))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return p_out, mst_out, m_out, v_out
+
+    # -- memory ---------------------------------------------------------------
+    def memory_bytes(self, n, N, r, stage, P, G, K, convention=0):
+        out = (_i64 * 3)()
+        rc = self.lib.orc_memory_bytes(n, N, r, stage, P, G, K, convention, out)
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return {"params": out[0], "grads": out[1], "optimizer": out[2],
+                "total": out[0] + out[1] + out[2]}
