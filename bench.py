@@ -1,0 +1,228 @@
+"""Benchmark of the fused ZeRO-sharded Adam step on one MI355X.
+
+A step is one call of zero_step over one batch of resident synthetic inputs:
+the reduce-scatter mean over N logical workers' gradients, Adam/AdamW on every
+shard, and the all-gather write-back, in one kernel launch. Inputs are
+generated on the device before the timed region; the timed region covers K
+steps (t = W+1 .. W+K) bracketed by device synchronisation.
+
+Prints one JSON line: throughput in parameters updated per second over the
+whole timed region, the HBM roofline of the step kernel (algorithmic bytes per
+launch over the mean launch duration, measured with HIP events on the stream
+the kernel runs on), and the CPU oracle timed on a bounded sample of the same
+workload on this host.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("params updated/sec + achieved HBM GB/s (% of peak), fused ZeRO Adam step, 1 GPU")
+DEFAULT_WORKLOAD = "fp32-320M-n8"
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
+KERNEL_SRC = os.path.join(ROOT, "zero_sharded_optimizer_amd", "csrc", "zero_kernels.hip")
+
+
+def bytes_per_param(wl):
+    """Algorithmic HBM bytes per updated parameter: every worker's gradient read
+    once; master (or in-place parameter), m and v read once and written once; the
+    gathered parameter written once when it is a separate buffer (bf16 in mixed
+    mode, the rank's slot in rank mode); one decay-mask bit when a mask is used."""
+    from zero_sharded_optimizer_amd import synth
+    g = {0: 8, 1: 4, 2: 2}[wl.mode]
+    s = 8 if wl.mode == 0 else 4
+    p = g
+    b = wl.n_workers * g + 6 * s
+    if wl.mode == 2 or wl.rank >= 0:
+        b += p
+    if synth.decay_flags(wl) is not None:
+        b += 1 / 8
+    return b
+
+
+def kernel_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload, algo_bytes):
+    """HBM bytes per launch measured by rocprofv3 counters, if a summary for
+    this workload was taken from the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_src_sha256_16") != kernel_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(wl, target_s=12.0, sample_n=1 << 22):
+    """The CPU oracle (single-threaded, as it stands) on the first sample_n
+    elements of the same workload, stepped until about target_s seconds."""
+    import numpy as np
+    import torch
+    from oracle import Oracle
+    from zero_sharded_optimizer_amd import synth
+    O = Oracle()
+    small = synth.scaled(wl, min(sample_n, wl.length), rank=-1, shapes=())
+    if wl.rank >= 0:
+        small = synth.scaled(wl, min(sample_n, wl.length), rank=-1, shapes=(), decay="all")
+    n = small.n
+
+    def host(x):
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+        return x.cpu().numpy().copy()
+
+    param = host(synth.make_params(small, "cuda")[0])
+    grads = [host(g) for g in synth.make_grads(small, 1, "cuda")]
+    mst, m, v = O.init_states(small.mode, param)
+    dec = None
+    if wl.decay == "2d":
+        dec = synth.decay_flags(wl)[:n].astype(np.uint8)
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        param, mst, m, v = O.zero_step(small.mode, param, grads, mst, m, v, steps + 1, small.lr,
+                                       small.beta1, small.beta2, small.eps, small.weight_decay,
+                                       dec)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= target_s:
+            break
+    return {"value": n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {n} elements of the workload, {wl.n_workers} workers, {steps} "
+                      f"steps, single-threaded C++ oracle, {el:.1f} s"}
+
+
+def copy_ceiling(nbytes=4 << 30, reps=10):
+    """A plain device copy of nbytes: read + write bytes over the time, GB/s."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    s.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / reps
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (all logical workers live in one GPU's HBM); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import zero_sharded_optimizer_amd as z
+    from zero_sharded_optimizer_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    a, b = wl.shard
+    L = b - a
+
+    # resident inputs
+    param, master0 = synth.make_params(wl, "cuda")
+    sdt = synth.state_dtype(wl)
+    need_master = wl.mode == 2 or wl.rank >= 0
+    st = z.States(torch.empty(L, dtype=sdt, device="cuda") if need_master else None,
+                  torch.empty(L, dtype=sdt, device="cuda"), torch.empty(L, dtype=sdt, device="cuda"))
+    flags = synth.decay_flags(wl)
+    mask = z.wd_mask_from_flags(flags) if flags is not None else None
+    hp = z.HParams(n=wl.n, n_workers=wl.n_workers, mode=wl.mode, lr=wl.lr, beta1=wl.beta1,
+                   beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay, rank=wl.rank,
+                   wd_mask=mask)
+    z.zero_init_states(hp, param, st)
+    if master0 is not None:
+        st.master.copy_(master0)
+        param[a:b].copy_(master0.to(param.dtype))
+        del master0
+    grads = synth.make_grads(wl, 1, "cuda")
+    torch.cuda.synchronize()
+
+    for t in range(1, args.warmup + 1):
+        z.zero_step(hp, param, grads, st, t)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        z.zero_step(hp, param, grads, st, args.warmup + 1 + i, stream=stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [s.elapsed_time(e) for s, e in ev]
+    avg_ms = sum(kern_ms) / len(kern_ms)
+
+    bpp = bytes_per_param(wl)
+    algo_bytes = bpp * L
+    achieved = algo_bytes / (avg_ms * 1e-3) / 1e9
+    traffic = load_traffic(wl.name, algo_bytes)
+    dtype = {0: "f64", 1: "f32", 2: "bf16+f32"}[wl.mode]
+
+    del grads, param, st
+    torch.cuda.empty_cache()
+    copy_gbps = None if args.no_copy_ceiling else copy_ceiling()
+    cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+
+    out = {
+        "metric": METRIC,
+        "value": L * args.steps / wall,
+        "unit": "params/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded device-side draws; no dataset)",
+        "config": {"workload": wl.name, "params_updated_per_step": L, "n_workers": wl.n_workers,
+                   "mode": dtype, "rank": wl.rank, "lr": wl.lr, "betas": [wl.beta1, wl.beta2],
+                   "eps": wl.eps, "weight_decay": wl.weight_decay, "decay": wl.decay,
+                   "bytes_per_param": bpp, "parallelism": "1 GPU, N logical workers in one HBM"},
+        "achieved_GBps": achieved,
+        "kernel_ms_mean": avg_ms,
+        "kernel_ms_min": min(kern_ms),
+        "copy_ceiling_GBps": copy_gbps,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,199 @@
+/*
+ * zero_adam.h: C ABI of the fused ZeRO-sharded Adam step for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation is the one defined by "ZeRO-Sharded Adam Step"
+ * (scratchllm.com/problems/zero-sharded-optimizer), sections "The step", "The
+ * shards" and "What to implement": N workers hold full-length local gradients;
+ * the parameter indices are split into N shards by np.array_split; (1) a
+ * reduce-scatter gives worker r the mean over all workers of the gradient on
+ * its shard only, (2) worker r runs Adam on its shard with its own m and v,
+ * (3) an all-gather leaves the full updated parameter vector on every worker.
+ * Per "Requirements" the result equals ordinary Adam on the full vector with
+ * the mean gradient. Stages and memory follow "Data parallelism and ZeRO
+ * stages 1 to 3" (openlearn L11.3), sections "2. Principles" and "4. The
+ * interface".
+ *
+ * On one GPU every logical worker lives in the same HBM, so the reduce-scatter
+ * is a local sum over N gradient buffers (in rank order, left to right) and the
+ * all-gather is the store into the one gathered parameter buffer. The whole
+ * step is one kernel launch that streams each byte through HBM once.
+ *
+ * Per element, in the state type S (double in fp64 mode, float otherwise),
+ * each operation one IEEE round-to-nearest-even operation, never fused:
+ *     gb  = (g_0 + g_1 + ... + g_{N-1}) / N
+ *     m   = b1*m + (1-b1)*gb
+ *     v   = b2*v + (1-b2)*(gb*gb)
+ *     mh  = m / (1-b1^t);   vh = v / (1-b2^t)
+ *     den = sqrt(vh) + eps
+ *     w   = w * (1 - lr*wd)                  where decay applies
+ *     w   = w - lr*(mh/den)
+ * 1-b1, 1-b2, 1-b1^t, 1-b2^t and 1-lr*wd are formed in double on the host and
+ * rounded once to S. In mixed mode the gathered parameter is the bf16
+ * round-to-nearest-even of w (NaN stored as 0x7FC0).
+ *
+ * Conventions shared by every function:
+ *   - All device buffers are owned by the caller; the library never allocates,
+ *     frees or keeps device memory, and keeps no pointer after a call returns.
+ *   - Device work is enqueued on `stream` (a hipStream_t; NULL is the null
+ *     stream) and runs asynchronously; synchronisation is the caller's job.
+ *     Calls that overlap in time on buffers they both write race.
+ *   - Every argument is validated on the host before any HIP call; a rejected
+ *     call enqueues nothing. No exception crosses the ABI.
+ *   - A non-OK status leaves a message for zero_last_error() in the calling
+ *     thread.
+ */
+#ifndef ZERO_ADAM_H
+#define ZERO_ADAM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZERO_OK = 0,
+  ZERO_EINVAL = -1,       /* a bad argument; nothing was enqueued */
+  ZERO_EUNSUPPORTED = -2, /* valid, but outside what this library implements */
+  ZERO_EHIP = -3          /* the HIP runtime reported an error at launch */
+} zero_status;
+
+typedef enum {
+  /* fp64 parameters, gradients, m and v; the parameter is its own master. */
+  ZERO_MODE_F64 = 0,
+  /* fp32 parameters, gradients, m and v (K = 8 optimizer bytes per parameter,
+   * "ZeRO One: Sharding the Optimizer", section "Training Memory
+   * Requirements"); the parameter is its own master. */
+  ZERO_MODE_F32 = 1,
+  /* bf16 parameters and gradients, fp32 master, m and v (K = 12, same section;
+   * "Data Parallelism & ZeRO", section "ZeRO, stage by stage"). */
+  ZERO_MODE_MIXED_BF16 = 2
+} zero_mode;
+
+/* Largest number of workers one zero_step call accepts (the gradient pointers
+ * travel in the kernel's argument block). zero_shard_bounds and
+ * zero_memory_bytes accept any N >= 1. */
+#define ZERO_MAX_WORKERS 256
+
+/* Hyperparameters and the shape of one call. There are no hidden defaults:
+ * every field is used as given ("Data parallelism and ZeRO stages 1 to 3",
+ * section "5. Pitfalls", dropped hyperparameters). */
+typedef struct {
+  int64_t n;         /* parameters in the gathered vector; >= 1 */
+  int32_t n_workers; /* N, 1 <= N <= ZERO_MAX_WORKERS for zero_step; N > n is
+                        allowed and gives trailing empty shards */
+  int32_t rank;      /* -1: every worker's share in this call (full mode);
+                        0..N-1: only worker `rank`'s share (rank mode) */
+  int32_t mode;      /* a zero_mode */
+  int32_t reserved;  /* must be 0 */
+  double lr;         /* finite */
+  double beta1;      /* in [0, 1) */
+  double beta2;      /* in [0, 1) */
+  double eps;        /* finite, > 0 */
+  double weight_decay; /* finite, >= 0; 0 disables decay */
+  /* Optional device bitmask over the global index space [0, n): element i
+   * decays iff bit (i % 32) of word i / 32 is set. It must hold at least
+   * (n + 31) / 32 readable words and be 4-byte aligned. NULL: every element
+   * decays when weight_decay > 0. Ignored when weight_decay == 0. */
+  const uint32_t* wd_mask;
+} zero_hparams;
+
+/* Optimizer state, caller-owned device buffers, each 16-byte aligned.
+ *   Full mode (rank == -1): m and v hold n elements of S; worker r's shard is
+ *     the view [a_r, b_r) of each (the N per-worker (m_shard, v_shard) pairs of
+ *     "What to implement", laid back to back). master holds n fp32 values in
+ *     mixed mode and must be NULL in fp64/fp32 mode, where the parameter is
+ *     updated in place and is its own master.
+ *   Rank mode (rank == r): m, v and master each hold c_r = b_r - a_r elements
+ *     of S: only worker r's shard. master is required in every mode (the rank's
+ *     master copy of its chunk, "Data parallelism and ZeRO stages 1 to 3",
+ *     section "2. Principles", stage 1). */
+typedef struct {
+  void* master;
+  void* m;
+  void* v;
+} zero_states;
+
+/* init_states ("What to implement"): zero m and v, and set the master copy
+ * from the parameters (exact bf16 -> fp32 widening in mixed mode, a copy in
+ * rank mode's fp64/fp32 master). `param` is the gathered parameter vector of n
+ * elements (bf16 in mixed mode, else S), read-only; in rank mode only
+ * [a_r, b_r) of it is read. Enqueued on `stream`. An empty rank shard
+ * enqueues nothing and touches no buffer (they may be NULL). Errors as for
+ * zero_step, without the step scalars and t. */
+zero_status zero_init_states(const zero_hparams* hp, const void* param,
+                             const zero_states* states, void* stream);
+
+/* zero_step ("What to implement"; "The step" items 1-3): one fused step.
+ *   param: the gathered parameter vector, n elements (bf16 in mixed mode,
+ *     else S), updated in place. Full mode: every element is rewritten; it
+ *     must be 16-byte aligned. Rank mode: only [a_r, b_r) is written; it must
+ *     be aligned to its element size.
+ *   grads: host array of N device pointers, in rank order, read-only, each
+ *     16-byte aligned (elements of G = bf16 in mixed mode, else S). Full mode:
+ *     worker k's full local gradient, n elements. Rank mode: the chunk
+ *     g_k[a_r:b_r) that worker k contributes to shard r, c_r elements.
+ *     Gradient buffers may alias one another but not any buffer the step
+ *     writes.
+ *   states: as described at zero_states; updated in place.
+ *   t: the 1-based step number ("What to implement"); t < 1 is rejected.
+ * Rank mode with an empty shard (c_r == 0) is valid and enqueues nothing; then
+ * no buffer is touched and param, grads and states may be NULL (the scalar
+ * arguments and t are still checked).
+ * Errors: ZERO_EINVAL for a null or misaligned pointer, overlapping written
+ * ranges, n < 1, N outside [1, ZERO_MAX_WORKERS], rank outside [-1, N), t < 1,
+ * a non-finite scalar, a beta outside [0, 1), eps <= 0, weight_decay < 0, a
+ * mode/master mismatch, or reserved != 0; ZERO_EHIP if the launch fails. */
+zero_status zero_step(const zero_hparams* hp, void* param, const void* const* grads,
+                      const zero_states* states, int64_t t, void* stream);
+
+/* Per-rank memory in bytes ("Data parallelism and ZeRO stages 1 to 3",
+ * section "2. Principles", table and "Your emulation's bookkeeping"; "Data
+ * Parallelism & ZeRO", section "ZeRO, stage by stage"; "Data parallelism and
+ * ZeRO optimization", sections "Memory Consumption Analysis" and "ZeRO-1/2/3";
+ * "ZeRO One: Sharding the Optimizer", section "Training Memory Requirements"). */
+typedef struct {
+  int64_t params;
+  int64_t grads;
+  int64_t optimizer;
+  int64_t total; /* params + grads + optimizer */
+} zero_mem;
+
+/* Host-only; touches no device. Rank `rank` of N holds the chunk of
+ * c = b_r - a_r elements. Widths by mode (params P, gradient G, optimizer K
+ * bytes per parameter): mixed 2, 2, 12; fp32 4, 4, 8; fp64 8, 8, 16.
+ *   convention 0 (the closed forms):
+ *     stage 0 (plain data parallelism): P n,  G n,  K n
+ *     stage 1 (optimizer state sharded): P n,  G n,  K c
+ *     stage 2 (+ gradients sharded):     P n,  G c,  K c
+ *     stage 3 (+ parameters sharded):    P c,  G c,  K c
+ *   convention 1 (the emulation's bookkeeping of the L11.3 byte table, one
+ *   value width B = P; fp64 and fp32 modes only):
+ *     stage 0 (one process): B n,  B n,        2 B n
+ *     stage 1: B n,  B n + B c,  3 B c   (moments + master chunk; full mean
+ *              gradients kept in .grad plus the chunk's gradient)
+ *     stage 2: B n,  B c,        3 B c
+ *     stage 3: B c,  B c,        2 B c   (the chunk is the parameter storage)
+ * Errors: ZERO_EINVAL for n < 1, N < 1, rank outside [0, N), stage outside
+ * [0, 3], an unknown mode or convention, or a NULL out; ZERO_EUNSUPPORTED for
+ * convention 1 in mixed mode. */
+zero_status zero_memory_bytes(int64_t n, int32_t n_workers, int32_t rank, int32_t stage,
+                              int32_t mode, int32_t convention, zero_mem* out);
+
+/* Shard r of np.array_split(np.arange(n), N) as the half-open range
+ * [*begin, *end) ("ZeRO-Sharded Adam Step", section "The shards"): the first
+ * n mod N shards hold floor(n/N) + 1 indices, the rest floor(n/N). Host-only.
+ * n >= 0 (n == 0 gives empty shards), N >= 1, 0 <= r < N; else ZERO_EINVAL. */
+zero_status zero_shard_bounds(int64_t n, int32_t n_workers, int32_t r, int64_t* begin,
+                              int64_t* end);
+
+/* The calling thread's message for its last non-OK status ("" if none). The
+ * pointer stays valid until the thread's next call into the library. */
+const char* zero_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ZERO_ADAM_H */

@@ -1,0 +1,162 @@
+"""Drivers shared by the GPU parity tests: run the fused step through the C ABI
+and the CPU oracle on the same seeded inputs, and compare with the parity bar
+of oracle/compare.py."""
+import numpy as np
+
+import zero_sharded_optimizer_amd as z
+from zero_sharded_optimizer_amd import synth
+from oracle import MODE_F64, MODE_MIXED
+from oracle.compare import compare
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def host(x):
+    import torch
+    if x.dtype == torch.bfloat16:
+        return x.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+    return x.cpu().numpy().copy()
+
+
+def kinds(wl):
+    """(param kind, state kind) of the parity bar for a workload's mode."""
+    if wl.mode == MODE_F64:
+        return "exact", "exact"
+    if wl.mode == MODE_MIXED:
+        return "bf16", "f32"
+    return "f32", "f32"
+
+
+def hparams(wl, mask=None):
+    return z.HParams(n=wl.n, n_workers=wl.n_workers, mode=wl.mode, lr=wl.lr, beta1=wl.beta1,
+                     beta2=wl.beta2, eps=wl.eps, weight_decay=wl.weight_decay, rank=wl.rank,
+                     wd_mask=mask)
+
+
+def setup(wl):
+    """Device buffers for a workload, initialised as the step expects."""
+    import torch
+    param, master0 = synth.make_params(wl, "cuda")
+    a, b = wl.shard
+    L = b - a
+    sdt = synth.state_dtype(wl)
+    flags = synth.decay_flags(wl)
+    mask = z.wd_mask_from_flags(flags) if flags is not None else None
+    need_master = wl.mode == MODE_MIXED or wl.rank >= 0
+    st = z.States(master=torch.empty(L, dtype=sdt, device="cuda") if need_master else None,
+                  m=torch.empty(L, dtype=sdt, device="cuda"),
+                  v=torch.empty(L, dtype=sdt, device="cuda"))
+    hp = hparams(wl, mask)
+    z.zero_init_states(hp, param, st)
+    if master0 is not None:
+        # rank mode: the rank's master is drawn directly; its gathered slot holds
+        # the rounding of that master, as after an earlier step
+        st.master.copy_(master0)
+        param[a:b].copy_(master0.to(param.dtype))
+    return hp, param, st, flags
+
+
+def check_all(tag, wl, param_d, st, ref):
+    """ref = (param, master, m, v) from the oracle; returns the stats list."""
+    pk, sk = kinds(wl)
+    p_ref, mst_ref, m_ref, v_ref = ref
+    out = [compare(f"{tag} param", param_d, p_ref, pk),
+           compare(f"{tag} m", host(st.m) if not isinstance(st.m, np.ndarray) else st.m, m_ref, sk),
+           compare(f"{tag} v", host(st.v) if not isinstance(st.v, np.ndarray) else st.v, v_ref, sk)]
+    if mst_ref is not None:
+        mst = st.master if isinstance(st.master, np.ndarray) else host(st.master)
+        out.append(compare(f"{tag} master", mst, mst_ref, sk))
+    return out
+
+
+def run_full(O, wl, steps, compare_every=1):
+    """Every element compared, every `compare_every` steps and at the end."""
+    import torch
+    say(f"[case] full compare {wl.name}: mode={wl.mode} n={wl.n} N={wl.n_workers} "
+        f"rank={wl.rank} steps={steps}")
+    hp, param, st, flags = setup(wl)
+    dec = None if flags is None else flags.astype(np.uint8)
+    a, b = wl.shard
+    p_h = host(param)
+    m_h, v_h = host(st.m), host(st.v)
+    mst_h = host(st.master) if st.master is not None else None
+    assert not m_h.any() and not v_h.any()
+    stats = []
+    for t in range(1, steps + 1):
+        grads = synth.make_grads(wl, t, "cuda")
+        g_h = [host(g) for g in grads]
+        z.zero_step(hp, param, grads, st, t)
+        if wl.rank < 0:
+            p_h, mst_h, m_h, v_h = O.zero_step(wl.mode, p_h, g_h, mst_h, m_h, v_h, t, wl.lr,
+                                               wl.beta1, wl.beta2, wl.eps, wl.weight_decay, dec)
+        else:
+            p_h, mst_h, m_h, v_h = O.rank_step(wl.mode, wl.n_workers, wl.rank, p_h, g_h, mst_h,
+                                               m_h, v_h, t, wl.lr, wl.beta1, wl.beta2, wl.eps,
+                                               wl.weight_decay, dec)
+        if t % compare_every == 0 or t == steps:
+            torch.cuda.synchronize()
+            stats = check_all(f"{wl.name} t={t}", wl, host(param), st,
+                              (p_h, mst_h if st.master is not None else None, m_h, v_h))
+            # gradients are read-only
+            for k in (0, wl.n_workers - 1):
+                assert np.array_equal(host(grads[k]).view(np.uint8), g_h[k].view(np.uint8))
+    say(f"[done] {wl.name}: " + "; ".join(
+        f"{s['name'].split()[-1]} bitexact {s['bitexact']}/{s['n']} max_ulp {s['max_ulp']}"
+        for s in stats))
+    return stats
+
+
+def run_sampled(O, wl, steps, count, compare_steps=None):
+    """Full-size workload, compared on a sampled index set (exact per element,
+    because the step is elementwise)."""
+    import torch
+    say(f"[case] sampled compare {wl.name}: mode={wl.mode} n={wl.n} N={wl.n_workers} "
+        f"rank={wl.rank} steps={steps}")
+    hp, param, st, flags = setup(wl)
+    a, b = wl.shard
+    idx = synth.sample_indices(wl, count)
+    idx_d = torch.from_numpy(idx).to("cuda")
+    gidx_d = idx_d + a
+    dec = None if flags is None else flags[idx + a].astype(np.uint8)
+    if wl.decay == "all":
+        dec = None
+    p_h = host(param[gidx_d])
+    m_h, v_h = host(st.m[idx_d]), host(st.v[idx_d])
+    mst_h = host(st.master[idx_d]) if st.master is not None else None
+    outside = None
+    if wl.rank >= 0:
+        rng = np.random.default_rng(3)
+        pool = np.concatenate([np.arange(0, a), np.arange(b, wl.n)]) if wl.n < 10 ** 7 else None
+        if pool is not None and pool.size:
+            outside = rng.choice(pool, min(4096, pool.size), replace=False)
+        elif pool is None:
+            cand = rng.integers(0, wl.n, 8192)
+            outside = cand[(cand < a) | (cand >= b)][:4096]
+        outside_d = torch.from_numpy(np.asarray(outside, np.int64)).to("cuda")
+        outside_before = host(param[outside_d])
+    steps_to_compare = set(compare_steps or range(1, steps + 1)) | {steps}
+    stats = []
+    for t in range(1, steps + 1):
+        grads = synth.make_grads(wl, t, "cuda")
+        z.zero_step(hp, param, grads, st, t)
+        g_h = [host(g[idx_d]) for g in grads]
+        del grads
+        p_h, mst_h, m_h, v_h = O.full_step(wl.mode, p_h, g_h, mst_h, m_h, v_h, t, wl.lr, wl.beta1,
+                                           wl.beta2, wl.eps, wl.weight_decay, dec)
+        if t in steps_to_compare:
+            torch.cuda.synchronize()
+            dev = z.States(master=host(st.master[idx_d]) if st.master is not None else None,
+                           m=host(st.m[idx_d]), v=host(st.v[idx_d]))
+            stats = check_all(f"{wl.name} t={t}", wl, host(param[gidx_d]), dev,
+                              (p_h, mst_h, m_h, v_h))
+            say(f"  t={t}: {len(idx)} sampled elements within the bar")
+    if outside is not None:
+        assert np.array_equal(host(param[outside_d]).view(np.uint8), outside_before.view(np.uint8))
+    say(f"[done] {wl.name}: " + "; ".join(
+        f"{s['name'].split()[-1]} bitexact {s['bitexact']}/{s['n']} max_ulp {s['max_ulp']}"
+        for s in stats))
+    del param, st
+    torch.cuda.empty_cache()
+    return stats

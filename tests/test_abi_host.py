@@ -1,0 +1,251 @@
+"""The C-ABI library on the host, no GPU: it loads, exports every function
+include/zero_adam.h declares, and its host logic (shard bounds, memory model,
+argument validation) is right. No call here reaches a kernel launch."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import zero_sharded_optimizer_amd as z
+from zero_sharded_optimizer_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+A = 1 << 32  # fake, 16-byte aligned "device" addresses: never dereferenced here
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            txt = open(os.path.join(ROOT, "include", fn)).read()
+            txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(zero_\w+)\s*\(", txt, flags=re.M)
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = _abi.load()
+    names = declared_functions()
+    assert set(names) >= set(_abi.EXPORTED)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_header_is_plain_c():
+    txt = open(os.path.join(ROOT, "include", "zero_adam.h")).read()
+    assert 'extern "C"' in txt and "torch" not in txt.lower().replace("torch's", "")
+
+
+# -- shard bounds -------------------------------------------------------------
+def test_shard_bounds_match_numpy_array_split():
+    for n in list(range(0, 60)) + [1_048_579, 124_439_808, 8_000_000_000]:
+        for N in (1, 2, 3, 4, 5, 7, 8, 64, 70):
+            if n > 10 ** 7:
+                sizes = [n // N + (1 if r < n % N else 0) for r in range(N)]
+            else:
+                sizes = [len(p) for p in np.array_split(np.arange(n), N)]
+            start = 0
+            for r in range(N):
+                assert z.zero_shard_bounds(n, N, r) == (start, start + sizes[r])
+                start += sizes[r]
+
+
+def test_shard_bounds_match_oracle(oracle):
+    rng = np.random.default_rng(1)
+    for _ in range(2000):
+        n = int(rng.integers(0, 10 ** 12))
+        N = int(rng.integers(1, 300))
+        r = int(rng.integers(0, N))
+        assert z.zero_shard_bounds(n, N, r) == oracle.split_bounds(n, N, r)
+
+
+@pytest.mark.parametrize("args", [(-1, 2, 0), (10, 0, 0), (10, 2, 2), (10, 2, -1)])
+def test_shard_bounds_rejects(args):
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_shard_bounds(*args)
+    assert e.value.status == z.ZERO_EINVAL and e.value.message
+
+
+# -- memory model -------------------------------------------------------------
+WIDTH = {z.ZERO_MODE_MIXED_BF16: (2, 2, 12), z.ZERO_MODE_F32: (4, 4, 8), z.ZERO_MODE_F64: (8, 8, 16)}
+
+
+def test_memory_bytes_agrees_with_oracle(oracle):
+    rng = np.random.default_rng(2)
+    for _ in range(3000):
+        n = int(rng.integers(1, 10 ** 11))
+        N = int(rng.integers(1, 100))
+        r = int(rng.integers(0, N))
+        stage = int(rng.integers(0, 4))
+        mode = int(rng.integers(0, 3))
+        P, G, K = WIDTH[mode]
+        got = z.zero_memory_bytes(n, N, r, stage, mode, 0)
+        assert got == oracle.memory_bytes(n, N, r, stage, P, G, K, 0)
+        if mode != z.ZERO_MODE_MIXED_BF16:
+            got = z.zero_memory_bytes(n, N, r, stage, mode, 1)
+            assert got == oracle.memory_bytes(n, N, r, stage, P, G, K, 1)
+
+
+def test_memory_bytes_byte_table():
+    """openlearn L11.3, section '3. Worked example by hand': the byte table."""
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "p1_worked_example.json")))
+    for key, exp in g["byte_table"].items():
+        if key == "one_process":
+            got = z.zero_memory_bytes(10, 4, 0, 0, z.ZERO_MODE_F64, 1)
+        else:
+            stage, rank = int(key[5]), int(key[-1])
+            got = z.zero_memory_bytes(10, 4, rank, stage, z.ZERO_MODE_F64, 1)
+        assert {k: got[k] for k in exp} == exp, key
+
+
+def test_memory_bytes_closed_forms():
+    """Data Parallelism & ZeRO, section 'ZeRO, stage by stage': 16, 4 + 12/N,
+    2 + 14/N, 16/N bytes per parameter; an 8B model on 8 GPUs at 120/41/28/15 GiB."""
+    n = 8_000_000_000
+    gib = [z.zero_memory_bytes(n, 8, 0, s, z.ZERO_MODE_MIXED_BF16)["total"] / 2 ** 30 for s in range(4)]
+    assert [float(f"{x:.2g}") for x in gib] == [120, 41, 28, 15]
+    for N in (2, 8, 64):
+        m = 64_000
+        for s, (lead, tail) in {1: (4, 12), 2: (2, 14), 3: (0, 16)}.items():
+            assert z.zero_memory_bytes(m, N, N - 1, s, z.ZERO_MODE_MIXED_BF16)["total"] * N == (lead * N + tail) * m
+    assert z.zero_memory_bytes(320_000_000, 1, 0, 0, z.ZERO_MODE_F32)["total"] == 5_120_000_000
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 4, 0, 1, 0, 0), z.ZERO_EINVAL),      # no parameters
+    ((10, 0, 0, 1, 0, 0), z.ZERO_EINVAL),
+    ((10, 4, 4, 1, 0, 0), z.ZERO_EINVAL),
+    ((10, 4, 0, 4, 0, 0), z.ZERO_EINVAL),     # stage 4
+    ((10, 4, 0, -1, 0, 0), z.ZERO_EINVAL),
+    ((10, 4, 0, 1, 3, 0), z.ZERO_EINVAL),     # unknown mode
+    ((10, 4, 0, 1, 0, 2), z.ZERO_EINVAL),     # unknown convention
+    ((10, 4, 0, 1, 2, 1), z.ZERO_EUNSUPPORTED),
+])
+def test_memory_bytes_rejects(args, status):
+    with pytest.raises(z.ZeroError) as e:
+        z.zero_memory_bytes(*args)
+    assert e.value.status == status
+
+
+# -- step / init validation (rejected before any HIP call) ---------------------
+def _hp(**kw):
+    d = dict(n=1000, n_workers=4, rank=-1, mode=z.ZERO_MODE_F32, reserved=0, lr=1e-3, beta1=0.9,
+             beta2=0.999, eps=1e-8, weight_decay=0.0, wd_mask=None)
+    d.update(kw)
+    return _abi.zero_hparams(**d)
+
+
+def _call_step(hp, param=A, grads=None, master=None, m=A + (1 << 24), v=A + (2 << 24), t=1):
+    lib = _abi.load()
+    if grads is None:
+        grads = [A + ((3 + k) << 24) for k in range(hp.n_workers)]
+    arr = (C.c_void_p * max(1, len(grads)))(*grads)
+    st = _abi.zero_states(master=master, m=m, v=v)
+    rc = lib.zero_step(C.byref(hp), param, arr, C.byref(st), t, None)
+    return rc, lib.zero_last_error().decode()
+
+
+BAD_STEPS = {
+    "no parameters": (dict(n=0), {}),
+    "zero workers": (dict(n_workers=0), {}),
+    "too many workers": (dict(n_workers=257), {}),
+    "rank too large": (dict(rank=4), {}),
+    "rank below -1": (dict(rank=-2), {}),
+    "unknown mode": (dict(mode=7), {}),
+    "reserved": (dict(reserved=1), {}),
+    "t = 0": ({}, dict(t=0)),
+    "beta1 = 1": (dict(beta1=1.0), {}),
+    "beta2 < 0": (dict(beta2=-0.1), {}),
+    "eps = 0": (dict(eps=0.0), {}),
+    "lr nan": (dict(lr=float("nan")), {}),
+    "lr inf": (dict(lr=float("inf")), {}),
+    "wd < 0": (dict(weight_decay=-0.1), {}),
+    "wd nan": (dict(weight_decay=float("nan")), {}),
+    "mask misaligned": (dict(weight_decay=0.1, wd_mask=A + 2), {}),
+    "null param": ({}, dict(param=None)),
+    "misaligned param": ({}, dict(param=A + 4)),
+    "null m": ({}, dict(m=None)),
+    "misaligned v": ({}, dict(v=A + (2 << 24) + 8)),
+    "master in full fp32": ({}, dict(master=A + (9 << 24))),
+    "master missing in mixed": (dict(mode=z.ZERO_MODE_MIXED_BF16), {}),
+    "master missing in rank mode": (dict(rank=1), {}),
+    "misaligned master": (dict(mode=z.ZERO_MODE_MIXED_BF16), dict(master=A + (9 << 24) + 4)),
+    "null grad": ({}, dict(grads=[A + (3 << 24), None, A + (5 << 24), A + (6 << 24)])),
+    "misaligned grad": ({}, dict(grads=[A + (3 << 24), A + (4 << 24) + 4, A + (5 << 24), A + (6 << 24)])),
+    "m overlaps v": ({}, dict(v=A + (1 << 24) + 16)),
+    "param overlaps m": ({}, dict(m=A + 16)),
+    "grad overlaps m": ({}, dict(grads=[A + (1 << 24), A + (4 << 24), A + (5 << 24), A + (6 << 24)])),
+    "mask overlaps v": (dict(weight_decay=0.1, wd_mask=A + (2 << 24)), {}),
+}
+
+
+@pytest.mark.parametrize("case", sorted(BAD_STEPS))
+def test_step_rejects(case):
+    hpkw, callkw = BAD_STEPS[case]
+    rc, msg = _call_step(_hp(**hpkw), **callkw)
+    assert rc == z.ZERO_EINVAL, (case, rc, msg)
+    assert msg, case
+
+
+def test_step_null_hparams_and_states():
+    lib = _abi.load()
+    arr = (C.c_void_p * 1)(A)
+    assert lib.zero_step(None, A, arr, None, 1, None) == z.ZERO_EINVAL
+    hp = _hp(n_workers=1)
+    assert lib.zero_step(C.byref(hp), A, arr, None, 1, None) == z.ZERO_EINVAL
+    assert lib.zero_step(C.byref(hp), A, None, C.byref(_abi.zero_states(None, A, A + 4096)), 1,
+                         None) == z.ZERO_EINVAL
+
+
+def test_grads_may_alias_each_other_but_checks_still_run():
+    # identical gradient buffers for every worker are read-only and allowed; the call
+    # is still rejected here, for t = 0, so nothing is launched
+    hp = _hp()
+    rc, msg = _call_step(hp, grads=[A + (3 << 24)] * 4, t=0)
+    assert rc == z.ZERO_EINVAL and "t must be" in msg
+
+
+def test_empty_rank_shard_is_a_no_op():
+    """N > n gives trailing empty shards (numpy semantics); a rank-mode call for
+    an empty shard is valid and enqueues nothing."""
+    hp = _hp(n=3, n_workers=5, rank=4)
+    rc, msg = _call_step(hp, master=A + (9 << 24))
+    assert rc == z.ZERO_OK, msg
+    lib = _abi.load()
+    st = _abi.zero_states(master=A + (9 << 24), m=A + (1 << 24), v=A + (2 << 24))
+    assert lib.zero_init_states(C.byref(hp), A, C.byref(st), None) == z.ZERO_OK
+
+
+@pytest.mark.parametrize("case", ["no parameters", "master in full fp32", "m overlaps v",
+                                  "master missing in mixed", "unknown mode"])
+def test_init_rejects(case):
+    hpkw, callkw = BAD_STEPS[case]
+    lib = _abi.load()
+    hp = _hp(**hpkw)
+    st = _abi.zero_states(master=callkw.get("master"), m=callkw.get("m", A + (1 << 24)),
+                          v=callkw.get("v", A + (2 << 24)))
+    assert lib.zero_init_states(C.byref(hp), A, C.byref(st), None) == z.ZERO_EINVAL
+    assert lib.zero_last_error()
+
+
+# -- binding ------------------------------------------------------------------
+def test_binding_rejects_host_tensors():
+    import torch
+    hp = z.HParams(n=8, n_workers=1, mode=z.ZERO_MODE_F32, lr=1e-3, beta1=0.9, beta2=0.999,
+                   eps=1e-8)
+    x = torch.zeros(8)
+    st = z.States(None, torch.zeros(8), torch.zeros(8))
+    with pytest.raises(ValueError, match="GPU tensor"):
+        z.zero_step(hp, x, [torch.zeros(8)], st, 1, stream=0)
+
+
+def test_wd_mask_packing():
+    flags = np.zeros(70, bool)
+    flags[[0, 5, 31, 32, 63, 69]] = True
+    w = z.wd_mask_from_flags(flags, device="cpu").numpy().view(np.uint32)
+    assert w.size == 3
+    bits = [(int(w[i // 32]) >> (i % 32)) & 1 for i in range(70)]
+    assert bits == flags.astype(int).tolist()

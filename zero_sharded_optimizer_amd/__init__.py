@@ -1,0 +1,215 @@
+"""Fused ZeRO-sharded Adam step for AMD Instinct MI355X (gfx950).
+
+A thin Python binding over the C ABI of libzero.so (include/zero_adam.h), with
+the same function names. It only marshals arguments (device pointers, the HIP
+stream, the hyperparameter struct) and checks that each tensor is a
+contiguous device tensor of the dtype and size the call will touch; every step
+of the computation runs in the library's HIP kernels. There is no CPU
+fallback: without libzero.so every call raises.
+
+The operation is the one of "ZeRO-Sharded Adam Step" (scratchllm.com),
+sections "The step", "The shards" and "What to implement", with N logical
+workers sharing one GPU:
+  zero_init_states(hp, param, states)   -> m = v = 0, master from param
+  zero_step(hp, param, grads, states, t) -> one reduce-scatter-mean / Adam /
+                                            all-gather step, in place
+  zero_memory_bytes(...)                 -> per-rank memory by ZeRO stage
+  zero_shard_bounds(n, N, r)             -> np.array_split shard [a, b)
+"""
+import ctypes as C
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import _abi
+from ._abi import (ZERO_EHIP, ZERO_EINVAL, ZERO_EUNSUPPORTED, ZERO_MAX_WORKERS,  # noqa: F401
+                   ZERO_MODE_F32, ZERO_MODE_F64, ZERO_MODE_MIXED_BF16, ZERO_OK)
+
+__all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
+           "zero_memory_bytes", "zero_shard_bounds", "zero_last_error", "wd_mask_from_flags",
+           "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MAX_WORKERS"]
+
+
+class ZeroError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{_abi.STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+        self.message = message
+
+
+@dataclass
+class HParams:
+    """Mirror of zero_hparams. No defaults for the optimizer's hyperparameters."""
+    n: int
+    n_workers: int
+    mode: int
+    lr: float
+    beta1: float
+    beta2: float
+    eps: float
+    weight_decay: float = 0.0
+    rank: int = -1
+    wd_mask: object = None  # device int32/uint32 tensor of (n + 31) // 32 words, or None
+
+    def to_c(self):
+        return _abi.zero_hparams(
+            n=int(self.n), n_workers=int(self.n_workers), rank=int(self.rank),
+            mode=int(self.mode), reserved=0, lr=float(self.lr), beta1=float(self.beta1),
+            beta2=float(self.beta2), eps=float(self.eps), weight_decay=float(self.weight_decay),
+            wd_mask=_addr(self.wd_mask))
+
+
+@dataclass
+class States:
+    """Caller-owned optimizer state (master may be None in full fp64/fp32 mode)."""
+    master: object
+    m: object
+    v: object
+
+    def to_c(self):
+        return _abi.zero_states(master=_addr(self.master), m=_addr(self.m), v=_addr(self.v))
+
+
+# element types per mode: (parameter, gradient, state)
+_DTYPES = {
+    ZERO_MODE_F64: ("float64", "float64", "float64"),
+    ZERO_MODE_F32: ("float32", "float32", "float32"),
+    ZERO_MODE_MIXED_BF16: ("bfloat16", "bfloat16", "float32"),
+}
+
+
+def _addr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _check_tensor(x, dtype_name, numel, what):
+    """A raw int is taken as a device address the caller vouches for; a tensor
+    must be a contiguous GPU tensor of the right dtype holding >= numel elements."""
+    if x is None or isinstance(x, int):
+        return
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError(f"{what}: expected a torch.Tensor or a device address")
+    if not x.is_cuda:
+        raise ValueError(f"{what}: must be a GPU tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous")
+    if x.dtype != getattr(torch, dtype_name):
+        raise ValueError(f"{what}: dtype {x.dtype}, expected torch.{dtype_name}")
+    if x.numel() < numel:
+        raise ValueError(f"{what}: {x.numel()} elements, the call touches {numel}")
+
+
+def _stream_handle(stream, like):
+    if stream is None:
+        import torch
+        dev = like.device if hasattr(like, "device") else None
+        return torch.cuda.current_stream(dev).cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _raise(status):
+    lib = _abi.load()
+    raise ZeroError(status, lib.zero_last_error().decode())
+
+
+def _shard_len(hp):
+    if hp.rank < 0:
+        return 0, hp.n
+    a, b = zero_shard_bounds(hp.n, hp.n_workers, hp.rank)
+    return a, b
+
+
+def _check_common(hp, param, states):
+    if hp.mode not in _DTYPES:
+        return None
+    p_dt, g_dt, s_dt = _DTYPES[hp.mode]
+    if hp.n < 1 or hp.n_workers < 1 or not (-1 <= hp.rank < hp.n_workers):
+        return None  # the library rejects these with its own message
+    a, b = _shard_len(hp)
+    _check_tensor(param, p_dt, hp.n, "param")
+    _check_tensor(states.m, s_dt, b - a, "states.m")
+    _check_tensor(states.v, s_dt, b - a, "states.v")
+    _check_tensor(states.master, s_dt, b - a, "states.master")
+    if hp.weight_decay != 0.0 and hp.wd_mask is not None and not isinstance(hp.wd_mask, int):
+        import torch
+        if hp.wd_mask.dtype not in (torch.int32, torch.uint32):
+            raise ValueError("wd_mask: expected int32/uint32 words")
+        if not hp.wd_mask.is_cuda or not hp.wd_mask.is_contiguous():
+            raise ValueError("wd_mask: must be a contiguous GPU tensor")
+        if hp.wd_mask.numel() < (hp.n + 31) // 32:
+            raise ValueError("wd_mask: needs (n + 31) // 32 words")
+    return g_dt, b - a
+
+
+def zero_init_states(hp: HParams, param, states: States, stream=None) -> None:
+    """Enqueue init_states: m = v = 0, master = widen(param) (see zero_adam.h)."""
+    _check_common(hp, param, states)
+    lib = _abi.load()
+    c_hp, c_st = hp.to_c(), states.to_c()
+    st = lib.zero_init_states(C.byref(c_hp), _addr(param), C.byref(c_st),
+                              _stream_handle(stream, states.m))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+def zero_step(hp: HParams, param, grads: Sequence, states: States, t: int, stream=None) -> None:
+    """Enqueue one fused step, in place (see zero_adam.h)."""
+    chk = _check_common(hp, param, states)
+    if chk is not None:
+        g_dt, glen = chk
+        if len(grads) != hp.n_workers:
+            raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
+        for k, g in enumerate(grads):
+            _check_tensor(g, g_dt, glen, f"grads[{k}]")
+    lib = _abi.load()
+    c_hp, c_st = hp.to_c(), states.to_c()
+    arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
+    st = lib.zero_step(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t),
+                       _stream_handle(stream, states.m))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+def zero_memory_bytes(n: int, n_workers: int, rank: int, stage: int, mode: int,
+                      convention: int = 0) -> dict:
+    lib = _abi.load()
+    out = _abi.zero_mem()
+    st = lib.zero_memory_bytes(n, n_workers, rank, stage, mode, convention, C.byref(out))
+    if st != ZERO_OK:
+        _raise(st)
+    return {"params": out.params, "grads": out.grads, "optimizer": out.optimizer,
+            "total": out.total}
+
+
+def zero_shard_bounds(n: int, n_workers: int, r: int):
+    lib = _abi.load()
+    a, b = C.c_int64(), C.c_int64()
+    st = lib.zero_shard_bounds(n, n_workers, r, C.byref(a), C.byref(b))
+    if st != ZERO_OK:
+        _raise(st)
+    return a.value, b.value
+
+
+def zero_last_error() -> str:
+    return _abi.load().zero_last_error().decode()
+
+
+def wd_mask_from_flags(flags, device="cuda") -> "torch.Tensor":
+    """Pack per-element decay flags (bool, length n) into the ABI's bitmask:
+    element i is bit i % 32 of word i // 32. Returns an int32 device tensor."""
+    import torch
+    f = np.asarray(flags.cpu().numpy() if hasattr(flags, "cpu") else flags, dtype=bool)
+    n = f.size
+    words = (n + 31) // 32
+    padded = np.zeros(words * 32, dtype=bool)
+    padded[:n] = f
+    packed = np.packbits(padded, bitorder="little").view("<u4").view(np.int32)
+    return torch.from_numpy(packed.copy()).to(device)

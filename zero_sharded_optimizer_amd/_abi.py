@@ -1,0 +1,86 @@
+"""ctypes declarations of the C ABI in include/zero_adam.h.
+
+Loading the library touches no GPU: libzero.so makes no HIP call until a
+function that enqueues device work is called with valid arguments.
+"""
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzero.so")
+
+ZERO_OK = 0
+ZERO_EINVAL = -1
+ZERO_EUNSUPPORTED = -2
+ZERO_EHIP = -3
+
+ZERO_MODE_F64 = 0
+ZERO_MODE_F32 = 1
+ZERO_MODE_MIXED_BF16 = 2
+
+ZERO_MAX_WORKERS = 256
+
+STATUS_NAMES = {ZERO_OK: "ZERO_OK", ZERO_EINVAL: "ZERO_EINVAL",
+                ZERO_EUNSUPPORTED: "ZERO_EUNSUPPORTED", ZERO_EHIP: "ZERO_EHIP"}
+
+
+class zero_hparams(C.Structure):
+    _fields_ = [
+        ("n", C.c_int64),
+        ("n_workers", C.c_int32),
+        ("rank", C.c_int32),
+        ("mode", C.c_int32),
+        ("reserved", C.c_int32),
+        ("lr", C.c_double),
+        ("beta1", C.c_double),
+        ("beta2", C.c_double),
+        ("eps", C.c_double),
+        ("weight_decay", C.c_double),
+        ("wd_mask", C.c_void_p),
+    ]
+
+
+class zero_states(C.Structure):
+    _fields_ = [("master", C.c_void_p), ("m", C.c_void_p), ("v", C.c_void_p)]
+
+
+class zero_mem(C.Structure):
+    _fields_ = [("params", C.c_int64), ("grads", C.c_int64), ("optimizer", C.c_int64),
+                ("total", C.c_int64)]
+
+
+EXPORTED = ("zero_init_states", "zero_step", "zero_memory_bytes", "zero_shard_bounds",
+            "zero_last_error")
+
+_lib = None
+
+
+def load(path=None):
+    """Load libzero.so (once). Raises if it has not been built: there is no
+    fallback path."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(
+            f"{p} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+            "or `python zero_sharded_optimizer_amd/build_lib.py`")
+    lib = C.CDLL(p)
+    lib.zero_init_states.argtypes = [C.POINTER(zero_hparams), C.c_void_p,
+                                     C.POINTER(zero_states), C.c_void_p]
+    lib.zero_init_states.restype = C.c_int
+    lib.zero_step.argtypes = [C.POINTER(zero_hparams), C.c_void_p, C.POINTER(C.c_void_p),
+                              C.POINTER(zero_states), C.c_int64, C.c_void_p]
+    lib.zero_step.restype = C.c_int
+    lib.zero_memory_bytes.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
+                                      C.c_int32, C.POINTER(zero_mem)]
+    lib.zero_memory_bytes.restype = C.c_int
+    lib.zero_shard_bounds.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.POINTER(C.c_int64),
+                                      C.POINTER(C.c_int64)]
+    lib.zero_shard_bounds.restype = C.c_int
+    lib.zero_last_error.argtypes = []
+    lib.zero_last_error.restype = C.c_char_p
+    if path is None:
+        _lib = lib
+    return lib

@@ -1,0 +1,292 @@
+// Host side of the C ABI declared in include/zero_adam.h: argument validation,
+// np.array_split shard bounds, the per-rank memory model and the per-step
+// scalars. Touches no HIP API itself; device work goes through zlaunch::.
+#include "zero_adam.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "zero_launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+zero_status fail(zero_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+zero_status fail(zero_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+zero_status ok() {
+  g_last_error.clear();
+  return ZERO_OK;
+}
+
+// Shard r of np.array_split(np.arange(n), N) ("ZeRO-Sharded Adam Step",
+// section "The shards"): q = n / N, rho = n % N; the first rho shards have
+// q + 1 elements, so shard r starts at r*q + min(r, rho).
+void shard_range(int64_t n, int64_t N, int64_t r, int64_t* a, int64_t* b) {
+  const int64_t q = n / N, rho = n % N;
+  *a = r * q + (r < rho ? r : rho);
+  *b = *a + q + (r < rho ? 1 : 0);
+}
+
+struct Widths {
+  int64_t param, grad, state, optimizer;
+};
+
+bool mode_widths(int32_t mode, Widths* w) {
+  switch (mode) {
+    case ZERO_MODE_F64: *w = {8, 8, 8, 16}; return true;
+    case ZERO_MODE_F32: *w = {4, 4, 4, 8}; return true;
+    case ZERO_MODE_MIXED_BF16: *w = {2, 2, 4, 12}; return true;
+    default: return false;
+  }
+}
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  const char* name;
+};
+
+bool overlaps(const Range& x, const Range& y) {
+  return x.lo < x.hi && y.lo < y.hi && x.lo < y.hi && y.lo < x.hi;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shared checks of zero_hparams. On success fills the shard range this call
+// covers ([a, b): the whole vector in full mode, worker `rank`'s shard in rank
+// mode).
+zero_status check_hparams(const zero_hparams* hp, bool for_step, Widths* wd, int64_t* a,
+                          int64_t* b) {
+  if (hp == nullptr) return fail(ZERO_EINVAL, "hparams is NULL");
+  if (hp->reserved != 0) return fail(ZERO_EINVAL, "hparams.reserved must be 0");
+  if (!mode_widths(hp->mode, wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
+  if (hp->n < 1) return fail(ZERO_EINVAL, "n must be >= 1 (no parameters), got %lld",
+                             (long long)hp->n);
+  if (hp->n_workers < 1 || hp->n_workers > ZERO_MAX_WORKERS)
+    return fail(ZERO_EINVAL, "n_workers must be in [1, %d], got %d", ZERO_MAX_WORKERS,
+                hp->n_workers);
+  if (hp->rank < -1 || hp->rank >= hp->n_workers)
+    return fail(ZERO_EINVAL, "rank must be -1 or in [0, %d), got %d", hp->n_workers, hp->rank);
+  if (hp->rank >= 0) {
+    shard_range(hp->n, hp->n_workers, hp->rank, a, b);
+  } else {
+    *a = 0;
+    *b = hp->n;
+  }
+  if (!for_step) return ZERO_OK;
+  if (!std::isfinite(hp->lr)) return fail(ZERO_EINVAL, "lr must be finite");
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return fail(ZERO_EINVAL, "beta1 must be in [0, 1)");
+  if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return fail(ZERO_EINVAL, "beta2 must be in [0, 1)");
+  if (!(std::isfinite(hp->eps) && hp->eps > 0.0)) return fail(ZERO_EINVAL, "eps must be finite and > 0");
+  if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
+    return fail(ZERO_EINVAL, "weight_decay must be finite and >= 0");
+  if (hp->wd_mask != nullptr && !aligned(hp->wd_mask, 4))
+    return fail(ZERO_EINVAL, "wd_mask must be 4-byte aligned");
+  return ZERO_OK;
+}
+
+// Pointer checks shared by init and step: the state buffers of `len` elements
+// and the role of the master pointer per mode.
+zero_status check_states(const zero_hparams* hp, const zero_states* st, const Widths& wd) {
+  if (st == nullptr) return fail(ZERO_EINVAL, "states is NULL");
+  if (st->m == nullptr || st->v == nullptr) return fail(ZERO_EINVAL, "states.m / states.v is NULL");
+  if (!aligned(st->m, 16) || !aligned(st->v, 16))
+    return fail(ZERO_EINVAL, "states.m and states.v must be 16-byte aligned");
+  const bool need_master = hp->mode == ZERO_MODE_MIXED_BF16 || hp->rank >= 0;
+  if (need_master && st->master == nullptr)
+    return fail(ZERO_EINVAL, "states.master is required in mixed mode and in rank mode");
+  if (!need_master && st->master != nullptr)
+    return fail(ZERO_EINVAL,
+                "states.master must be NULL in full fp64/fp32 mode (the parameter is its own "
+                "master)");
+  if (st->master != nullptr && !aligned(st->master, 16))
+    return fail(ZERO_EINVAL, "states.master must be 16-byte aligned");
+  (void)wd;
+  return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* zero_last_error(void) { return g_last_error.c_str(); }
+
+zero_status zero_shard_bounds(int64_t n, int32_t n_workers, int32_t r, int64_t* begin,
+                              int64_t* end) {
+  if (begin == nullptr || end == nullptr) return fail(ZERO_EINVAL, "begin/end is NULL");
+  if (n < 0) return fail(ZERO_EINVAL, "n must be >= 0");
+  if (n_workers < 1) return fail(ZERO_EINVAL, "n_workers must be >= 1");
+  if (r < 0 || r >= n_workers) return fail(ZERO_EINVAL, "r must be in [0, %d)", n_workers);
+  shard_range(n, n_workers, r, begin, end);
+  return ok();
+}
+
+zero_status zero_memory_bytes(int64_t n, int32_t n_workers, int32_t rank, int32_t stage,
+                              int32_t mode, int32_t convention, zero_mem* out) {
+  if (out == nullptr) return fail(ZERO_EINVAL, "out is NULL");
+  if (n < 1) return fail(ZERO_EINVAL, "n must be >= 1 (no parameters)");
+  if (n_workers < 1) return fail(ZERO_EINVAL, "n_workers must be >= 1");
+  if (rank < 0 || rank >= n_workers) return fail(ZERO_EINVAL, "rank must be in [0, %d)", n_workers);
+  if (stage < 0 || stage > 3) return fail(ZERO_EINVAL, "stage must be in [0, 3], got %d", stage);
+  Widths w;
+  if (!mode_widths(mode, &w)) return fail(ZERO_EINVAL, "unknown mode %d", mode);
+  int64_t a, b;
+  shard_range(n, n_workers, rank, &a, &b);
+  const int64_t c = b - a;
+  if (convention == 0) {
+    out->params = w.param * (stage >= 3 ? c : n);
+    out->grads = w.grad * (stage >= 2 ? c : n);
+    out->optimizer = w.optimizer * (stage >= 1 ? c : n);
+  } else if (convention == 1) {
+    if (mode == ZERO_MODE_MIXED_BF16)
+      return fail(ZERO_EUNSUPPORTED, "convention 1 counts one value width; not for mixed mode");
+    const int64_t B = w.param;
+    switch (stage) {
+      case 0: out->params = B * n; out->grads = B * n; out->optimizer = 2 * B * n; break;
+      case 1: out->params = B * n; out->grads = B * n + B * c; out->optimizer = 3 * B * c; break;
+      case 2: out->params = B * n; out->grads = B * c; out->optimizer = 3 * B * c; break;
+      default: out->params = B * c; out->grads = B * c; out->optimizer = 2 * B * c; break;
+    }
+  } else {
+    return fail(ZERO_EINVAL, "unknown convention %d", convention);
+  }
+  out->total = out->params + out->grads + out->optimizer;
+  return ok();
+}
+
+zero_status zero_init_states(const zero_hparams* hp, const void* param, const zero_states* st,
+                             void* stream) {
+  Widths wd;
+  int64_t a = 0, b = 0;
+  zero_status s = check_hparams(hp, false, &wd, &a, &b);
+  if (s != ZERO_OK) return s;
+  if (b == a) return ok();  // an empty shard: no buffer is touched
+  if ((s = check_states(hp, st, wd)) != ZERO_OK) return s;
+  if (st->master != nullptr && param == nullptr)
+    return fail(ZERO_EINVAL, "param is NULL but a master copy is requested");
+  if (param != nullptr && !aligned(param, (uintptr_t)wd.param))
+    return fail(ZERO_EINVAL, "param must be aligned to its element size");
+  const int64_t len = b - a;
+  const Range r_m{(uintptr_t)st->m, (uintptr_t)st->m + (uintptr_t)(len * wd.state), "m"};
+  const Range r_v{(uintptr_t)st->v, (uintptr_t)st->v + (uintptr_t)(len * wd.state), "v"};
+  const Range r_ms{(uintptr_t)st->master,
+                   st->master ? (uintptr_t)st->master + (uintptr_t)(len * wd.state) : 0, "master"};
+  const Range r_p{(uintptr_t)param + (uintptr_t)(a * wd.param),
+                  param ? (uintptr_t)param + (uintptr_t)(b * wd.param) : 0, "param"};
+  const Range written[3] = {r_m, r_v, r_ms};
+  const Range all[4] = {r_m, r_v, r_ms, r_p};
+  for (int i = 0; i < 3; ++i)
+    for (int j = 0; j < 4; ++j)
+      if (i != j && overlaps(written[i], all[j]))
+        return fail(ZERO_EINVAL, "%s overlaps %s", written[i].name, all[j].name);
+  zlaunch::InitArgs ia;
+  ia.mode = hp->mode;
+  ia.param = st->master ? static_cast<const char*>(param) + a * wd.param : nullptr;
+  ia.master = st->master;
+  ia.m = st->m;
+  ia.v = st->v;
+  ia.len = len;
+  const char* err = zlaunch::launch_init(ia, stream);
+  if (err) return fail(ZERO_EHIP, "init launch failed: %s", err);
+  return ok();
+}
+
+zero_status zero_step(const zero_hparams* hp, void* param, const void* const* grads,
+                      const zero_states* st, int64_t t, void* stream) {
+  Widths wd;
+  int64_t a = 0, b = 0;
+  zero_status s = check_hparams(hp, true, &wd, &a, &b);
+  if (s != ZERO_OK) return s;
+  if (t < 1) return fail(ZERO_EINVAL, "t must be >= 1 (1-based step number), got %lld", (long long)t);
+  if (b == a) return ok();  // an empty shard: no buffer is touched
+  if ((s = check_states(hp, st, wd)) != ZERO_OK) return s;
+  if (param == nullptr) return fail(ZERO_EINVAL, "param is NULL");
+  if (grads == nullptr) return fail(ZERO_EINVAL, "grads is NULL");
+  const bool rank_mode = hp->rank >= 0;
+  if (rank_mode ? !aligned(param, (uintptr_t)wd.param) : !aligned(param, 16))
+    return fail(ZERO_EINVAL, rank_mode ? "param must be aligned to its element size"
+                                       : "param must be 16-byte aligned");
+  const int N = hp->n_workers;
+  for (int k = 0; k < N; ++k) {
+    if (grads[k] == nullptr) return fail(ZERO_EINVAL, "grads[%d] is NULL", k);
+    if (!aligned(grads[k], 16)) return fail(ZERO_EINVAL, "grads[%d] must be 16-byte aligned", k);
+  }
+  const int64_t len = b - a;
+  // Written ranges must not overlap one another or anything read.
+  Range written[4];
+  int nw = 0;
+  written[nw++] = {(uintptr_t)param + (uintptr_t)(a * wd.param),
+                   (uintptr_t)param + (uintptr_t)(b * wd.param), "param"};
+  written[nw++] = {(uintptr_t)st->m, (uintptr_t)st->m + (uintptr_t)(len * wd.state), "m"};
+  written[nw++] = {(uintptr_t)st->v, (uintptr_t)st->v + (uintptr_t)(len * wd.state), "v"};
+  if (st->master)
+    written[nw++] = {(uintptr_t)st->master, (uintptr_t)st->master + (uintptr_t)(len * wd.state),
+                     "master"};
+  for (int i = 0; i < nw; ++i)
+    for (int j = i + 1; j < nw; ++j)
+      if (overlaps(written[i], written[j]))
+        return fail(ZERO_EINVAL, "%s overlaps %s", written[i].name, written[j].name);
+  const bool decays = hp->weight_decay != 0.0;
+  for (int i = 0; i < nw; ++i) {
+    for (int k = 0; k < N; ++k) {
+      const Range g{(uintptr_t)grads[k], (uintptr_t)grads[k] + (uintptr_t)(len * wd.grad), "grad"};
+      if (overlaps(written[i], g)) return fail(ZERO_EINVAL, "%s overlaps grads[%d]", written[i].name, k);
+    }
+    if (decays && hp->wd_mask) {
+      const Range mk{(uintptr_t)hp->wd_mask,
+                     (uintptr_t)hp->wd_mask + (uintptr_t)(((hp->n + 31) / 32) * 4), "wd_mask"};
+      if (overlaps(written[i], mk)) return fail(ZERO_EINVAL, "%s overlaps wd_mask", written[i].name);
+    }
+  }
+
+  zlaunch::StepArgs la;
+  la.mode = hp->mode;
+  la.n_workers = N;
+  for (int k = 0; k < zlaunch::kMaxWorkers; ++k) la.grads[k] = k < N ? grads[k] : nullptr;
+  la.m = st->m;
+  la.v = st->v;
+  if (rank_mode || hp->mode == ZERO_MODE_MIXED_BF16) {
+    la.w = st->master;
+    la.out = static_cast<char*>(param) + a * wd.param;
+  } else {
+    la.w = param;  // updated in place: the parameter is its own master
+    la.out = nullptr;
+  }
+  la.len = len;
+  la.decay_kind = !decays ? 0 : (hp->wd_mask ? 2 : 1);
+  la.mask = decays ? hp->wd_mask : nullptr;
+  la.mask_bit_offset = a;
+  // Step scalars: formed in double, rounded to the state type by the launch.
+  const double tt = (double)t;
+  la.beta1 = hp->beta1;
+  la.beta2 = hp->beta2;
+  la.one_minus_beta1 = 1.0 - hp->beta1;
+  la.one_minus_beta2 = 1.0 - hp->beta2;
+  la.bias1 = 1.0 - std::pow(hp->beta1, tt);
+  la.bias2 = 1.0 - std::pow(hp->beta2, tt);
+  la.lr = hp->lr;
+  la.eps = hp->eps;
+  la.decay_factor = 1.0 - hp->lr * hp->weight_decay;
+  la.n_workers_value = (double)N;
+  if (!(la.bias1 > 0.0) || !(la.bias2 > 0.0))
+    return fail(ZERO_EINVAL, "bias correction 1 - beta^t is not positive (beta = 0 is fine; "
+                             "check beta and t)");
+  const char* err = zlaunch::launch_step(la, stream);
+  if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,45 @@
+// Interface between the host-side ABI layer (zero_abi.cpp: validation, shard
+// bounds, step scalars) and the gfx950 kernels (zero_kernels.hip). Plain C++,
+// no HIP types, so the ABI layer builds with the host compiler alone.
+#pragma once
+
+#include <cstdint>
+
+namespace zlaunch {
+
+constexpr int kMaxWorkers = 256;
+
+// Everything one fused step launch needs. All pointers are device addresses
+// that the ABI layer has validated (alignment, extents, no overlap of written
+// ranges).
+struct StepArgs {
+  int mode;        // 0 fp64, 1 fp32, 2 mixed bf16/fp32
+  int n_workers;   // 1..kMaxWorkers
+  const void* grads[kMaxWorkers];  // rank order; element j of worker k at grads[k][j]
+  void* w;         // master values (S): the parameter itself when updated in place
+  void* m;         // S
+  void* v;         // S
+  void* out;       // gathered parameter slot (P) written from w, or nullptr (in place)
+  int64_t len;     // elements this launch updates
+  const uint32_t* mask;     // decay bitmask or nullptr
+  int64_t mask_bit_offset;  // bit index of element 0
+  int decay_kind;  // 0 no decay, 1 every element, 2 per the bitmask
+  // Step scalars in double; the launch rounds each once to S.
+  double beta1, beta2, one_minus_beta1, one_minus_beta2, bias1, bias2, lr, eps,
+      decay_factor, n_workers_value;
+};
+
+struct InitArgs {
+  int mode;
+  const void* param;  // source of the master copy (P), or nullptr
+  void* master;       // S or nullptr
+  void* m;
+  void* v;
+  int64_t len;
+};
+
+// Each returns nullptr on success, or the HIP runtime's error string.
+const char* launch_step(const StepArgs& a, void* stream);
+const char* launch_init(const InitArgs& a, void* stream);
+
+}  // namespace zlaunch
