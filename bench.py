@@ -65,6 +65,87 @@ def load_traffic(workload, algo_bytes):
     return d.get("bytes_per_launch")
 
 
+STEP_KERNEL = "zero_step_kernel"
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_BYTES = 4 << 30  # the copy ceiling's buffer: 4 GiB read + 4 GiB written per copy
+
+
+def _pmc_rows(d):
+    import csv
+    import glob
+    out = []
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            out += list(csv.DictReader(fh))
+    return out
+
+
+def pmc_summary(workload, fetch_dir, write_dir, cmd):
+    """HBM bytes per step launch from two rocprofv3 --pmc passes (FETCH_SIZE,
+    WRITE_SIZE; KiB per dispatch). Each counter is scaled by what it reads for
+    the plain 4 GiB device copy run in the same process (known bytes / counter).
+    Writes profiles/traffic_<workload>.json and .md."""
+    import statistics
+    wl = None
+    from zero_sharded_optimizer_amd import synth
+    wl = synth.WORKLOADS[workload]
+    res = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _pmc_rows(d) if r["Counter_Name"] == name]
+        step = [float(r["Counter_Value"]) for r in rows if STEP_KERNEL in r["Kernel_Name"]]
+        copy = [float(r["Counter_Value"]) for r in rows if COPY_KERNEL in r["Kernel_Name"]]
+        big = max(copy)
+        copy = [c for c in copy if c > 0.9 * big]  # the 4 GiB copies
+        factor = COPY_BYTES / (statistics.median(copy) * 1024)
+        res[name] = {"step_kib_mean": statistics.mean(step), "step_dispatches": len(step),
+                     "copy_kib_median": statistics.median(copy), "copy_dispatches": len(copy),
+                     "factor": factor,
+                     "step_bytes": statistics.mean(step) * 1024 * factor}
+    algo = bytes_per_param(wl) * wl.length
+    total = res["FETCH_SIZE"]["step_bytes"] + res["WRITE_SIZE"]["step_bytes"]
+    out = {"workload": workload, "kernel": STEP_KERNEL, "kernel_src_sha256_16": kernel_hash(),
+           "bytes_per_launch": total, "algorithmic_bytes_per_launch": algo,
+           "traffic_over_algorithmic": total / algo, "counters": res, "command": cmd}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    base = os.path.join(ROOT, "profiles", f"traffic_{workload}")
+    with open(base + ".json", "w") as f:
+        json.dump(out, f, indent=2)
+    with open(base + ".md", "w") as f:
+        f.write(f"# HBM traffic of {STEP_KERNEL}, workload {workload}\n\n")
+        f.write(f"Commands (run from the repository root on one MI355X):\n\n```\n{cmd}\n```\n\n")
+        f.write("| counter | step kernel, KiB/dispatch | dispatches | 4 GiB copy, KiB | factor | bytes/launch |\n|---|---|---|---|---|---|\n")
+        for k, v in res.items():
+            f.write(f"| {k} | {v['step_kib_mean']:.1f} | {v['step_dispatches']} | {v['copy_kib_median']:.1f} | "
+                    f"{v['factor']:.4f} | {v['step_bytes']:.4e} |\n")
+        f.write(f"\nTraffic {total:.4e} B per launch against {algo:.4e} algorithmic bytes "
+                f"({bytes_per_param(wl)} B/param x {wl.length} params): ratio "
+                f"{total / algo:.4f}.\n")
+    return out
+
+
+def kt_summary(workload, kt_dir, cmd):
+    """Per-kernel durations from rocprofv3 --kernel-trace --stats, as
+    profiles/kernel_trace_<workload>.md."""
+    import csv
+    import glob
+    f = glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(f)))
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.md")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        fh.write(f"# rocprofv3 kernel statistics, workload {workload}\n\n")
+        fh.write(f"Command (run from the repository root on one MI355X):\n\n```\n{cmd}\n```\n\n")
+        fh.write("| kernel | calls | average ns | min ns | max ns | % of GPU time |\n|---|---|---|---|---|---|\n")
+        for r in rows:
+            name = r["Name"]
+            if STEP_KERNEL in name:
+                name = name.split("(")[0] + "<" + name.split("<", 1)[1].split(">(")[0] + ">"
+            name = name[:110]
+            fh.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
+                     f"{r['MaxNs']} | {float(r['Percentage']):.2f} |\n")
+    return path
+
+
 def cpu_baseline(wl, target_s=12.0, sample_n=1 << 22):
     """The CPU oracle (single-threaded, as it stands) on the first sample_n
     elements of the same workload, stepped until about target_s seconds."""
@@ -73,10 +154,12 @@ def cpu_baseline(wl, target_s=12.0, sample_n=1 << 22):
     from oracle import Oracle
     from zero_sharded_optimizer_amd import synth
     O = Oracle()
-    small = synth.scaled(wl, min(sample_n, wl.length), rank=-1, shapes=())
-    if wl.rank >= 0:
-        small = synth.scaled(wl, min(sample_n, wl.length), rank=-1, shapes=(), decay="all")
+    # the first sample_n elements, as a full-mode call over all N workers; the
+    # decay flags (if any) are those of the workload's first sample_n elements
+    small = synth.scaled(wl, min(sample_n, wl.length), rank=-1, shapes=(),
+                         decay="all" if wl.decay == "all" else "none")
     n = small.n
+    assert n > 0
 
     def host(x):
         if x.dtype == torch.bfloat16:
@@ -130,7 +213,18 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
+    ap.add_argument("--kt-summary", metavar="KT_DIR",
+                    help="summarise a rocprofv3 --kernel-trace --stats run into profiles/ and exit")
+    ap.add_argument("--cmd", default="", help="the profiling command, recorded in the summary")
     args = ap.parse_args()
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(args.workload, *args.pmc_summary, args.cmd)))
+        return
+    if args.kt_summary:
+        print(kt_summary(args.workload, args.kt_summary, args.cmd))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (all logical workers live in one GPU's HBM); "
               f"--gpus {args.gpus} is not supported", file=sys.stderr)

@@ -98,9 +98,10 @@ WORKLOADS = {
 
 def scaled(wl: Workload, n: int, name=None, shapes=None, **kw) -> Workload:
     """The same workload at another size (for oracle-sized parity cases)."""
-    if shapes is not None:
+    if shapes:
         n = tensor_starts(shapes)[1]
-    return replace(wl, n=n, name=name or f"{wl.name}@{n}", shapes=shapes or wl.shapes, **kw)
+    shapes = wl.shapes if shapes is None else tuple(shapes)
+    return replace(wl, n=n, name=name or f"{wl.name}@{n}", shapes=shapes, **kw)
 
 
 def decay_flags(wl: Workload) -> Optional[np.ndarray]:
