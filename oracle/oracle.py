@@ -52,6 +52,14 @@ class Oracle:
             f.restype = _i32
         lib.orc_rank_step.argtypes = [_i32, _i64, _i64, _i64] + step_args[3:]
         lib.orc_rank_step.restype = _i32
+        lib.orc_mean_grad.argtypes = [_i32, _i64, _i64, _i64, _vp, _vp, C.POINTER(_dbl)]
+        lib.orc_mean_grad.restype = _i32
+        lib.orc_step_mean.argtypes = [_i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _vp, _vp, _i64, _dbl, _dbl, _dbl, _dbl, _dbl, _vp,
+                                      C.POINTER(_dbl), _dbl]
+        lib.orc_step_mean.restype = _i32
+        lib.orc_clip_factor.argtypes = [_dbl, _dbl]
+        lib.orc_clip_factor.restype = _dbl
         lib.orc_memory_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _i64, _i32,
                                          C.POINTER(_i64)]
         lib.orc_memory_bytes.restype = _i32
@@ -149,6 +157,61 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return p_out, mst_out, m_out, v_out
+
+    # -- materialised mean gradient and clipping --------------------------------
+    def mean_grad(self, mode, n, N, grads, rank=-1):
+        """The reduce-scatter mean, materialised, and the squared norm.
+
+        Full mode (rank < 0): grads are N full-length arrays; returns (mean of
+        length n, sum over shards of the shard squared norms). Rank mode: grads are
+        worker `rank`'s N chunks; returns (its c_r means, its shard's squared norm)."""
+        grads = [np.ascontiguousarray(g, dtype=_PARAM_DT[mode]) for g in grads]
+        assert len(grads) == N
+        if rank < 0:
+            length = n
+        else:
+            a, b = self.split_bounds(n, N, rank)
+            length = b - a
+        for g in grads:
+            assert g.size == length
+        out = np.empty(length, _STATE_DT[mode])
+        ss = _dbl()
+        rc = self.lib.orc_mean_grad(mode, n, N, rank, _ptr_array(grads), _ptr(out), C.byref(ss))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return out, ss.value
+
+    def step_mean(self, mode, N, param, mean, master, m, v, t, lr, b1=0.9, b2=0.999, eps=1e-8,
+                  wd=0.0, decay=None, clip_sumsq=None, max_norm=0.0, rank=-1):
+        """Adam from a materialised mean gradient, optionally clipped by the global
+        squared norm clip_sumsq. Returns (param, master, m, v); in rank mode master,
+        m, v are the shard's."""
+        param = np.ascontiguousarray(param, dtype=_PARAM_DT[mode])
+        sdt = _STATE_DT[mode]
+        mean = np.ascontiguousarray(mean, dtype=sdt)
+        m = np.ascontiguousarray(m, dtype=sdt)
+        v = np.ascontiguousarray(v, dtype=sdt)
+        n = param.size
+        if master is not None:
+            master = np.ascontiguousarray(master, dtype=np.float32 if mode == MODE_MIXED else sdt)
+        p_out = np.empty_like(param)
+        if rank >= 0:
+            mst_out = np.empty_like(master)
+        else:
+            mst_out = np.empty(n, np.float32) if mode == MODE_MIXED else None
+        m_out, v_out = np.empty_like(m), np.empty_like(v)
+        dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.uint8)
+        cs = None if clip_sumsq is None else C.byref(_dbl(float(clip_sumsq)))
+        rc = self.lib.orc_step_mean(mode, n, N, rank, _ptr(param), _ptr(mean), _ptr(master),
+                                    _ptr(m), _ptr(v), _ptr(p_out), _ptr(mst_out), _ptr(m_out),
+                                    _ptr(v_out), int(t), float(lr), float(b1), float(b2),
+                                    float(eps), float(wd), _ptr(dec), cs, float(max_norm))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return p_out, mst_out, m_out, v_out
+
+    def clip_factor(self, sumsq, max_norm):
+        return self.lib.orc_clip_factor(float(sumsq), float(max_norm))
 
     # -- memory ---------------------------------------------------------------
     def memory_bytes(self, n, N, r, stage, P, G, K, convention=0):

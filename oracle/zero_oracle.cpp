@@ -47,6 +47,13 @@
 //     and rounded once to S.
 //   * bf16 write-back in mixed precision: round to nearest, ties to even; NaN
 //     becomes the quiet NaN 0x7FC0.
+//   * Global-norm clipping ("Data parallelism and ZeRO stages 1 to 3", section
+//     "Going further": an all-reduce of squared chunk norms before the step;
+//     no formula): each shard's squared norm of its mean gradient, summed in
+//     index order in double, then summed over shards in rank order; the factor
+//     min(1, max_norm / (sqrt(sum) + 1e-6)) in double, as torch's
+//     clip_grad_norm_ defines it, rounded once to S; the mean gradient is
+//     multiplied by it before the moments.
 //
 // Build: g++ -O2 -std=c++17 -ffp-contract=off -fno-fast-math -shared -fPIC.
 // Single-threaded and deliberately unfused: every worker materialises its own
@@ -392,6 +399,103 @@ void rank_step(int mode, int64_t n, int64_t N, int64_t r, const void* param_in,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Squared norm of one shard's mean gradient, summed in index order in double.
+// "Data parallelism and ZeRO stages 1 to 3", section "Going further": sharded
+// global-norm clipping is an all-reduce of the squared chunk norms before the
+// step.
+// ---------------------------------------------------------------------------
+template <class S>
+double shard_sumsq(const std::vector<S>& g) {
+  double acc = 0.0;
+  for (const S x : g) {
+    const double d = (double)x;
+#if ORACLE_MUTANT == 16
+    acc = acc + (d < 0 ? -d : d);  // planted: a 1-norm instead of squares
+#else
+    acc = acc + d * d;
+#endif
+  }
+  return acc;
+}
+
+// The reduce-scatter mean of every shard in the call's range, materialised
+// (stage 1 keeps the averaged gradient: "2. Principles", "Your emulation's
+// bookkeeping"). Full mode (r < 0): all N shards, mean_out holds n values and
+// *sumsq_out the sum over shards, in rank order, of each shard's squared norm
+// (the all-reduce). Rank mode: worker r's shard from chunk gradients; mean_out
+// holds c_r values and *sumsq_out that shard's squared norm alone.
+template <class S>
+void mean_grad(int mode, int64_t n, int64_t N, int64_t r, const void* const* grads,
+               S* mean_out, double* sumsq_out) {
+  double total = 0.0;
+  const int64_t r0 = r < 0 ? 0 : r, r1 = r < 0 ? N : r + 1;
+  for (int64_t k = r0; k < r1; ++k) {
+    int64_t a, b;
+    split_bounds(n, N, k, &a, &b);
+    const int64_t base = r < 0 ? 0 : a;  // chunk buffers start at the shard
+    std::vector<S> gbar = reduce_scatter_mean<S>(grads, N, a, b, base, mode);
+    for (int64_t j = a; j < b; ++j) mean_out[j - base] = gbar[(size_t)(j - a)];
+    total = total + shard_sumsq<S>(gbar);
+  }
+  if (sumsq_out) *sumsq_out = total;
+}
+
+// The clipping factor from the global squared norm, as torch's
+// clip_grad_norm_ (the production equivalent the openlearn page names)
+// defines it: min(1, max_norm / (norm + 1e-6)), in double.
+double clip_factor(double sumsq, double max_norm) {
+#if ORACLE_MUTANT == 15
+  return max_norm / (std::sqrt(sumsq) + 1e-6);  // planted: no clamp at 1
+#else
+  const double c = max_norm / (std::sqrt(sumsq) + 1e-6);
+  return c < 1.0 ? c : 1.0;
+#endif
+}
+
+// Adam driven by a materialised mean gradient: every shard in the call's range
+// steps with its own state, the mean gradient optionally scaled by the clipping
+// factor (rounded once to S) before the moments.
+template <class S>
+void step_from_mean(int mode, int64_t n, int64_t N, int64_t r, const void* param_in,
+                    const S* mean, const void* master_in, const S* m_in, const S* v_in,
+                    void* param_out, void* master_out, S* m_out, S* v_out, int64_t t,
+                    double lr, double b1, double b2, double eps, double wd,
+                    const uint8_t* decay, const double* clip_sumsq, double max_norm) {
+  const StepConsts<S> c = step_consts<S>(lr, b1, b2, eps, wd, t);
+  const bool clip = clip_sumsq != nullptr;
+  const S coef = clip ? (S)clip_factor(*clip_sumsq, max_norm) : (S)1;
+  const size_t pbytes = mode == MODE_F64 ? 8 : (mode == MODE_F32 ? 4 : 2);
+  std::memcpy(param_out, param_in, (size_t)n * pbytes);
+  const int64_t r0 = r < 0 ? 0 : r, r1 = r < 0 ? N : r + 1;
+  for (int64_t k = r0; k < r1; ++k) {
+    int64_t a, b;
+    split_bounds(n, N, k, &a, &b);
+    const int64_t len = b - a;
+    const int64_t base = r < 0 ? 0 : a;  // index of element a in mean/states
+    std::vector<S> g(len), w(len), m(len), v(len);
+    std::vector<uint8_t> dec;
+    for (int64_t j = 0; j < len; ++j) {
+      g[j] = mean[a - base + j];
+      if (clip) g[j] = g[j] * coef;
+      if (r < 0) w[j] = load_master<S>(param_in, master_in, a + j, mode);
+      else w[j] = ((const S*)master_in)[j];
+      m[j] = m_in[a - base + j];
+      v[j] = v_in[a - base + j];
+    }
+    if (decay) dec.assign(decay + a, decay + b);
+    adam_update<S>(w.data(), g.data(), m.data(), v.data(), len, c,
+                   decay ? dec.data() : nullptr, (S)wd);
+    for (int64_t j = 0; j < len; ++j) {
+      store_param<S>(param_out, a + j, w[(size_t)j], mode);
+      if (r >= 0) ((S*)master_out)[j] = w[(size_t)j];
+      else if (mode == MODE_MIXED) ((float*)master_out)[a + j] = (float)w[(size_t)j];
+      m_out[a - base + j] = m[(size_t)j];
+      v_out[a - base + j] = v[(size_t)j];
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -493,6 +597,46 @@ int orc_rank_step(int mode, int64_t n, int64_t N, int64_t r, const void* param_i
     return -1;
   return 0;
 }
+
+// Materialised reduce-scatter mean (and the squared norm, if sumsq_out).
+// rank < 0: full mode; else rank mode with chunk gradients.
+int orc_mean_grad(int mode, int64_t n, int64_t N, int64_t rank, const void* const* grads,
+                  void* mean_out, double* sumsq_out) {
+  if (n < 0 || N < 1 || rank >= N) return -1;
+  if (mode == MODE_F64)
+    mean_grad<double>(mode, n, N, rank, grads, (double*)mean_out, sumsq_out);
+  else if (mode == MODE_F32 || mode == MODE_MIXED)
+    mean_grad<float>(mode, n, N, rank, grads, (float*)mean_out, sumsq_out);
+  else
+    return -1;
+  return 0;
+}
+
+// The step from a materialised mean gradient; clip_sumsq (nullable) is the
+// global squared norm that sets the clipping factor.
+int orc_step_mean(int mode, int64_t n, int64_t N, int64_t rank, const void* param_in,
+                  const void* mean, const void* master_in, const void* m_in, const void* v_in,
+                  void* param_out, void* master_out, void* m_out, void* v_out, int64_t t,
+                  double lr, double b1, double b2, double eps, double wd, const uint8_t* decay,
+                  const double* clip_sumsq, double max_norm) {
+  if (n < 0 || N < 1 || rank >= N || t < 1) return -1;
+  if (mode == MODE_F64)
+    step_from_mean<double>(mode, n, N, rank, param_in, (const double*)mean, master_in,
+                           (const double*)m_in, (const double*)v_in, param_out, master_out,
+                           (double*)m_out, (double*)v_out, t, lr, b1, b2, eps, wd, decay,
+                           clip_sumsq, max_norm);
+  else if (mode == MODE_F32 || mode == MODE_MIXED)
+    step_from_mean<float>(mode, n, N, rank, param_in, (const float*)mean, master_in,
+                          (const float*)m_in, (const float*)v_in, param_out, master_out,
+                          (float*)m_out, (float*)v_out, t, lr, b1, b2, eps, wd, decay,
+                          clip_sumsq, max_norm);
+  else
+    return -1;
+  return 0;
+}
+
+// The clipping factor for a squared norm (for pins).
+double orc_clip_factor(double sumsq, double max_norm) { return clip_factor(sumsq, max_norm); }
 
 // ---------------------------------------------------------------------------
 // Memory per rank, in bytes: out[0] params, out[1] grads, out[2] optimizer.

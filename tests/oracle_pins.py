@@ -14,6 +14,7 @@ The same pins run against oracle builds with a planted mistake
 (tests/test_oracle_mutants.py) to show each mistake is caught.
 """
 import json
+import math
 import os
 
 import numpy as np
@@ -440,6 +441,115 @@ def pin_memory_closed_forms(O):
     assert lo <= d["optimizer"] / d["total"] <= hi
 
 
+# ---------------------------------------------------------------------------
+# Materialised mean gradient and global-norm clipping
+# ---------------------------------------------------------------------------
+def pin_mean_grad_worked_example(O):
+    """ZeRO-Sharded Adam Step, section 'The step': the reduce-scatter gives worker 0
+    [0.3, 0.2, 0.4] and worker 1 [0.0, 2.0]; their squared norms sum to 4.29."""
+    g = _golden("p2_worked_example.json")
+    grads = [np.array(x, np.float64) for x in g["grads"]]
+    mean, ss = O.mean_grad(MODE_F64, g["n"], g["n_workers"], grads)
+    printed = np.concatenate([np.array(x) for x in g["shard_means"]])
+    assert np.allclose(mean, printed, rtol=0, atol=1e-15), mean
+    assert abs(ss - float(np.sum(printed ** 2))) <= 1e-14
+    for r, part in enumerate(g["shard_means"]):
+        chunks = [x[slice(*O.split_bounds(g["n"], g["n_workers"], r))] for x in grads]
+        mr, sr = O.mean_grad(MODE_F64, g["n"], g["n_workers"], chunks, rank=r)
+        assert np.allclose(mr, part, rtol=0, atol=1e-15)
+        assert abs(sr - float(np.sum(np.array(part) ** 2))) <= 1e-14
+
+
+def pin_mean_grad_sumsq_exact_sum(O):
+    """The squared norm of fp32 mean gradients: every square is exact in double, so
+    math.fsum (a correctly rounded sum) gives the exact sum rounded once; the
+    oracle's plain double sum is within (n-1) * 2^-53 of it relatively."""
+    import math
+    rng = np.random.default_rng(21)
+    for n, N in ((100_003, 8), (4099, 3), (1000, 64)):
+        grads = [(1e-3 * rng.standard_normal(n)).astype(np.float32) for _ in range(N)]
+        mean, ss = O.mean_grad(MODE_F32, n, N, grads)
+        exact = math.fsum(float(x) * float(x) for x in mean.astype(np.float64))
+        assert abs(ss - exact) <= (n - 1) * 2.0 ** -53 * exact, (ss, exact)
+        # rank mode: each shard's partial, and their rank-order sum is the total
+        total = 0.0
+        for r in range(N):
+            a, b = O.split_bounds(n, N, r)
+            mr, sr = O.mean_grad(MODE_F32, n, N, [x[a:b] for x in grads], rank=r)
+            assert np.array_equal(mr, mean[a:b])
+            total = total + sr
+        assert total == ss
+
+
+def pin_step_from_mean_equals_step(O):
+    """Materialising the reduce-scatter output does not change the arithmetic: the
+    step from the mean gradient, unclipped or clipped with a threshold the norm does
+    not reach, equals the fused step bit for bit, in every mode."""
+    rng = np.random.default_rng(22)
+    for mode in (MODE_F64, MODE_F32, MODE_MIXED):
+        n, N = 3001, 5
+        w, grads = _case_for_mode(rng, mode, n, N)
+        mst, m, v = O.init_states(mode, w)
+        flags = (rng.random(n) < 0.5).astype(np.uint8)
+        ref = O.zero_step(mode, w, grads, mst, m, v, 3, 1e-3, 0.9, 0.95, 1e-8, 0.1, decay=flags)
+        mean, ss = O.mean_grad(mode, n, N, grads)
+        for clip in (None, 10.0 * math.sqrt(ss) + 1.0):
+            got = O.step_mean(mode, N, w, mean, mst, m, v, 3, 1e-3, 0.9, 0.95, 1e-8, 0.1,
+                              decay=flags, clip_sumsq=None if clip is None else ss,
+                              max_norm=clip or 0.0)
+            for x, y in zip(got, ref):
+                if x is not None:
+                    assert np.array_equal(x.view(np.uint8), y.view(np.uint8)), (mode, clip)
+
+
+def pin_clipping_vs_torch(O):
+    """One worker: clipping by the global norm then Adam/AdamW equals
+    torch.nn.utils.clip_grad_norm_ followed by torch.optim (fp64), with the
+    threshold crossed on some steps and not on others."""
+    import torch
+    rng = np.random.default_rng(23)
+    n, T = 257, 8
+    for wd, adamw in ((0.0, False), (0.1, True)):
+        w0 = rng.standard_normal(n)
+        gseq = [rng.standard_normal(n) * (3.0 if t % 2 else 0.2) for t in range(T)]
+        max_norm = 5.0
+        p = torch.nn.Parameter(torch.tensor(w0))
+        cls = torch.optim.AdamW if adamw else torch.optim.Adam
+        opt = cls([p], lr=1e-2, betas=(0.9, 0.95), eps=1e-8, weight_decay=wd, foreach=False)
+        _, m, v = O.init_states(MODE_F64, w0)
+        w = w0
+        clipped = 0
+        for t, g in enumerate(gseq, 1):
+            p.grad = torch.tensor(g)
+            tn = float(torch.nn.utils.clip_grad_norm_([p], max_norm, foreach=False))
+            opt.step()
+            mean, ss = O.mean_grad(MODE_F64, n, 1, [g])
+            assert abs(math.sqrt(ss) - tn) <= 1e-13 * tn
+            clipped += tn > max_norm
+            w, _, m, v = O.step_mean(MODE_F64, 1, w, mean, None, m, v, t, 1e-2, 0.9, 0.95, 1e-8,
+                                     wd, clip_sumsq=ss, max_norm=max_norm)
+            tw = p.detach().numpy()
+            assert np.allclose(w, tw, rtol=1e-12, atol=1e-14), (t, np.max(np.abs(w - tw)))
+        assert 0 < clipped < T
+
+
+def pin_clipping_closed_form(O):
+    """With clipping active at t = 1, m1 = (1-b1) * c * gbar with
+    c = max_norm / (|gbar| + 1e-6), so |m1| / (1-b1) = max_norm |gbar| / (|gbar| + 1e-6)."""
+    rng = np.random.default_rng(24)
+    n, N = 5000, 4
+    w, grads = _rand_case(rng, n, N)
+    mean, ss = O.mean_grad(MODE_F64, n, N, grads)
+    norm = math.sqrt(ss)
+    for max_norm in (0.5, 0.01 * norm):
+        _, m0, v0 = O.init_states(MODE_F64, w)
+        _, _, m1, _ = O.step_mean(MODE_F64, N, w, mean, None, m0, v0, 1, 1e-3, 0.9, 0.999, 1e-8,
+                                  clip_sumsq=ss, max_norm=max_norm)
+        got = np.linalg.norm(m1) / 0.1
+        assert abs(got - max_norm * norm / (norm + 1e-6)) <= 1e-12 * max_norm
+    assert O.clip_factor(4.0, 100.0) == 1.0
+
+
 ALL_PINS = [
     pin_p2_worked_example,
     pin_p1_worked_example,
@@ -457,4 +567,9 @@ ALL_PINS = [
     pin_mixed_precision,
     pin_memory_byte_table,
     pin_memory_closed_forms,
+    pin_mean_grad_worked_example,
+    pin_mean_grad_sumsq_exact_sum,
+    pin_step_from_mean_equals_step,
+    pin_clipping_vs_torch,
+    pin_clipping_closed_form,
 ]

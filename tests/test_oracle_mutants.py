@@ -6,7 +6,8 @@ starting from the wrong chunk, no all-gather after the update, stage 2 keeping t
 full gradients, dropped hyperparameters) plus plausible slips in the Adam formula
 itself (exchanged betas, a dropped bias correction, eps inside the square root,
 coupled instead of decoupled decay, a wrong sign, an off-by-one step count, an
-inverted decay mask, truncating instead of rounding to bf16). The mistakes are
+inverted decay mask, truncating instead of rounding to bf16, an unclamped or
+wrongly normed clipping factor). The mistakes are
 planted in the oracle on the CPU only.
 """
 import pytest
@@ -29,6 +30,8 @@ MUTANTS = {
     12: "decay mask inverted",
     13: "stage 2 counts full grads",
     14: "off-by-one step in bias correction",
+    15: "clipping factor not clamped at 1",
+    16: "1-norm instead of squared norm",
 }
 
 
