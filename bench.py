@@ -47,6 +47,14 @@ def bytes_per_param(wl):
     return b
 
 
+def bytes_per_param_clipped(wl):
+    """The clipped step moves the fused step's bytes plus the materialised mean
+    gradient, written once by the reduce-scatter kernel and read once by the step
+    kernel (2 * sizeof(S)); the per-block partial sums are negligible."""
+    s = 8 if wl.mode == 0 else 4
+    return bytes_per_param(wl) + 2 * s
+
+
 def kernel_hash():
     with open(KERNEL_SRC, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
@@ -213,6 +221,9 @@ def main():
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--clip", type=float, default=None, metavar="FRACTION",
+                    help="time the clipped step (zero_step_clipped) with max_norm set to "
+                         "FRACTION times the first step's global gradient norm")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     ap.add_argument("--kt-summary", metavar="KT_DIR",
@@ -261,8 +272,29 @@ def main():
     grads = synth.make_grads(wl, 1, "cuda")
     torch.cuda.synchronize()
 
+    max_norm = None
+    if args.clip is not None:
+        if wl.rank >= 0:
+            print("--clip needs a full-mode workload", file=sys.stderr)
+            sys.exit(2)
+        ss = torch.zeros(1, dtype=torch.float64, device="cuda")
+        mean = torch.empty(L, dtype=sdt, device="cuda")
+        ws = torch.empty(max(1, z.zero_mean_grad_workspace_bytes(hp)), dtype=torch.uint8,
+                         device="cuda")
+        z.zero_mean_grad(hp, grads, mean, ss, ws)
+        max_norm = args.clip * float(ss.item()) ** 0.5
+        del mean, ws
+        ws = torch.empty(z.zero_step_clipped_workspace_bytes(hp), dtype=torch.uint8, device="cuda")
+
+    def one_step(t, stream=None):
+        if max_norm is None:
+            z.zero_step(hp, param, grads, st, t, stream=stream)
+        else:
+            z.zero_step_clipped(hp, param, grads, st, t, max_norm, ws, sumsq_out=ss,
+                                stream=stream)
+
     for t in range(1, args.warmup + 1):
-        z.zero_step(hp, param, grads, st, t)
+        one_step(t)
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
@@ -272,17 +304,17 @@ def main():
     t0 = time.perf_counter()
     for i in range(args.steps):
         ev[i][0].record(stream)
-        z.zero_step(hp, param, grads, st, args.warmup + 1 + i, stream=stream)
+        one_step(args.warmup + 1 + i, stream=stream)
         ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kern_ms = [s.elapsed_time(e) for s, e in ev]
     avg_ms = sum(kern_ms) / len(kern_ms)
 
-    bpp = bytes_per_param(wl)
+    bpp = bytes_per_param(wl) if max_norm is None else bytes_per_param_clipped(wl)
     algo_bytes = bpp * L
     achieved = algo_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name, algo_bytes)
+    traffic = load_traffic(wl.name, algo_bytes) if max_norm is None else None
     dtype = {0: "f64", 1: "f32", 2: "bf16+f32"}[wl.mode]
 
     del grads, param, st
@@ -306,7 +338,9 @@ def main():
         "config": {"workload": wl.name, "params_updated_per_step": L, "n_workers": wl.n_workers,
                    "mode": dtype, "rank": wl.rank, "lr": wl.lr, "betas": [wl.beta1, wl.beta2],
                    "eps": wl.eps, "weight_decay": wl.weight_decay, "decay": wl.decay,
-                   "bytes_per_param": bpp, "parallelism": "1 GPU, N logical workers in one HBM"},
+                   "bytes_per_param": bpp, "parallelism": "1 GPU, N logical workers in one HBM",
+                   **({} if max_norm is None else
+                      {"clipped": True, "clip_fraction": args.clip, "max_norm": max_norm})},
         "achieved_GBps": achieved,
         "kernel_ms_mean": avg_ms,
         "kernel_ms_min": min(kern_ms),

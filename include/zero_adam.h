@@ -46,6 +46,7 @@
 #ifndef ZERO_ADAM_H
 #define ZERO_ADAM_H
 
+#include <stddef.h>
 #include <stdint.h>
 
 #ifdef __cplusplus
@@ -147,6 +148,62 @@ zero_status zero_init_states(const zero_hparams* hp, const void* param,
  * mode/master mismatch, or reserved != 0; ZERO_EHIP if the launch fails. */
 zero_status zero_step(const zero_hparams* hp, void* param, const void* const* grads,
                       const zero_states* states, int64_t t, void* stream);
+
+/* ---- The materialised reduce-scatter mean and global-norm clipping ----------
+ * "Data parallelism and ZeRO stages 1 to 3", section "2. Principles": stage 1
+ * keeps the averaged gradient in .grad ("Your emulation's bookkeeping"), and
+ * the reduce-scatter of stage 2 leaves each rank its chunk of it; section
+ * "Going further": sharded global-norm clipping is an all-reduce of the
+ * squared chunk norms before the step. The clipping factor is
+ * min(1, max_norm / (sqrt(sumsq) + 1e-6)) in double (the definition torch's
+ * clip_grad_norm_ uses), rounded once to S and multiplied into the mean
+ * gradient before the moments. The squared norm is summed in double in a fixed
+ * order that depends only on n and the mode (block sums, then the blocks in
+ * order), so it is the same on every run; it may differ from another summation
+ * order in the last bits. */
+
+/* Device workspace bytes zero_mean_grad needs when sumsq_out is non-NULL. */
+zero_status zero_mean_grad_workspace_bytes(const zero_hparams* hp, size_t* bytes);
+
+/* The reduce-scatter mean of the call's range, materialised: mean_out[j] for
+ * the call's elements (full mode: n; rank mode: c_r of worker `rank`, from its
+ * N chunk gradients), in S, computed exactly as zero_step computes it (rank-order
+ * left fold, one division by N). If sumsq_out is non-NULL (a device double),
+ * also writes the range's squared norm sum(mean^2) there, using `workspace`
+ * (16-byte aligned, >= zero_mean_grad_workspace_bytes). In rank mode that is
+ * this shard's squared norm: the caller sums the ranks' values (the all-reduce)
+ * before zero_step_mean. mean_out is 16-byte aligned and must not overlap the
+ * gradients, the workspace or sumsq_out. Only hp's shape fields are used.
+ * Errors as zero_step. */
+zero_status zero_mean_grad(const zero_hparams* hp, const void* const* grads, void* mean_out,
+                           double* sumsq_out, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* The step driven by a materialised mean gradient (mean_grad: the call's len
+ * elements of S, 16-byte aligned, read-only), otherwise as zero_step. If
+ * clip_sumsq is non-NULL it points to the global squared norm (device double)
+ * and the mean is scaled by the clipping factor for max_norm (finite, > 0).
+ * Unclipped, or with a factor of exactly 1, the result is bit-identical to
+ * zero_step on the gradients that produced the mean. */
+zero_status zero_step_mean(const zero_hparams* hp, void* param, const void* mean_grad,
+                           const zero_states* states, int64_t t, const double* clip_sumsq,
+                           double max_norm, void* stream);
+
+/* Device workspace bytes zero_step_clipped needs: the mean gradient (n values
+ * of S), the block partial sums and the squared norm. */
+zero_status zero_step_clipped_workspace_bytes(const zero_hparams* hp, size_t* bytes);
+
+/* One clipped step, full mode: the materialised mean, its global squared norm
+ * (also written to sumsq_out if non-NULL), and the step with the clipping
+ * factor for max_norm, all enqueued on `stream`. Rank mode returns
+ * ZERO_EUNSUPPORTED: a rank alone does not hold the other shards' norms (use
+ * zero_mean_grad, sum the ranks' squared norms, then zero_step_mean). The
+ * workspace (16-byte aligned, >= zero_step_clipped_workspace_bytes) and
+ * sumsq_out must not overlap any buffer the step reads or writes. */
+zero_status zero_step_clipped(const zero_hparams* hp, void* param, const void* const* grads,
+                              const zero_states* states, int64_t t, double max_norm,
+                              double* sumsq_out, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /* Per-rank memory in bytes ("Data parallelism and ZeRO stages 1 to 3",
  * section "2. Principles", table and "Your emulation's bookkeeping"; "Data

@@ -249,3 +249,56 @@ def test_wd_mask_packing():
     assert w.size == 3
     bits = [(int(w[i // 32]) >> (i % 32)) & 1 for i in range(70)]
     assert bits == flags.astype(int).tolist()
+
+
+# -- mean gradient and clipping entry points (host validation) -----------------
+def test_workspace_sizes_follow_the_launch_geometry():
+    lib = _abi.load()
+    out = C.c_size_t()
+    hp = _hp(n=1_000_000, n_workers=8, mode=z.ZERO_MODE_F32)
+    assert lib.zero_mean_grad_workspace_bytes(C.byref(hp), C.byref(out)) == z.ZERO_OK
+    mean_ws = out.value
+    assert mean_ws % 8 == 0 and mean_ws >= 8
+    assert lib.zero_step_clipped_workspace_bytes(C.byref(hp), C.byref(out)) == z.ZERO_OK
+    assert out.value >= 4 * 1_000_000 + mean_ws + 8
+    hp0 = _hp(n=3, n_workers=5, rank=4)  # empty shard: one partial
+    assert lib.zero_mean_grad_workspace_bytes(C.byref(hp0), C.byref(out)) == z.ZERO_OK
+    assert out.value == 8
+
+
+def test_clipped_step_rejects_rank_mode_and_bad_max_norm():
+    lib = _abi.load()
+    st = _abi.zero_states(master=A + (9 << 24), m=A + (1 << 24), v=A + (2 << 24))
+    arr = (C.c_void_p * 4)(*[A + ((3 + k) << 24) for k in range(4)])
+    hp = _hp(rank=1)
+    rc = lib.zero_step_clipped(C.byref(hp), A, arr, C.byref(st), 1, 1.0, None, A + (20 << 24),
+                               1 << 24, None)
+    assert rc == z.ZERO_EUNSUPPORTED
+    st = _abi.zero_states(master=None, m=A + (1 << 24), v=A + (2 << 24))
+    for bad in (0.0, -1.0, float("nan"), float("inf")):
+        rc = lib.zero_step_clipped(C.byref(_hp()), A, arr, C.byref(st), 1, bad, None,
+                                   A + (20 << 24), 1 << 24, None)
+        assert rc == z.ZERO_EINVAL, bad
+    # workspace too small, misaligned, overlapping m
+    for ws, nb in ((A + (20 << 24), 16), (A + (20 << 24) + 4, 1 << 24), (A + (1 << 24), 1 << 24)):
+        rc = lib.zero_step_clipped(C.byref(_hp()), A, arr, C.byref(st), 1, 1.0, None, ws, nb, None)
+        assert rc == z.ZERO_EINVAL, (ws, nb)
+
+
+def test_step_mean_and_mean_grad_reject():
+    lib = _abi.load()
+    st = _abi.zero_states(master=None, m=A + (1 << 24), v=A + (2 << 24))
+    hp = _hp()
+    # clipping with a bad max_norm; mean overlapping m
+    assert lib.zero_step_mean(C.byref(hp), A, A + (5 << 24), C.byref(st), 1, A + (7 << 24), 0.0,
+                              None) == z.ZERO_EINVAL
+    assert lib.zero_step_mean(C.byref(hp), A, A + (1 << 24), C.byref(st), 1, None, 0.0,
+                              None) == z.ZERO_EINVAL
+    assert lib.zero_step_mean(C.byref(hp), A, A + (5 << 24) + 8, C.byref(st), 1, None, 0.0,
+                              None) == z.ZERO_EINVAL
+    arr = (C.c_void_p * 4)(*[A + ((3 + k) << 24) for k in range(4)])
+    # mean_out misaligned / overlapping a gradient; workspace missing for a norm
+    assert lib.zero_mean_grad(C.byref(hp), arr, A + 4, None, None, 0, None) == z.ZERO_EINVAL
+    assert lib.zero_mean_grad(C.byref(hp), arr, A + (3 << 24), None, None, 0, None) == z.ZERO_EINVAL
+    assert lib.zero_mean_grad(C.byref(hp), arr, A, A + (9 << 24), None, 0, None) == z.ZERO_EINVAL
+    assert lib.zero_mean_grad(C.byref(_hp(n=0)), arr, A, None, None, 0, None) == z.ZERO_EINVAL

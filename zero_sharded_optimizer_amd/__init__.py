@@ -13,6 +13,13 @@ workers sharing one GPU:
   zero_init_states(hp, param, states)   -> m = v = 0, master from param
   zero_step(hp, param, grads, states, t) -> one reduce-scatter-mean / Adam /
                                             all-gather step, in place
+  zero_mean_grad(hp, grads, mean, sumsq)  -> the reduce-scatter mean, materialised,
+                                            and its squared norm
+  zero_step_mean(hp, param, mean, states, t, clip_sumsq, max_norm)
+                                         -> the step from a materialised mean,
+                                            optionally clipped by the global norm
+  zero_step_clipped(hp, param, grads, states, t, max_norm, sumsq, workspace)
+                                         -> both, as one clipped step
   zero_memory_bytes(...)                 -> per-rank memory by ZeRO stage
   zero_shard_bounds(n, N, r)             -> np.array_split shard [a, b)
 """
@@ -28,6 +35,8 @@ from ._abi import (ZERO_EHIP, ZERO_EINVAL, ZERO_EUNSUPPORTED, ZERO_MAX_WORKERS, 
 
 __all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
            "zero_memory_bytes", "zero_shard_bounds", "zero_last_error", "wd_mask_from_flags",
+           "zero_mean_grad_workspace_bytes", "zero_mean_grad", "zero_step_mean",
+           "zero_step_clipped_workspace_bytes", "zero_step_clipped",
            "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MAX_WORKERS"]
 
 
@@ -174,6 +183,112 @@ def zero_step(hp: HParams, param, grads: Sequence, states: States, t: int, strea
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
     st = lib.zero_step(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t),
                        _stream_handle(stream, states.m))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+def _check_double(x, what):
+    if x is None or isinstance(x, int):
+        return
+    _check_tensor(x, "float64", 1, what)
+
+
+def _check_bytes(x, nbytes, what):
+    """A workspace tensor: any dtype, contiguous, on the GPU, >= nbytes."""
+    if x is None or isinstance(x, int):
+        return
+    import torch
+    if not isinstance(x, torch.Tensor) or not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{what}: must be a contiguous GPU tensor")
+    if x.numel() * x.element_size() < nbytes:
+        raise ValueError(f"{what}: {x.numel() * x.element_size()} bytes, needs {nbytes}")
+
+
+def _nbytes(x):
+    if x is None or isinstance(x, int):
+        return 1 << 62 if isinstance(x, int) else 0
+    return x.numel() * x.element_size()
+
+
+def zero_mean_grad_workspace_bytes(hp: HParams) -> int:
+    lib = _abi.load()
+    out = C.c_size_t()
+    c_hp = hp.to_c()
+    st = lib.zero_mean_grad_workspace_bytes(C.byref(c_hp), C.byref(out))
+    if st != ZERO_OK:
+        _raise(st)
+    return out.value
+
+
+def zero_mean_grad(hp: HParams, grads: Sequence, mean_out, sumsq_out=None, workspace=None,
+                   stream=None) -> None:
+    """Enqueue the materialised reduce-scatter mean (and squared norm)."""
+    if hp.mode in _DTYPES and hp.n >= 1 and 1 <= hp.n_workers and -1 <= hp.rank < hp.n_workers:
+        _, g_dt, s_dt = _DTYPES[hp.mode]
+        a, b = _shard_len(hp)
+        if len(grads) != hp.n_workers:
+            raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
+        for k, g in enumerate(grads):
+            _check_tensor(g, g_dt, b - a, f"grads[{k}]")
+        _check_tensor(mean_out, s_dt, b - a, "mean_out")
+        _check_double(sumsq_out, "sumsq_out")
+        if sumsq_out is not None:
+            _check_bytes(workspace, zero_mean_grad_workspace_bytes(hp), "workspace")
+    lib = _abi.load()
+    c_hp = hp.to_c()
+    arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
+    st = lib.zero_mean_grad(C.byref(c_hp), arr, _addr(mean_out), _addr(sumsq_out),
+                            _addr(workspace), _nbytes(workspace),
+                            _stream_handle(stream, mean_out if mean_out is not None else grads[0]))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+def zero_step_mean(hp: HParams, param, mean_grad, states: States, t: int, clip_sumsq=None,
+                   max_norm: float = 0.0, stream=None) -> None:
+    """Enqueue the step from a materialised mean gradient (optionally clipped)."""
+    chk = _check_common(hp, param, states)
+    if chk is not None:
+        _, glen = chk
+        _check_tensor(mean_grad, _DTYPES[hp.mode][2], glen, "mean_grad")
+        _check_double(clip_sumsq, "clip_sumsq")
+    lib = _abi.load()
+    c_hp, c_st = hp.to_c(), states.to_c()
+    st = lib.zero_step_mean(C.byref(c_hp), _addr(param), _addr(mean_grad), C.byref(c_st), int(t),
+                            _addr(clip_sumsq), float(max_norm), _stream_handle(stream, states.m))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+def zero_step_clipped_workspace_bytes(hp: HParams) -> int:
+    lib = _abi.load()
+    out = C.c_size_t()
+    c_hp = hp.to_c()
+    st = lib.zero_step_clipped_workspace_bytes(C.byref(c_hp), C.byref(out))
+    if st != ZERO_OK:
+        _raise(st)
+    return out.value
+
+
+def zero_step_clipped(hp: HParams, param, grads: Sequence, states: States, t: int,
+                      max_norm: float, workspace, sumsq_out=None, stream=None) -> None:
+    """Enqueue one clipped step (full mode): mean, global squared norm, step."""
+    chk = _check_common(hp, param, states)
+    if chk is not None:
+        g_dt, glen = chk
+        if len(grads) != hp.n_workers:
+            raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
+        for k, g in enumerate(grads):
+            _check_tensor(g, g_dt, glen, f"grads[{k}]")
+        _check_double(sumsq_out, "sumsq_out")
+        if hp.rank < 0:
+            _check_bytes(workspace, zero_step_clipped_workspace_bytes(hp), "workspace")
+    lib = _abi.load()
+    c_hp, c_st = hp.to_c(), states.to_c()
+    arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
+    st = lib.zero_step_clipped(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t),
+                               float(max_norm), _addr(sumsq_out), _addr(workspace),
+                               _nbytes(workspace), _stream_handle(stream, states.m))
     if st != ZERO_OK:
         _raise(st)
 

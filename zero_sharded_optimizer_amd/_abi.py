@@ -50,7 +50,8 @@ class zero_mem(C.Structure):
 
 
 EXPORTED = ("zero_init_states", "zero_step", "zero_memory_bytes", "zero_shard_bounds",
-            "zero_last_error")
+            "zero_last_error", "zero_mean_grad_workspace_bytes", "zero_mean_grad",
+            "zero_step_mean", "zero_step_clipped_workspace_bytes", "zero_step_clipped")
 
 _lib = None
 
@@ -79,6 +80,22 @@ def load(path=None):
     lib.zero_shard_bounds.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.POINTER(C.c_int64),
                                       C.POINTER(C.c_int64)]
     lib.zero_shard_bounds.restype = C.c_int
+    lib.zero_mean_grad_workspace_bytes.argtypes = [C.POINTER(zero_hparams), C.POINTER(C.c_size_t)]
+    lib.zero_mean_grad_workspace_bytes.restype = C.c_int
+    lib.zero_mean_grad.argtypes = [C.POINTER(zero_hparams), C.POINTER(C.c_void_p), C.c_void_p,
+                                   C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.zero_mean_grad.restype = C.c_int
+    lib.zero_step_mean.argtypes = [C.POINTER(zero_hparams), C.c_void_p, C.c_void_p,
+                                   C.POINTER(zero_states), C.c_int64, C.c_void_p, C.c_double,
+                                   C.c_void_p]
+    lib.zero_step_mean.restype = C.c_int
+    lib.zero_step_clipped_workspace_bytes.argtypes = [C.POINTER(zero_hparams),
+                                                      C.POINTER(C.c_size_t)]
+    lib.zero_step_clipped_workspace_bytes.restype = C.c_int
+    lib.zero_step_clipped.argtypes = [C.POINTER(zero_hparams), C.c_void_p, C.POINTER(C.c_void_p),
+                                      C.POINTER(zero_states), C.c_int64, C.c_double, C.c_void_p,
+                                      C.c_void_p, C.c_size_t, C.c_void_p]
+    lib.zero_step_clipped.restype = C.c_int
     lib.zero_last_error.argtypes = []
     lib.zero_last_error.restype = C.c_char_p
     if path is None:

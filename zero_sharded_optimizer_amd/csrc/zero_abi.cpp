@@ -204,14 +204,26 @@ zero_status zero_init_states(const zero_hparams* hp, const void* param, const ze
   return ok();
 }
 
-zero_status zero_step(const zero_hparams* hp, void* param, const void* const* grads,
-                      const zero_states* st, int64_t t, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validates one step call and fills the launch arguments. `grads` holds ngp
+// device pointers whose elements are gelem bytes (the workers' gradients, or
+// the one materialised mean); each holds the call's len elements. Sets *empty
+// for an empty rank shard, when nothing is to be launched.
+zero_status build_step(const zero_hparams* hp, void* param, const void* const* grads, int ngp,
+                       int64_t gelem, const zero_states* st, int64_t t, zlaunch::StepArgs* la,
+                       bool* empty, int64_t* a_out, int64_t* b_out) {
   Widths wd;
   int64_t a = 0, b = 0;
   zero_status s = check_hparams(hp, true, &wd, &a, &b);
   if (s != ZERO_OK) return s;
   if (t < 1) return fail(ZERO_EINVAL, "t must be >= 1 (1-based step number), got %lld", (long long)t);
-  if (b == a) return ok();  // an empty shard: no buffer is touched
+  *empty = b == a;
+  *a_out = a;
+  *b_out = b;
+  if (*empty) return ZERO_OK;  // an empty shard: no buffer is touched
   if ((s = check_states(hp, st, wd)) != ZERO_OK) return s;
   if (param == nullptr) return fail(ZERO_EINVAL, "param is NULL");
   if (grads == nullptr) return fail(ZERO_EINVAL, "grads is NULL");
@@ -219,8 +231,7 @@ zero_status zero_step(const zero_hparams* hp, void* param, const void* const* gr
   if (rank_mode ? !aligned(param, (uintptr_t)wd.param) : !aligned(param, 16))
     return fail(ZERO_EINVAL, rank_mode ? "param must be aligned to its element size"
                                        : "param must be 16-byte aligned");
-  const int N = hp->n_workers;
-  for (int k = 0; k < N; ++k) {
+  for (int k = 0; k < ngp; ++k) {
     if (grads[k] == nullptr) return fail(ZERO_EINVAL, "grads[%d] is NULL", k);
     if (!aligned(grads[k], 16)) return fail(ZERO_EINVAL, "grads[%d] must be 16-byte aligned", k);
   }
@@ -241,8 +252,8 @@ zero_status zero_step(const zero_hparams* hp, void* param, const void* const* gr
         return fail(ZERO_EINVAL, "%s overlaps %s", written[i].name, written[j].name);
   const bool decays = hp->weight_decay != 0.0;
   for (int i = 0; i < nw; ++i) {
-    for (int k = 0; k < N; ++k) {
-      const Range g{(uintptr_t)grads[k], (uintptr_t)grads[k] + (uintptr_t)(len * wd.grad), "grad"};
+    for (int k = 0; k < ngp; ++k) {
+      const Range g{(uintptr_t)grads[k], (uintptr_t)grads[k] + (uintptr_t)(len * gelem), "grad"};
       if (overlaps(written[i], g)) return fail(ZERO_EINVAL, "%s overlaps grads[%d]", written[i].name, k);
     }
     if (decays && hp->wd_mask) {
@@ -252,39 +263,245 @@ zero_status zero_step(const zero_hparams* hp, void* param, const void* const* gr
     }
   }
 
-  zlaunch::StepArgs la;
-  la.mode = hp->mode;
-  la.n_workers = N;
-  for (int k = 0; k < zlaunch::kMaxWorkers; ++k) la.grads[k] = k < N ? grads[k] : nullptr;
-  la.m = st->m;
-  la.v = st->v;
+  *la = zlaunch::StepArgs{};
+  la->mode = hp->mode;
+  la->n_workers = ngp;
+  for (int k = 0; k < ngp; ++k) la->grads[k] = grads[k];
+  la->m = st->m;
+  la->v = st->v;
   if (rank_mode || hp->mode == ZERO_MODE_MIXED_BF16) {
-    la.w = st->master;
-    la.out = static_cast<char*>(param) + a * wd.param;
+    la->w = st->master;
+    la->out = static_cast<char*>(param) + a * wd.param;
   } else {
-    la.w = param;  // updated in place: the parameter is its own master
-    la.out = nullptr;
+    la->w = param;  // updated in place: the parameter is its own master
+    la->out = nullptr;
   }
-  la.len = len;
-  la.decay_kind = !decays ? 0 : (hp->wd_mask ? 2 : 1);
-  la.mask = decays ? hp->wd_mask : nullptr;
-  la.mask_bit_offset = a;
+  la->len = len;
+  la->decay_kind = !decays ? 0 : (hp->wd_mask ? 2 : 1);
+  la->mask = decays ? hp->wd_mask : nullptr;
+  la->mask_bit_offset = a;
   // Step scalars: formed in double, rounded to the state type by the launch.
   const double tt = (double)t;
-  la.beta1 = hp->beta1;
-  la.beta2 = hp->beta2;
-  la.one_minus_beta1 = 1.0 - hp->beta1;
-  la.one_minus_beta2 = 1.0 - hp->beta2;
-  la.bias1 = 1.0 - std::pow(hp->beta1, tt);
-  la.bias2 = 1.0 - std::pow(hp->beta2, tt);
-  la.lr = hp->lr;
-  la.eps = hp->eps;
-  la.decay_factor = 1.0 - hp->lr * hp->weight_decay;
-  la.n_workers_value = (double)N;
-  if (!(la.bias1 > 0.0) || !(la.bias2 > 0.0))
+  la->beta1 = hp->beta1;
+  la->beta2 = hp->beta2;
+  la->one_minus_beta1 = 1.0 - hp->beta1;
+  la->one_minus_beta2 = 1.0 - hp->beta2;
+  la->bias1 = 1.0 - std::pow(hp->beta1, tt);
+  la->bias2 = 1.0 - std::pow(hp->beta2, tt);
+  la->lr = hp->lr;
+  la->eps = hp->eps;
+  la->decay_factor = 1.0 - hp->lr * hp->weight_decay;
+  la->n_workers_value = (double)ngp;
+  la->clip_sumsq = nullptr;
+  la->max_norm = 0.0;
+  if (!(la->bias1 > 0.0) || !(la->bias2 > 0.0))
     return fail(ZERO_EINVAL, "bias correction 1 - beta^t is not positive (beta = 0 is fine; "
                              "check beta and t)");
+  return ZERO_OK;
+}
+
+int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Workspace of zero_step_clipped: the mean gradient, the block partials, the
+// squared norm.
+struct ClipLayout {
+  int64_t mean_off, partials_off, sumsq_off, total;
+};
+ClipLayout clip_layout(int mode, int64_t len, int64_t state_bytes) {
+  ClipLayout l;
+  l.mean_off = 0;
+  l.partials_off = align_up(len * state_bytes, 256);
+  l.sumsq_off = l.partials_off + align_up(zlaunch::mean_partials(mode, len) * 8, 256);
+  l.total = l.sumsq_off + 8;
+  return l;
+}
+
+zero_status check_max_norm(double max_norm) {
+  if (!(std::isfinite(max_norm) && max_norm > 0.0))
+    return fail(ZERO_EINVAL, "max_norm must be finite and > 0");
+  return ZERO_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+zero_status zero_step(const zero_hparams* hp, void* param, const void* const* grads,
+                      const zero_states* st, int64_t t, void* stream) {
+  zlaunch::StepArgs la;
+  bool empty = false;
+  int64_t a, b;
+  if (hp == nullptr) return fail(ZERO_EINVAL, "hparams is NULL");
+  Widths wd;
+  if (!mode_widths(hp->mode, &wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
+  const int N = hp->n_workers >= 1 && hp->n_workers <= ZERO_MAX_WORKERS ? hp->n_workers : 0;
+  zero_status s = build_step(hp, param, grads, N, wd.grad, st, t, &la, &empty, &a, &b);
+  if (s != ZERO_OK || empty) return s == ZERO_OK ? ok() : s;
   const char* err = zlaunch::launch_step(la, stream);
+  if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
+  return ok();
+}
+
+zero_status zero_mean_grad_workspace_bytes(const zero_hparams* hp, size_t* bytes) {
+  Widths wd;
+  int64_t a = 0, b = 0;
+  if (bytes == nullptr) return fail(ZERO_EINVAL, "bytes is NULL");
+  zero_status s = check_hparams(hp, false, &wd, &a, &b);
+  if (s != ZERO_OK) return s;
+  *bytes = (size_t)(zlaunch::mean_partials(hp->mode, b - a) * 8);
+  return ok();
+}
+
+zero_status zero_mean_grad(const zero_hparams* hp, const void* const* grads, void* mean_out,
+                           double* sumsq_out, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  Widths wd;
+  int64_t a = 0, b = 0;
+  zero_status s = check_hparams(hp, false, &wd, &a, &b);
+  if (s != ZERO_OK) return s;
+  const int64_t len = b - a;
+  const int N = hp->n_workers;
+  const int64_t need = zlaunch::mean_partials(hp->mode, len) * 8;
+  if (sumsq_out != nullptr) {
+    if (!aligned(sumsq_out, 8)) return fail(ZERO_EINVAL, "sumsq_out must be 8-byte aligned");
+    if (workspace == nullptr || !aligned(workspace, 16) || (int64_t)workspace_bytes < need)
+      return fail(ZERO_EINVAL, "workspace must be 16-byte aligned and hold %lld bytes",
+                  (long long)need);
+  }
+  zlaunch::MeanArgs ma{};
+  ma.mode = hp->mode;
+  ma.n_workers = N;
+  ma.len = len;
+  ma.n_workers_value = (double)N;
+  ma.partials = static_cast<double*>(workspace);
+  ma.sumsq_out = sumsq_out;
+  if (len > 0) {
+    if (grads == nullptr) return fail(ZERO_EINVAL, "grads is NULL");
+    if (mean_out == nullptr || !aligned(mean_out, 16))
+      return fail(ZERO_EINVAL, "mean_out must be non-NULL and 16-byte aligned");
+    const Range rm{(uintptr_t)mean_out, (uintptr_t)mean_out + (uintptr_t)(len * wd.state), "mean_out"};
+    const Range rw{(uintptr_t)workspace,
+                   sumsq_out ? (uintptr_t)workspace + (uintptr_t)need : (uintptr_t)workspace,
+                   "workspace"};
+    const Range rs{(uintptr_t)sumsq_out, sumsq_out ? (uintptr_t)sumsq_out + 8 : 0, "sumsq_out"};
+    for (int k = 0; k < N; ++k) {
+      if (grads[k] == nullptr) return fail(ZERO_EINVAL, "grads[%d] is NULL", k);
+      if (!aligned(grads[k], 16)) return fail(ZERO_EINVAL, "grads[%d] must be 16-byte aligned", k);
+      const Range g{(uintptr_t)grads[k], (uintptr_t)grads[k] + (uintptr_t)(len * wd.grad), "grad"};
+      if (overlaps(rm, g) || overlaps(rw, g) || overlaps(rs, g))
+        return fail(ZERO_EINVAL, "an output overlaps grads[%d]", k);
+    }
+    if (overlaps(rm, rw) || overlaps(rm, rs) || overlaps(rw, rs))
+      return fail(ZERO_EINVAL, "mean_out, workspace and sumsq_out must not overlap");
+    ma.mean = mean_out;
+    for (int k = 0; k < N; ++k) ma.grads[k] = grads[k];
+  }
+  if (len == 0 && sumsq_out == nullptr) return ok();  // an empty shard: nothing to do
+  const char* err = zlaunch::launch_mean(ma, stream);
+  if (err) return fail(ZERO_EHIP, "mean launch failed: %s", err);
+  return ok();
+}
+
+zero_status zero_step_mean(const zero_hparams* hp, void* param, const void* mean_grad,
+                           const zero_states* st, int64_t t, const double* clip_sumsq,
+                           double max_norm, void* stream) {
+  zlaunch::StepArgs la;
+  bool empty = false;
+  int64_t a, b;
+  if (hp == nullptr) return fail(ZERO_EINVAL, "hparams is NULL");
+  Widths wd;
+  if (!mode_widths(hp->mode, &wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
+  if (clip_sumsq != nullptr) {
+    zero_status c = check_max_norm(max_norm);
+    if (c != ZERO_OK) return c;
+    if (!aligned(clip_sumsq, 8)) return fail(ZERO_EINVAL, "clip_sumsq must be 8-byte aligned");
+  }
+  const void* one[1] = {mean_grad};
+  zero_status s = build_step(hp, param, one, 1, wd.state, st, t, &la, &empty, &a, &b);
+  if (s != ZERO_OK || empty) return s == ZERO_OK ? ok() : s;
+  la.clip_sumsq = clip_sumsq;
+  la.max_norm = max_norm;
+  const char* err = zlaunch::launch_step_mean(la, stream);
+  if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
+  return ok();
+}
+
+zero_status zero_step_clipped_workspace_bytes(const zero_hparams* hp, size_t* bytes) {
+  Widths wd;
+  int64_t a = 0, b = 0;
+  if (bytes == nullptr) return fail(ZERO_EINVAL, "bytes is NULL");
+  zero_status s = check_hparams(hp, false, &wd, &a, &b);
+  if (s != ZERO_OK) return s;
+  *bytes = (size_t)clip_layout(hp->mode, b - a, wd.state).total;
+  return ok();
+}
+
+zero_status zero_step_clipped(const zero_hparams* hp, void* param, const void* const* grads,
+                              const zero_states* st, int64_t t, double max_norm,
+                              double* sumsq_out, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  zlaunch::StepArgs la;
+  bool empty = false;
+  int64_t a, b;
+  if (hp == nullptr) return fail(ZERO_EINVAL, "hparams is NULL");
+  if (hp->rank >= 0)
+    return fail(ZERO_EUNSUPPORTED,
+                "a clipped step needs every shard's squared norm; in rank mode use "
+                "zero_mean_grad, sum the ranks' squared norms, then zero_step_mean");
+  Widths wd;
+  if (!mode_widths(hp->mode, &wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
+  zero_status s = check_max_norm(max_norm);
+  if (s != ZERO_OK) return s;
+  const int N = hp->n_workers >= 1 && hp->n_workers <= ZERO_MAX_WORKERS ? hp->n_workers : 0;
+  s = build_step(hp, param, grads, N, wd.grad, st, t, &la, &empty, &a, &b);
+  if (s != ZERO_OK) return s;
+  const int64_t len = b - a;
+  const ClipLayout L = clip_layout(hp->mode, len, wd.state);
+  if (workspace == nullptr || !aligned(workspace, 16) || (int64_t)workspace_bytes < L.total)
+    return fail(ZERO_EINVAL, "workspace must be 16-byte aligned and hold %lld bytes",
+                (long long)L.total);
+  if (sumsq_out != nullptr && !aligned(sumsq_out, 8))
+    return fail(ZERO_EINVAL, "sumsq_out must be 8-byte aligned");
+  // the workspace and sumsq_out must not overlap anything the step reads or writes
+  const Range rw{(uintptr_t)workspace, (uintptr_t)workspace + (uintptr_t)L.total, "workspace"};
+  const Range rs{(uintptr_t)sumsq_out, sumsq_out ? (uintptr_t)sumsq_out + 8 : 0, "sumsq_out"};
+  const Range others[4] = {
+      {(uintptr_t)param, (uintptr_t)param + (uintptr_t)(hp->n * wd.param), "param"},
+      {(uintptr_t)st->m, (uintptr_t)st->m + (uintptr_t)(len * wd.state), "m"},
+      {(uintptr_t)st->v, (uintptr_t)st->v + (uintptr_t)(len * wd.state), "v"},
+      {(uintptr_t)st->master, st->master ? (uintptr_t)st->master + (uintptr_t)(len * wd.state) : 0,
+       "master"}};
+  for (const Range& o : others)
+    if (overlaps(rw, o) || overlaps(rs, o)) return fail(ZERO_EINVAL, "workspace/sumsq_out overlaps %s", o.name);
+  if (overlaps(rw, rs)) return fail(ZERO_EINVAL, "sumsq_out overlaps the workspace");
+  for (int k = 0; k < N; ++k) {
+    const Range g{(uintptr_t)grads[k], (uintptr_t)grads[k] + (uintptr_t)(len * wd.grad), "grad"};
+    if (overlaps(rw, g) || overlaps(rs, g)) return fail(ZERO_EINVAL, "workspace/sumsq_out overlaps grads[%d]", k);
+  }
+  if (hp->wd_mask && hp->weight_decay != 0.0) {
+    const Range mk{(uintptr_t)hp->wd_mask, (uintptr_t)hp->wd_mask + (uintptr_t)(((hp->n + 31) / 32) * 4), "wd_mask"};
+    if (overlaps(rw, mk) || overlaps(rs, mk)) return fail(ZERO_EINVAL, "workspace/sumsq_out overlaps wd_mask");
+  }
+  char* ws = static_cast<char*>(workspace);
+  double* sumsq = sumsq_out ? sumsq_out : reinterpret_cast<double*>(ws + L.sumsq_off);
+  zlaunch::MeanArgs ma{};
+  ma.mode = hp->mode;
+  ma.n_workers = N;
+  for (int k = 0; k < N; ++k) ma.grads[k] = grads[k];
+  ma.mean = ws + L.mean_off;
+  ma.len = len;
+  ma.n_workers_value = (double)N;
+  ma.partials = reinterpret_cast<double*>(ws + L.partials_off);
+  ma.sumsq_out = sumsq;
+  const char* err = zlaunch::launch_mean(ma, stream);
+  if (err) return fail(ZERO_EHIP, "mean launch failed: %s", err);
+  la.n_workers = 1;
+  la.grads[0] = ws + L.mean_off;
+  for (int k = 1; k < zlaunch::kMaxWorkers; ++k) la.grads[k] = nullptr;
+  la.n_workers_value = 1.0;
+  la.clip_sumsq = sumsq;
+  la.max_norm = max_norm;
+  err = zlaunch::launch_step_mean(la, stream);
   if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
   return ok();
 }

@@ -137,6 +137,15 @@ struct ModeMixed {
   static constexpr int VEC = 4;
 };
 
+// The step driven by a materialised fp32 mean gradient in mixed precision:
+// fp32 "gradient" groups, fp32 state, bf16 write-back.
+struct ModeMixedMean {
+  typedef float S;
+  typedef float G;
+  typedef uint16_t P;
+  static constexpr int VEC = 4;
+};
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) {
   return __uint_as_float(h << 16);
 }
@@ -200,6 +209,9 @@ struct GradRaw<ModeMixed> {
   }
 };
 
+template <>
+struct GradRaw<ModeMixedMean> : GradRaw<ModeF32> {};
+
 // State group (VEC elements of S) load / store.
 template <class M>
 struct StateIO;
@@ -229,6 +241,8 @@ struct StateIO<ModeF32> {
 };
 template <>
 struct StateIO<ModeMixed> : StateIO<ModeF32> {};
+template <>
+struct StateIO<ModeMixedMean> : StateIO<ModeF32> {};
 
 // Gathered-parameter write-back of a group to a destination aligned to kAlign.
 template <class M>
@@ -261,6 +275,9 @@ struct OutIO<ModeMixed> {
   __device__ __forceinline__ static uint16_t conv(float x) { return (uint16_t)f32_to_bf16(x); }
 };
 
+template <>
+struct OutIO<ModeMixedMean> : OutIO<ModeMixed> {};
+
 __device__ __forceinline__ float sqrt_rn(float x) { return __builtin_sqrtf(x); }
 __device__ __forceinline__ double sqrt_rn(double x) { return __builtin_sqrt(x); }
 
@@ -270,12 +287,22 @@ __device__ __forceinline__ float grad_elem(const uint16_t* p, int64_t i) {
   return bf16_to_f32(p[i]);
 }
 
+// The global-norm clipping factor min(1, max_norm / (sqrt(sumsq) + 1e-6)), in
+// double (the definition torch's clip_grad_norm_ uses), rounded once to S.
+template <class S>
+__device__ __forceinline__ S clip_coef(const double* __restrict__ sumsq, double max_norm) {
+  const double nrm = __builtin_sqrt(*sumsq);
+  const double cf = max_norm / (nrm + 1e-6);
+  return (S)(cf < 1.0 ? cf : 1.0);
+}
+
 // Steps 2-3 for one element: the moments, bias correction, optional decoupled
 // decay, and the update of the master value w, in the defined order.
 template <class S>
 __device__ __forceinline__ void adam_element(S s, S& w, S& m, S& v, bool decay,
-                                             const Consts<S>& c) {
-  const S gb = s / c.nw;
+                                             const Consts<S>& c, bool clip, S coef) {
+  S gb = s / c.nw;
+  if (clip) gb = gb * coef;
   const S b1m = c.beta1 * m;
   const S g1 = c.omb1 * gb;
   const S m_new = b1m + g1;
@@ -314,11 +341,14 @@ __global__ void __launch_bounds__(BLOCK)
                      typename M::S* __restrict__ m, typename M::S* __restrict__ v,
                      typename M::P* __restrict__ out, int out_vec, int64_t len,
                      Consts<typename M::S> c, const uint32_t* __restrict__ mask,
-                     int64_t mask_off, int decay_kind) {
+                     int64_t mask_off, int decay_kind, const double* __restrict__ clip_sumsq,
+                     double max_norm) {
   typedef typename M::S S;
   constexpr int VEC = M::VEC;
   const int64_t ngroups = len / VEC;
   const int64_t g0 = (int64_t)blockIdx.x * (BLOCK * C) + threadIdx.x;
+  const bool clip = clip_sumsq != nullptr;
+  const S coef = clip ? clip_coef<S>(clip_sumsq, max_norm) : S(1);
   const int N = NFIX > 0 ? NFIX : nw;
   bool live[C];
 #pragma unroll
@@ -375,7 +405,7 @@ __global__ void __launch_bounds__(BLOCK)
     else if (decay_kind == 2) dbits = decay_bits<VEC>(mask, mask_off + g * VEC);
 #pragma unroll
     for (int e = 0; e < VEC; ++e)
-      adam_element<S>(s[u][e], wv[e], mv[e], vv[e], (dbits >> e) & 1u, c);
+      adam_element<S>(s[u][e], wv[e], mv[e], vv[e], (dbits >> e) & 1u, c, clip, coef);
     StateIO<M>::store(m, g, mv);
     StateIO<M>::store(v, g, vv);
     StateIO<M>::store(w, g, wv);
@@ -401,12 +431,127 @@ __global__ void __launch_bounds__(BLOCK)
       const int64_t bit = mask_off + i;
       dec = (mask[bit >> 5] >> (bit & 31)) & 1u;
     }
-    adam_element<S>(sum, wi, mi, vi, dec, c);
+    adam_element<S>(sum, wi, mi, vi, dec, c, clip, coef);
     w[i] = wi;
     m[i] = mi;
     v[i] = vi;
     if (out != nullptr) out[i] = OutIO<M>::conv(wi);
   }
+}
+
+// Deterministic block sum of one double per thread: a butterfly inside each
+// wave, then the waves' totals in wave order. The same inputs in the same
+// threads give the same bits on every run.
+template <int BLOCK>
+__device__ __forceinline__ double block_sum(double x) {
+  static_assert(BLOCK % 64 == 0, "whole waves");
+  __shared__ double wave_tot[BLOCK / 64];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x = x + __shfl_xor(x, off, 64);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) wave_tot[wave] = x;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0) {
+    t = wave_tot[0];
+#pragma unroll
+    for (int k = 1; k < BLOCK / 64; ++k) t = t + wave_tot[k];
+  }
+  return t;  // meaningful in thread 0
+}
+
+// Reduce-scatter mean, materialised: mean[g] for every group of the call's
+// range (the same rank-order fold and division as the step, stored in S), and,
+// if partials != nullptr, each block's sum of the squares of its means in
+// double (squares of fp32 means are exact in double).
+template <class M, int NFIX, int CAP, int BLOCK, int C>
+__global__ void __launch_bounds__(BLOCK)
+    zero_mean_kernel(GradSet<CAP> gs, int nw, typename M::S* __restrict__ mean, int64_t len,
+                     typename M::S nws, double* __restrict__ partials) {
+  typedef typename M::S S;
+  constexpr int VEC = M::VEC;
+  const int64_t ngroups = len / VEC;
+  const int64_t g0 = (int64_t)blockIdx.x * (BLOCK * C) + threadIdx.x;
+  const int N = NFIX > 0 ? NFIX : nw;
+  bool live[C];
+#pragma unroll
+  for (int u = 0; u < C; ++u) live[u] = g0 + (int64_t)u * BLOCK < ngroups;
+
+  S s[C][VEC];
+  if constexpr (NFIX > 0) {
+    GradRaw<M> raw[C][NFIX];
+#pragma unroll
+    for (int u = 0; u < C; ++u)
+#pragma unroll
+      for (int k = 0; k < NFIX; ++k)
+        if (live[u]) raw[u][k].load(gs.p[k], g0 + (int64_t)u * BLOCK);
+#pragma unroll
+    for (int u = 0; u < C; ++u) {
+      raw[u][0].widen(s[u]);
+#pragma unroll
+      for (int k = 1; k < NFIX; ++k) raw[u][k].add(s[u]);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < C; ++u) {
+      GradRaw<M> r0;
+      if (live[u]) r0.load(gs.p[0], g0 + (int64_t)u * BLOCK);
+      r0.widen(s[u]);
+    }
+    for (int k0 = 1; k0 < N; k0 += 8) {
+      GradRaw<M> raw[C][8];
+#pragma unroll
+      for (int u = 0; u < C; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (k0 + j < N && live[u]) raw[u][j].load(gs.p[k0 + j], g0 + (int64_t)u * BLOCK);
+#pragma unroll
+      for (int u = 0; u < C; ++u)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (k0 + j < N) raw[u][j].add(s[u]);
+    }
+  }
+  double sq = 0.0;
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    if (!live[u]) continue;
+    S gb[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      gb[e] = s[u][e] / nws;
+      const double d = (double)gb[e];
+      sq = sq + d * d;
+    }
+    StateIO<M>::store(mean, g0 + (int64_t)u * BLOCK, gb);
+  }
+  // leftover elements, one per thread of block 0
+  const int64_t i = ngroups * VEC + threadIdx.x;
+  if (blockIdx.x == 0 && i < len) {
+    typedef typename M::G G;
+    S sum = grad_elem(reinterpret_cast<const G*>(gs.p[0]), i);
+    for (int k = 1; k < N; ++k) sum = sum + grad_elem(reinterpret_cast<const G*>(gs.p[k]), i);
+    const S gb = sum / nws;
+    mean[i] = gb;
+    const double d = (double)gb;
+    sq = sq + d * d;
+  }
+  if (partials != nullptr) {
+    const double t = block_sum<BLOCK>(sq);
+    if (threadIdx.x == 0) partials[blockIdx.x] = t;
+  }
+}
+
+// Sum of the block partials, in a fixed order: thread t adds partials t,
+// t + 1024, ... in order, then the block sum.
+constexpr int kFinalBlock = 1024;
+__global__ void __launch_bounds__(kFinalBlock)
+    zero_sumsq_finalize(const double* __restrict__ partials, int64_t count,
+                        double* __restrict__ out) {
+  double x = 0.0;
+  for (int64_t k = threadIdx.x; k < count; k += kFinalBlock) x = x + partials[k];
+  const double t = block_sum<kFinalBlock>(x);
+  if (threadIdx.x == 0) *out = t;
 }
 
 // init_states: m = v = 0; master from the gathered parameters when asked.
@@ -493,7 +638,7 @@ void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
                      dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
                      static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
                      out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
-                     a.decay_kind);
+                     a.decay_kind, a.clip_sumsq, a.max_norm);
 }
 
 template <class M>
@@ -506,6 +651,47 @@ void launch_mode(const zlaunch::StepArgs& a, hipStream_t st) {
     default:
       if (a.n_workers <= 64) launch_mode_n<M, 0, 64>(a, st);
       else launch_mode_n<M, 0, zlaunch::kMaxWorkers>(a, st);
+      break;
+  }
+}
+
+template <>
+struct Shape<ModeMixedMean> {
+  static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
+};
+
+template <class M>
+int64_t mean_blocks(int64_t len) {
+  const int64_t per_block = (int64_t)Shape<M>::BLOCK * Shape<M>::C;
+  const int64_t b = (len / M::VEC + per_block - 1) / per_block;
+  return b < 1 ? 1 : b;
+}
+
+template <class M, int NFIX, int CAP>
+void launch_mean_n(const zlaunch::MeanArgs& a, hipStream_t st) {
+  typedef typename M::S S;
+  constexpr int BLOCK = Shape<M>::BLOCK, C = Shape<M>::C;
+  const int64_t blocks = mean_blocks<M>(a.len);
+  GradSet<CAP> gs;
+  for (int k = 0; k < CAP; ++k) gs.p[k] = k < a.n_workers ? a.grads[k] : nullptr;
+  hipLaunchKernelGGL((zero_mean_kernel<M, NFIX, CAP, BLOCK, C>), dim3((unsigned)blocks),
+                     dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.mean), a.len,
+                     (S)a.n_workers_value, a.sumsq_out ? a.partials : nullptr);
+  if (a.sumsq_out)
+    hipLaunchKernelGGL(zero_sumsq_finalize, dim3(1), dim3(kFinalBlock), 0, st, a.partials,
+                       blocks, a.sumsq_out);
+}
+
+template <class M>
+void launch_mean_mode(const zlaunch::MeanArgs& a, hipStream_t st) {
+  switch (a.n_workers) {
+    case 1: launch_mean_n<M, 1, 1>(a, st); break;
+    case 2: launch_mean_n<M, 2, 2>(a, st); break;
+    case 4: launch_mean_n<M, 4, 4>(a, st); break;
+    case 8: launch_mean_n<M, 8, 8>(a, st); break;
+    default:
+      if (a.n_workers <= 64) launch_mean_n<M, 0, 64>(a, st);
+      else launch_mean_n<M, 0, zlaunch::kMaxWorkers>(a, st);
       break;
   }
 }
@@ -533,6 +719,40 @@ const char* launch_step(const StepArgs& a, void* stream) {
     case 0: launch_mode<ModeF64>(a, st); break;
     case 1: launch_mode<ModeF32>(a, st); break;
     case 2: launch_mode<ModeMixed>(a, st); break;
+    default: return "unknown mode";
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? nullptr : hipGetErrorString(e);
+}
+
+const char* launch_step_mean(const StepArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  switch (a.mode) {
+    case 0: launch_mode_n<ModeF64, 1, 1>(a, st); break;
+    case 1: launch_mode_n<ModeF32, 1, 1>(a, st); break;
+    case 2: launch_mode_n<ModeMixedMean, 1, 1>(a, st); break;
+    default: return "unknown mode";
+  }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? nullptr : hipGetErrorString(e);
+}
+
+int64_t mean_partials(int mode, int64_t len) {
+  switch (mode) {
+    case 0: return mean_blocks<ModeF64>(len);
+    case 1: return mean_blocks<ModeF32>(len);
+    default: return mean_blocks<ModeMixed>(len);
+  }
+}
+
+const char* launch_mean(const MeanArgs& a, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  switch (a.mode) {
+    case 0: launch_mean_mode<ModeF64>(a, st); break;
+    case 1: launch_mean_mode<ModeF32>(a, st); break;
+    case 2: launch_mean_mode<ModeMixed>(a, st); break;
     default: return "unknown mode";
   }
   const hipError_t e = hipGetLastError();

@@ -27,6 +27,21 @@ struct StepArgs {
   // Step scalars in double; the launch rounds each once to S.
   double beta1, beta2, one_minus_beta1, one_minus_beta2, bias1, bias2, lr, eps,
       decay_factor, n_workers_value;
+  // Global-norm clipping: device pointer to the squared norm, or nullptr.
+  const double* clip_sumsq;
+  double max_norm;
+};
+
+// The materialised reduce-scatter mean of one call's range.
+struct MeanArgs {
+  int mode;
+  int n_workers;
+  const void* grads[kMaxWorkers];
+  void* mean;            // len elements of S
+  int64_t len;
+  double n_workers_value;
+  double* partials;      // mean_partials(mode, len) doubles, used when sumsq_out
+  double* sumsq_out;     // device double, or nullptr
 };
 
 struct InitArgs {
@@ -41,5 +56,10 @@ struct InitArgs {
 // Each returns nullptr on success, or the HIP runtime's error string.
 const char* launch_step(const StepArgs& a, void* stream);
 const char* launch_init(const InitArgs& a, void* stream);
+// The step with grads = {mean}, one "worker" (the mean is already divided).
+const char* launch_step_mean(const StepArgs& a, void* stream);
+const char* launch_mean(const MeanArgs& a, void* stream);
+// Number of per-block partial sums launch_mean writes for a range of len.
+int64_t mean_partials(int mode, int64_t len);
 
 }  // namespace zlaunch
