@@ -224,6 +224,9 @@ def main():
     ap.add_argument("--clip", type=float, default=None, metavar="FRACTION",
                     help="time the clipped step (zero_step_clipped) with max_norm set to "
                          "FRACTION times the first step's global gradient norm")
+    ap.add_argument("--bucket-mib", type=float, default=None, metavar="MIB",
+                    help="time the bucketed step: zero_step_range over buckets of MIB MiB of "
+                         "one worker's gradient, last bucket first")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     ap.add_argument("--kt-summary", metavar="KT_DIR",
@@ -286,8 +289,18 @@ def main():
         del mean, ws
         ws = torch.empty(z.zero_step_clipped_workspace_bytes(hp), dtype=torch.uint8, device="cuda")
 
+    buckets = None
+    if args.bucket_mib is not None:
+        gbytes = {0: 8, 1: 4, 2: 2}[wl.mode]
+        size = max(8, int(args.bucket_mib * (1 << 20)) // gbytes // 8 * 8)
+        edges = list(range(0, L, size)) + [L]
+        buckets = list(reversed(list(zip(edges[:-1], edges[1:]))))
+
     def one_step(t, stream=None):
-        if max_norm is None:
+        if buckets is not None:
+            for lo, hi in buckets:
+                z.zero_step_range(hp, param, grads, st, t, lo, hi, stream=stream)
+        elif max_norm is None:
             z.zero_step(hp, param, grads, st, t, stream=stream)
         else:
             z.zero_step_clipped(hp, param, grads, st, t, max_norm, ws, sumsq_out=ss,
@@ -314,7 +327,7 @@ def main():
     bpp = bytes_per_param(wl) if max_norm is None else bytes_per_param_clipped(wl)
     algo_bytes = bpp * L
     achieved = algo_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name, algo_bytes) if max_norm is None else None
+    traffic = load_traffic(wl.name, algo_bytes) if max_norm is None and buckets is None else None
     dtype = {0: "f64", 1: "f32", 2: "bf16+f32"}[wl.mode]
 
     del grads, param, st
@@ -340,7 +353,9 @@ def main():
                    "eps": wl.eps, "weight_decay": wl.weight_decay, "decay": wl.decay,
                    "bytes_per_param": bpp, "parallelism": "1 GPU, N logical workers in one HBM",
                    **({} if max_norm is None else
-                      {"clipped": True, "clip_fraction": args.clip, "max_norm": max_norm})},
+                      {"clipped": True, "clip_fraction": args.clip, "max_norm": max_norm}),
+                   **({} if buckets is None else
+                      {"bucket_mib": args.bucket_mib, "buckets": len(buckets)})},
         "achieved_GBps": achieved,
         "kernel_ms_mean": avg_ms,
         "kernel_ms_min": min(kern_ms),

@@ -149,6 +149,22 @@ zero_status zero_init_states(const zero_hparams* hp, const void* param,
 zero_status zero_step(const zero_hparams* hp, void* param, const void* const* grads,
                       const zero_states* states, int64_t t, void* stream);
 
+/* The step on the sub-range [begin, end) of the call's index space (full mode:
+ * [0, n); rank mode: [0, c_r) of worker `rank`'s shard), with the same
+ * full-length buffers and arguments as zero_step. The step is elementwise
+ * ("Data parallelism and ZeRO stages 1 to 3", section "2. Principles"), so
+ * stepping disjoint ranges that cover the index space, in any order and on any
+ * streams, gives bit for bit the result of one zero_step. This is the
+ * bucketed step: gradients reduced bucket by bucket during backward
+ * ("Data Parallelism & ZeRO", section "Data parallelism, and why the obvious
+ * implementation is bad": ~25 MB buckets) can be stepped as each bucket lands.
+ * begin must be a multiple of 8 (keeps every stream's groups aligned); end may
+ * be anything up to the range's length. Errors as zero_step, plus ZERO_EINVAL
+ * for a bad range; an empty range enqueues nothing. */
+zero_status zero_step_range(const zero_hparams* hp, void* param, const void* const* grads,
+                            const zero_states* states, int64_t t, int64_t begin, int64_t end,
+                            void* stream);
+
 /* ---- The materialised reduce-scatter mean and global-norm clipping ----------
  * "Data parallelism and ZeRO stages 1 to 3", section "2. Principles": stage 1
  * keeps the averaged gradient in .grad ("Your emulation's bookkeeping"), and

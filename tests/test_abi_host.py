@@ -302,3 +302,15 @@ def test_step_mean_and_mean_grad_reject():
     assert lib.zero_mean_grad(C.byref(hp), arr, A + (3 << 24), None, None, 0, None) == z.ZERO_EINVAL
     assert lib.zero_mean_grad(C.byref(hp), arr, A, A + (9 << 24), None, 0, None) == z.ZERO_EINVAL
     assert lib.zero_mean_grad(C.byref(_hp(n=0)), arr, A, None, None, 0, None) == z.ZERO_EINVAL
+
+
+def test_step_range_rejects_bad_ranges():
+    lib = _abi.load()
+    st = _abi.zero_states(master=None, m=A + (1 << 24), v=A + (2 << 24))
+    arr = (C.c_void_p * 4)(*[A + ((3 + k) << 24) for k in range(4)])
+    hp = _hp()
+    for begin, end in ((-8, 10), (16, 8), (0, 1001), (4, 100)):
+        rc = lib.zero_step_range(C.byref(hp), A, arr, C.byref(st), 1, begin, end, None)
+        assert rc == z.ZERO_EINVAL, (begin, end)
+    # an empty range is valid and launches nothing
+    assert lib.zero_step_range(C.byref(hp), A, arr, C.byref(st), 1, 8, 8, None) == z.ZERO_OK

@@ -13,6 +13,9 @@ workers sharing one GPU:
   zero_init_states(hp, param, states)   -> m = v = 0, master from param
   zero_step(hp, param, grads, states, t) -> one reduce-scatter-mean / Adam /
                                             all-gather step, in place
+  zero_step_range(hp, param, grads, states, t, begin, end)
+                                         -> the same step on [begin, end) only
+                                            (one bucket of a bucketed step)
   zero_mean_grad(hp, grads, mean, sumsq)  -> the reduce-scatter mean, materialised,
                                             and its squared norm
   zero_step_mean(hp, param, mean, states, t, clip_sumsq, max_norm)
@@ -36,7 +39,7 @@ from ._abi import (ZERO_EHIP, ZERO_EINVAL, ZERO_EUNSUPPORTED, ZERO_MAX_WORKERS, 
 __all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
            "zero_memory_bytes", "zero_shard_bounds", "zero_last_error", "wd_mask_from_flags",
            "zero_mean_grad_workspace_bytes", "zero_mean_grad", "zero_step_mean",
-           "zero_step_clipped_workspace_bytes", "zero_step_clipped",
+           "zero_step_clipped_workspace_bytes", "zero_step_clipped", "zero_step_range",
            "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MAX_WORKERS"]
 
 
@@ -183,6 +186,25 @@ def zero_step(hp: HParams, param, grads: Sequence, states: States, t: int, strea
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
     st = lib.zero_step(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t),
                        _stream_handle(stream, states.m))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+def zero_step_range(hp: HParams, param, grads: Sequence, states: States, t: int, begin: int,
+                    end: int, stream=None) -> None:
+    """Enqueue the step on elements [begin, end) of the call's range."""
+    chk = _check_common(hp, param, states)
+    if chk is not None:
+        g_dt, glen = chk
+        if len(grads) != hp.n_workers:
+            raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
+        for k, g in enumerate(grads):
+            _check_tensor(g, g_dt, glen, f"grads[{k}]")
+    lib = _abi.load()
+    c_hp, c_st = hp.to_c(), states.to_c()
+    arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
+    st = lib.zero_step_range(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t), int(begin),
+                             int(end), _stream_handle(stream, states.m))
     if st != ZERO_OK:
         _raise(st)
 

@@ -51,7 +51,8 @@ class zero_mem(C.Structure):
 
 EXPORTED = ("zero_init_states", "zero_step", "zero_memory_bytes", "zero_shard_bounds",
             "zero_last_error", "zero_mean_grad_workspace_bytes", "zero_mean_grad",
-            "zero_step_mean", "zero_step_clipped_workspace_bytes", "zero_step_clipped")
+            "zero_step_mean", "zero_step_clipped_workspace_bytes", "zero_step_clipped",
+            "zero_step_range")
 
 _lib = None
 
@@ -80,6 +81,10 @@ def load(path=None):
     lib.zero_shard_bounds.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.POINTER(C.c_int64),
                                       C.POINTER(C.c_int64)]
     lib.zero_shard_bounds.restype = C.c_int
+    lib.zero_step_range.argtypes = [C.POINTER(zero_hparams), C.c_void_p, C.POINTER(C.c_void_p),
+                                    C.POINTER(zero_states), C.c_int64, C.c_int64, C.c_int64,
+                                    C.c_void_p]
+    lib.zero_step_range.restype = C.c_int
     lib.zero_mean_grad_workspace_bytes.argtypes = [C.POINTER(zero_hparams), C.POINTER(C.c_size_t)]
     lib.zero_mean_grad_workspace_bytes.restype = C.c_int
     lib.zero_mean_grad.argtypes = [C.POINTER(zero_hparams), C.POINTER(C.c_void_p), C.c_void_p,

@@ -342,6 +342,39 @@ zero_status zero_step(const zero_hparams* hp, void* param, const void* const* gr
   return ok();
 }
 
+zero_status zero_step_range(const zero_hparams* hp, void* param, const void* const* grads,
+                            const zero_states* st, int64_t t, int64_t begin, int64_t end,
+                            void* stream) {
+  zlaunch::StepArgs la;
+  bool empty = false;
+  int64_t a, b;
+  if (hp == nullptr) return fail(ZERO_EINVAL, "hparams is NULL");
+  Widths wd;
+  if (!mode_widths(hp->mode, &wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
+  const int N = hp->n_workers >= 1 && hp->n_workers <= ZERO_MAX_WORKERS ? hp->n_workers : 0;
+  zero_status s = build_step(hp, param, grads, N, wd.grad, st, t, &la, &empty, &a, &b);
+  if (s != ZERO_OK) return s;
+  const int64_t len = b - a;
+  if (begin < 0 || end < begin || end > len)
+    return fail(ZERO_EINVAL, "need 0 <= begin <= end <= %lld, got [%lld, %lld)", (long long)len,
+                (long long)begin, (long long)end);
+  if (begin % 8 != 0)
+    return fail(ZERO_EINVAL, "begin must be a multiple of 8, got %lld", (long long)begin);
+  if (empty || begin == end) return ok();
+  // Elementwise: the sub-range is the same step on offset views.
+  for (int k = 0; k < la.n_workers; ++k)
+    la.grads[k] = static_cast<const char*>(la.grads[k]) + begin * wd.grad;
+  la.w = static_cast<char*>(la.w) + begin * wd.state;
+  la.m = static_cast<char*>(la.m) + begin * wd.state;
+  la.v = static_cast<char*>(la.v) + begin * wd.state;
+  if (la.out) la.out = static_cast<char*>(la.out) + begin * wd.param;
+  la.mask_bit_offset += begin;
+  la.len = end - begin;
+  const char* err = zlaunch::launch_step(la, stream);
+  if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
+  return ok();
+}
+
 zero_status zero_mean_grad_workspace_bytes(const zero_hparams* hp, size_t* bytes) {
   Widths wd;
   int64_t a = 0, b = 0;
