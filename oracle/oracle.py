@@ -60,6 +60,9 @@ class Oracle:
         lib.orc_step_mean.restype = _i32
         lib.orc_clip_factor.argtypes = [_dbl, _dbl]
         lib.orc_clip_factor.restype = _dbl
+        lib.orc_sgd_step.argtypes = [_i32, _i32, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
+                                     _vp, _i64, _dbl, _dbl, _dbl, _dbl, _i32, _vp]
+        lib.orc_sgd_step.restype = _i32
         lib.orc_memory_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _i64, _i32,
                                          C.POINTER(_i64)]
         lib.orc_memory_bytes.restype = _i32
@@ -157,6 +160,36 @@ class Oracle:
         if rc != 0:
             raise ValueError("oracle rejected the arguments")
         return p_out, mst_out, m_out, v_out
+
+    # -- momentum SGD -----------------------------------------------------------
+    def sgd_step(self, mode, param, grads, master, buf, t, lr, wd=0.0, momentum=0.0,
+                 dampening=0.0, nesterov=False, decay=None, form="sharded", N=None, rank=-1):
+        """Momentum SGD. form: 'sharded' (all workers), 'full' (shard-free) or 'rank'
+        (worker `rank`'s share: chunk gradients, shard-local master and buffer).
+        Returns (param, master, buf)."""
+        f = {"sharded": 0, "full": 1, "rank": 2}[form]
+        param = np.ascontiguousarray(param, dtype=_PARAM_DT[mode])
+        grads = [np.ascontiguousarray(g, dtype=_PARAM_DT[mode]) for g in grads]
+        sdt = _STATE_DT[mode]
+        buf = np.ascontiguousarray(buf, dtype=sdt)
+        n = param.size
+        N = len(grads) if N is None else N
+        if master is not None:
+            master = np.ascontiguousarray(master, dtype=np.float32 if mode == MODE_MIXED else sdt)
+        p_out = np.empty_like(param)
+        if f == 2:
+            mst_out = np.empty_like(master)
+        else:
+            mst_out = np.empty(n, np.float32) if mode == MODE_MIXED else None
+        b_out = np.empty_like(buf)
+        dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.uint8)
+        rc = self.lib.orc_sgd_step(f, mode, n, N, rank, _ptr(param), _ptr_array(grads),
+                                   _ptr(master), _ptr(buf), _ptr(p_out), _ptr(mst_out),
+                                   _ptr(b_out), int(t), float(lr), float(wd), float(momentum),
+                                   float(dampening), int(bool(nesterov)), _ptr(dec))
+        if rc != 0:
+            raise ValueError("oracle rejected the arguments")
+        return p_out, mst_out, b_out
 
     # -- materialised mean gradient and clipping --------------------------------
     def mean_grad(self, mode, n, N, grads, rank=-1):

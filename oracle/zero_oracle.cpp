@@ -47,6 +47,10 @@
 //     and rounded once to S.
 //   * bf16 write-back in mixed precision: round to nearest, ties to even; NaN
 //     becomes the quiet NaN 0x7FC0.
+//   * Momentum SGD (the other wrapped optimizer of "Data parallelism and ZeRO
+//     stages 1 to 3"; no formula printed): torch.optim.SGD's definition with
+//     coupled L2 decay, the buffer set to the first step's gradient, optional
+//     dampening and Nesterov; see sgd_update.
 //   * Global-norm clipping ("Data parallelism and ZeRO stages 1 to 3", section
 //     "Going further": an all-reduce of squared chunk norms before the step;
 //     no formula): each shard's squared norm of its mean gradient, summed in
@@ -235,6 +239,74 @@ void adam_update(S* w, const S* g, S* m, S* v, int64_t len,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Momentum SGD ("Data parallelism and ZeRO stages 1 to 3": the wrapped
+// optimizers are M10.2 SGD and M10.3 AdamW; the DDP tests run momentum-SGD
+// steps; no formula is printed). Reading: torch.optim.SGD's definition, in S:
+//   d = g;  where decay applies: d = d + wd*w         (coupled L2 decay)
+//   if momentum != 0:
+//     buf = d at the first step (t == 1), else buf = momentum*buf + (1-dampening)*d
+//     d = nesterov ? d + momentum*buf : buf
+//   w = w - lr*d
+// The momentum buffer is the m state array; v is not used.
+// ---------------------------------------------------------------------------
+struct OptSel {
+  int kind;  // 0: Adam/AdamW, 1: momentum SGD
+  double momentum, dampening;
+  int nesterov;
+};
+const OptSel kAdam = {0, 0.0, 0.0, 0};
+
+template <class S>
+void sgd_update(S* w, const S* g, S* buf, int64_t len, int64_t t, double lr_d, double wd_d,
+                const OptSel& o, const uint8_t* decay) {
+  const S lr = (S)lr_d, wd = (S)wd_d, mom = (S)o.momentum;
+  const S one_minus_damp = (S)(1.0 - o.dampening);
+  for (int64_t i = 0; i < len; ++i) {
+    S d = g[i];
+    const bool dec = decay == nullptr ? true : decay[i] != 0;
+#if ORACLE_MUTANT == 18
+    if (wd_d != 0.0 && dec) w[i] = w[i] * (S)(1.0 - lr_d * wd_d);  // planted: decoupled decay
+#else
+    if (wd_d != 0.0 && dec) {
+      const S dw = wd * w[i];
+      d = d + dw;
+    }
+#endif
+    if (o.momentum != 0.0) {
+      S b;
+#if ORACLE_MUTANT == 17
+      if (false) {  // planted: the buffer starts at zero instead of the first gradient
+#else
+      if (t == 1) {
+#endif
+        b = d;
+      } else {
+        const S kept = mom * buf[i];
+        const S added = one_minus_damp * d;
+        b = kept + added;
+      }
+      buf[i] = b;
+      if (o.nesterov) {
+        const S nb = mom * b;
+        d = d + nb;
+      } else {
+        d = b;
+      }
+    }
+    const S step = lr * d;
+    w[i] = w[i] - step;
+  }
+}
+
+template <class S>
+void opt_update(S* w, const S* g, S* m, S* v, int64_t len, const StepConsts<S>& c,
+                const uint8_t* decay, S wd_raw, const OptSel& o, int64_t t, double lr,
+                double wd) {
+  if (o.kind == 0) adam_update<S>(w, g, m, v, len, c, decay, wd_raw);
+  else sgd_update<S>(w, g, m, len, t, lr, wd, o, decay);
+}
+
 // Element access by mode. mode 0: fp64 everywhere. mode 1: fp32 everywhere.
 // mode 2: bf16 gradients and gathered parameters, fp32 master/m/v.
 enum { MODE_F64 = 0, MODE_F32 = 1, MODE_MIXED = 2 };
@@ -299,7 +371,7 @@ void sharded_step(int mode, int64_t n, int64_t N, const void* param_in,
                   const void* const* grads, const void* master_in, const S* m_in,
                   const S* v_in, void* param_out, void* master_out, S* m_out,
                   S* v_out, int64_t t, double lr, double b1, double b2, double eps,
-                  double wd, const uint8_t* decay) {
+                  double wd, const uint8_t* decay, const OptSel& o = kAdam) {
   const StepConsts<S> c = step_consts<S>(lr, b1, b2, eps, wd, t);
   // Start the all-gather target from the old parameters; every element is
   // overwritten below by the worker that owns it.
@@ -321,8 +393,8 @@ void sharded_step(int mode, int64_t n, int64_t N, const void* param_in,
     }
     if (decay) dec.assign(decay + a, decay + b);
     // (2) Adam on the shard only
-    adam_update<S>(w.data(), gbar.data(), m.data(), v.data(), len, c,
-                   decay ? dec.data() : nullptr, (S)wd);
+    opt_update<S>(w.data(), gbar.data(), m.data(), v.data(), len, c,
+                  decay ? dec.data() : nullptr, (S)wd, o, t, lr, wd);
     // (3) all-gather: the shard lands in every worker's full vector; with one
     // shared vector that is one write per element.
 #if ORACLE_MUTANT == 3
@@ -346,7 +418,7 @@ void full_step(int mode, int64_t n, int64_t N, const void* param_in,
                const void* const* grads, const void* master_in, const S* m_in,
                const S* v_in, void* param_out, void* master_out, S* m_out,
                S* v_out, int64_t t, double lr, double b1, double b2, double eps,
-               double wd, const uint8_t* decay) {
+               double wd, const uint8_t* decay, const OptSel& o = kAdam) {
   const StepConsts<S> c = step_consts<S>(lr, b1, b2, eps, wd, t);
   std::vector<S> gbar((size_t)n);
   for (int64_t i = 0; i < n; ++i) {
@@ -356,7 +428,7 @@ void full_step(int mode, int64_t n, int64_t N, const void* param_in,
   }
   std::vector<S> w((size_t)n), m(m_in, m_in + n), v(v_in, v_in + n);
   for (int64_t i = 0; i < n; ++i) w[(size_t)i] = load_master<S>(param_in, master_in, i, mode);
-  adam_update<S>(w.data(), gbar.data(), m.data(), v.data(), n, c, decay, (S)wd);
+  opt_update<S>(w.data(), gbar.data(), m.data(), v.data(), n, c, decay, (S)wd, o, t, lr, wd);
   for (int64_t i = 0; i < n; ++i) {
     store_param<S>(param_out, i, w[(size_t)i], mode);
     if (mode == MODE_MIXED) ((float*)master_out)[i] = (float)w[(size_t)i];
@@ -378,7 +450,7 @@ void rank_step(int mode, int64_t n, int64_t N, int64_t r, const void* param_in,
                const void* const* chunk_grads, const S* master_in, const S* m_in,
                const S* v_in, void* param_out, S* master_out, S* m_out, S* v_out,
                int64_t t, double lr, double b1, double b2, double eps, double wd,
-               const uint8_t* decay) {
+               const uint8_t* decay, const OptSel& o = kAdam) {
   const StepConsts<S> c = step_consts<S>(lr, b1, b2, eps, wd, t);
   int64_t a, b;
   split_bounds(n, N, r, &a, &b);
@@ -389,8 +461,8 @@ void rank_step(int mode, int64_t n, int64_t N, int64_t r, const void* param_in,
   std::vector<S> w(master_in, master_in + len), m(m_in, m_in + len), v(v_in, v_in + len);
   std::vector<uint8_t> dec;
   if (decay) dec.assign(decay + a, decay + b);
-  adam_update<S>(w.data(), gbar.data(), m.data(), v.data(), len, c,
-                 decay ? dec.data() : nullptr, (S)wd);
+  opt_update<S>(w.data(), gbar.data(), m.data(), v.data(), len, c,
+                decay ? dec.data() : nullptr, (S)wd, o, t, lr, wd);
   for (int64_t j = 0; j < len; ++j) {
     store_param<S>(param_out, a + j, w[(size_t)j], mode);
     master_out[j] = w[(size_t)j];
@@ -461,7 +533,8 @@ void step_from_mean(int mode, int64_t n, int64_t N, int64_t r, const void* param
                     const S* mean, const void* master_in, const S* m_in, const S* v_in,
                     void* param_out, void* master_out, S* m_out, S* v_out, int64_t t,
                     double lr, double b1, double b2, double eps, double wd,
-                    const uint8_t* decay, const double* clip_sumsq, double max_norm) {
+                    const uint8_t* decay, const double* clip_sumsq, double max_norm,
+                    const OptSel& o = kAdam) {
   const StepConsts<S> c = step_consts<S>(lr, b1, b2, eps, wd, t);
   const bool clip = clip_sumsq != nullptr;
   const S coef = clip ? (S)clip_factor(*clip_sumsq, max_norm) : (S)1;
@@ -484,8 +557,8 @@ void step_from_mean(int mode, int64_t n, int64_t N, int64_t r, const void* param
       v[j] = v_in[a - base + j];
     }
     if (decay) dec.assign(decay + a, decay + b);
-    adam_update<S>(w.data(), g.data(), m.data(), v.data(), len, c,
-                   decay ? dec.data() : nullptr, (S)wd);
+    opt_update<S>(w.data(), g.data(), m.data(), v.data(), len, c,
+                  decay ? dec.data() : nullptr, (S)wd, o, t, lr, wd);
     for (int64_t j = 0; j < len; ++j) {
       store_param<S>(param_out, a + j, w[(size_t)j], mode);
       if (r >= 0) ((S*)master_out)[j] = w[(size_t)j];
@@ -637,6 +710,55 @@ int orc_step_mean(int mode, int64_t n, int64_t N, int64_t rank, const void* para
 
 // The clipping factor for a squared norm (for pins).
 double orc_clip_factor(double sumsq, double max_norm) { return clip_factor(sumsq, max_norm); }
+
+// Momentum SGD in every call form: form 0 the sharded step (all workers),
+// 1 the shard-free reference, 2 worker `rank`'s share (chunk gradients,
+// shard-local master and buffer). The momentum buffer is buf_in/buf_out; the
+// master follows the conventions of the Adam entry points.
+int orc_sgd_step(int form, int mode, int64_t n, int64_t N, int64_t rank, const void* param_in,
+                 const void* const* grads, const void* master_in, const void* buf_in,
+                 void* param_out, void* master_out, void* buf_out, int64_t t, double lr,
+                 double wd, double momentum, double dampening, int nesterov,
+                 const uint8_t* decay) {
+  if (n < 0 || N < 1 || t < 1 || form < 0 || form > 2) return -1;
+  if (form == 2 && (rank < 0 || rank >= N)) return -1;
+  const OptSel o = {1, momentum, dampening, nesterov};
+  const int64_t len = form == 2 ? [&] { int64_t a, b; split_bounds(n, N, rank, &a, &b); return b - a; }() : n;
+  const size_t sb = mode == MODE_F64 ? 8 : 4;
+  std::vector<unsigned char> vin((size_t)len * sb, 0), vout((size_t)len * sb, 0);  // unused by SGD
+  if (mode == MODE_F64) {
+    typedef double S;
+    if (form == 0)
+      sharded_step<S>(mode, n, N, param_in, grads, master_in, (const S*)buf_in, (const S*)vin.data(),
+                      param_out, master_out, (S*)buf_out, (S*)vout.data(), t, lr, 0.9, 0.9, 1.0,
+                      wd, decay, o);
+    else if (form == 1)
+      full_step<S>(mode, n, N, param_in, grads, master_in, (const S*)buf_in, (const S*)vin.data(),
+                   param_out, master_out, (S*)buf_out, (S*)vout.data(), t, lr, 0.9, 0.9, 1.0, wd,
+                   decay, o);
+    else
+      rank_step<S>(mode, n, N, rank, param_in, grads, (const S*)master_in, (const S*)buf_in,
+                   (const S*)vin.data(), param_out, (S*)master_out, (S*)buf_out, (S*)vout.data(),
+                   t, lr, 0.9, 0.9, 1.0, wd, decay, o);
+  } else if (mode == MODE_F32 || mode == MODE_MIXED) {
+    typedef float S;
+    if (form == 0)
+      sharded_step<S>(mode, n, N, param_in, grads, master_in, (const S*)buf_in, (const S*)vin.data(),
+                      param_out, master_out, (S*)buf_out, (S*)vout.data(), t, lr, 0.9, 0.9, 1.0,
+                      wd, decay, o);
+    else if (form == 1)
+      full_step<S>(mode, n, N, param_in, grads, master_in, (const S*)buf_in, (const S*)vin.data(),
+                   param_out, master_out, (S*)buf_out, (S*)vout.data(), t, lr, 0.9, 0.9, 1.0, wd,
+                   decay, o);
+    else
+      rank_step<S>(mode, n, N, rank, param_in, grads, (const S*)master_in, (const S*)buf_in,
+                   (const S*)vin.data(), param_out, (S*)master_out, (S*)buf_out, (S*)vout.data(),
+                   t, lr, 0.9, 0.9, 1.0, wd, decay, o);
+  } else {
+    return -1;
+  }
+  return 0;
+}
 
 // ---------------------------------------------------------------------------
 // Memory per rank, in bytes: out[0] params, out[1] grads, out[2] optimizer.

@@ -550,6 +550,82 @@ def pin_clipping_closed_form(O):
     assert O.clip_factor(4.0, 100.0) == 1.0
 
 
+# ---------------------------------------------------------------------------
+# Momentum SGD
+# ---------------------------------------------------------------------------
+SGD_VARIANTS = [  # (momentum, dampening, nesterov, weight decay)
+    (0.9, 0.0, False, 0.0),
+    (0.9, 0.1, False, 0.01),
+    (0.8, 0.0, True, 0.05),
+    (0.0, 0.0, False, 0.1),
+]
+
+
+def pin_sgd_vs_torch(O):
+    """One worker, fp64: the oracle's momentum SGD equals torch.optim.SGD."""
+    import torch
+    rng = np.random.default_rng(25)
+    n, T, lr = 300, 6, 0.05
+    for mom, damp, nest, wd in SGD_VARIANTS:
+        w0 = rng.standard_normal(n)
+        gseq = [rng.standard_normal(n) for _ in range(T)]
+        p = torch.nn.Parameter(torch.tensor(w0))
+        opt = torch.optim.SGD([p], lr=lr, momentum=mom, dampening=damp, nesterov=nest,
+                              weight_decay=wd, foreach=False)
+        w, buf = w0, np.zeros(n)
+        for t, g in enumerate(gseq, 1):
+            p.grad = torch.tensor(g)
+            opt.step()
+            w, _, buf = O.sgd_step(MODE_F64, w, [g], None, buf, t, lr, wd, mom, damp, nest)
+            assert np.allclose(w, p.detach().numpy(), rtol=1e-12, atol=1e-14), (mom, damp, nest, t)
+            if mom:
+                tb = opt.state[p]["momentum_buffer"].numpy()
+                assert np.allclose(buf, tb, rtol=1e-12, atol=1e-14)
+
+
+def pin_sgd_constant_gradient(O):
+    """Momentum mu, no dampening, the same mean gradient c every step:
+    buf_t = c (1 - mu^t) / (1 - mu), w_t = w0 - lr c sum_{s<=t} (1 - mu^s) / (1 - mu)."""
+    rng = np.random.default_rng(26)
+    n, N, T, lr, mu = 400, 4, 12, 0.01, 0.9
+    w0 = rng.standard_normal(n)
+    c = rng.standard_normal(n)
+    grads = [N * c] + [np.zeros(n)] * (N - 1)
+    w, buf = w0, np.zeros(n)
+    acc = 0.0
+    for t in range(1, T + 1):
+        w, _, buf = O.sgd_step(MODE_F64, w, grads, None, buf, t, lr, 0.0, mu)
+        assert np.allclose(buf, c * (1 - mu ** t) / (1 - mu), rtol=1e-12, atol=1e-15)
+        acc += (1 - mu ** t) / (1 - mu)
+    assert np.allclose(w, w0 - lr * c * acc, rtol=1e-12, atol=1e-13)
+
+
+def pin_sgd_sharded_equals_shard_free_and_rank_share(O):
+    rng = np.random.default_rng(27)
+    for mode in (MODE_F64, MODE_F32, MODE_MIXED):
+        n, N = 2051, 7
+        w, _ = _case_for_mode(rng, mode, n, 1)
+        mst, buf, _ = O.init_states(mode, w)
+        flags = (rng.random(n) < 0.5).astype(np.uint8)
+        ws, bs, ms_ = w, buf, mst
+        for t in (1, 2, 3):
+            _, grads = _case_for_mode(rng, mode, n, N)
+            args = (t, 0.01, 0.05, 0.9, 0.1, False, flags)
+            a_p, a_m, a_b = O.sgd_step(mode, ws, grads, ms_, bs, *args, form="sharded")
+            f_p, f_m, f_b = O.sgd_step(mode, ws, grads, ms_, bs, *args, form="full")
+            assert np.array_equal(a_p.view(np.uint8), f_p.view(np.uint8)) and np.array_equal(a_b, f_b)
+            for r in (0, N // 2, N - 1):
+                lo, hi = O.split_bounds(n, N, r)
+                master_r = (ms_ if mode == MODE_MIXED else ws)[lo:hi].astype(bs.dtype)
+                r_p, r_m, r_b = O.sgd_step(mode, ws, [g[lo:hi] for g in grads], master_r,
+                                           bs[lo:hi], *args, form="rank", N=N, rank=r)
+                assert np.array_equal(r_p[lo:hi].view(np.uint8), a_p[lo:hi].view(np.uint8))
+                assert np.array_equal(r_p[:lo].view(np.uint8), ws[:lo].view(np.uint8))
+                assert np.array_equal(r_p[hi:].view(np.uint8), ws[hi:].view(np.uint8))
+                assert np.array_equal(r_b, a_b[lo:hi])
+            ws, ms_, bs = a_p, a_m, a_b
+
+
 ALL_PINS = [
     pin_p2_worked_example,
     pin_p1_worked_example,
@@ -572,4 +648,7 @@ ALL_PINS = [
     pin_step_from_mean_equals_step,
     pin_clipping_vs_torch,
     pin_clipping_closed_form,
+    pin_sgd_vs_torch,
+    pin_sgd_constant_gradient,
+    pin_sgd_sharded_equals_shard_free_and_rank_share,
 ]

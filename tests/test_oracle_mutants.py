@@ -32,6 +32,8 @@ MUTANTS = {
     14: "off-by-one step in bias correction",
     15: "clipping factor not clamped at 1",
     16: "1-norm instead of squared norm",
+    17: "SGD momentum buffer starting at zero",
+    18: "SGD with decoupled instead of coupled decay",
 }
 
 
