@@ -72,6 +72,23 @@ typedef enum {
   ZERO_MODE_MIXED_BF16 = 2
 } zero_mode;
 
+typedef enum {
+  /* Bias-corrected Adam with decoupled (AdamW) weight decay, as above. */
+  ZERO_OPT_ADAM = 0,
+  /* Momentum SGD, the other optimizer "Data parallelism and ZeRO stages 1 to
+   * 3" wraps (M10.2 SGD, run with momentum in its DDP tests); no formula is
+   * printed, so it follows torch.optim.SGD, per element in S, never fused:
+   *     d = gb;  where decay applies: d = d + wd*w        (coupled L2 decay)
+   *     if momentum != 0:
+   *       buf = (t == 1) ? d : momentum*buf + (1-dampening)*d
+   *       d   = nesterov ? d + momentum*buf : buf
+   *     w = w - lr*d
+   * The momentum buffer is states.m; states.v is not used (may be NULL);
+   * beta1, beta2 and eps are ignored. 1-dampening is formed in double and
+   * rounded once to S. */
+  ZERO_OPT_SGD = 1
+} zero_optimizer;
+
 /* Largest number of workers one zero_step call accepts (the gradient pointers
  * travel in the kernel's argument block). zero_shard_bounds and
  * zero_memory_bytes accept any N >= 1. */
@@ -87,20 +104,26 @@ typedef struct {
   int32_t rank;      /* -1: every worker's share in this call (full mode);
                         0..N-1: only worker `rank`'s share (rank mode) */
   int32_t mode;      /* a zero_mode */
-  int32_t reserved;  /* must be 0 */
+  int32_t optimizer; /* a zero_optimizer */
   double lr;         /* finite */
-  double beta1;      /* in [0, 1) */
-  double beta2;      /* in [0, 1) */
-  double eps;        /* finite, > 0 */
-  double weight_decay; /* finite, >= 0; 0 disables decay */
+  double beta1;      /* Adam: in [0, 1) */
+  double beta2;      /* Adam: in [0, 1) */
+  double eps;        /* Adam: finite, > 0 */
+  double weight_decay; /* finite, >= 0; 0 disables decay (decoupled for Adam,
+                          coupled L2 for SGD) */
   /* Optional device bitmask over the global index space [0, n): element i
    * decays iff bit (i % 32) of word i / 32 is set. It must hold at least
    * (n + 31) / 32 readable words and be 4-byte aligned. NULL: every element
    * decays when weight_decay > 0. Ignored when weight_decay == 0. */
   const uint32_t* wd_mask;
+  double momentum;   /* SGD: finite, >= 0; 0 keeps no buffer */
+  double dampening;  /* SGD: in [0, 1] */
+  int32_t nesterov;  /* SGD: 0 or 1; 1 needs momentum > 0 and dampening == 0 */
+  int32_t reserved;  /* must be 0 */
 } zero_hparams;
 
 /* Optimizer state, caller-owned device buffers, each 16-byte aligned.
+ *   (SGD: m is the momentum buffer and v is unused and may be NULL.)
  *   Full mode (rank == -1): m and v hold n elements of S; worker r's shard is
  *     the view [a_r, b_r) of each (the N per-worker (m_shard, v_shard) pairs of
  *     "What to implement", laid back to back). master holds n fp32 values in
@@ -144,8 +167,10 @@ zero_status zero_init_states(const zero_hparams* hp, const void* param,
  * arguments and t are still checked).
  * Errors: ZERO_EINVAL for a null or misaligned pointer, overlapping written
  * ranges, n < 1, N outside [1, ZERO_MAX_WORKERS], rank outside [-1, N), t < 1,
- * a non-finite scalar, a beta outside [0, 1), eps <= 0, weight_decay < 0, a
- * mode/master mismatch, or reserved != 0; ZERO_EHIP if the launch fails. */
+ * a non-finite scalar, a beta outside [0, 1), eps <= 0, weight_decay < 0, an
+ * unknown optimizer, SGD momentum < 0, dampening outside [0, 1], nesterov
+ * without momentum or with dampening, a mode/master mismatch, or
+ * reserved != 0; ZERO_EHIP if the launch fails. */
 zero_status zero_step(const zero_hparams* hp, void* param, const void* const* grads,
                       const zero_states* states, int64_t t, void* stream);
 

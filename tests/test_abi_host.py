@@ -34,8 +34,12 @@ def test_library_exports_every_declared_function():
 
 
 def test_header_is_plain_c():
+    """Plain C declarations: no torch or C++ types outside the comments."""
     txt = open(os.path.join(ROOT, "include", "zero_adam.h")).read()
-    assert 'extern "C"' in txt and "torch" not in txt.lower().replace("torch's", "")
+    code = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    assert 'extern "C"' in code
+    for word in ("torch", "at::", "c10", "std::", "Tensor", "hipStream_t"):
+        assert word not in code, word
 
 
 # -- shard bounds -------------------------------------------------------------
@@ -132,8 +136,9 @@ def test_memory_bytes_rejects(args, status):
 
 # -- step / init validation (rejected before any HIP call) ---------------------
 def _hp(**kw):
-    d = dict(n=1000, n_workers=4, rank=-1, mode=z.ZERO_MODE_F32, reserved=0, lr=1e-3, beta1=0.9,
-             beta2=0.999, eps=1e-8, weight_decay=0.0, wd_mask=None)
+    d = dict(n=1000, n_workers=4, rank=-1, mode=z.ZERO_MODE_F32, optimizer=0, lr=1e-3, beta1=0.9,
+             beta2=0.999, eps=1e-8, weight_decay=0.0, wd_mask=None, momentum=0.0, dampening=0.0,
+             nesterov=0, reserved=0)
     d.update(kw)
     return _abi.zero_hparams(**d)
 
@@ -179,6 +184,14 @@ BAD_STEPS = {
     "param overlaps m": ({}, dict(m=A + 16)),
     "grad overlaps m": ({}, dict(grads=[A + (1 << 24), A + (4 << 24), A + (5 << 24), A + (6 << 24)])),
     "mask overlaps v": (dict(weight_decay=0.1, wd_mask=A + (2 << 24)), {}),
+    "unknown optimizer": (dict(optimizer=2), {}),
+    "sgd momentum < 0": (dict(optimizer=1, momentum=-0.5), {}),
+    "sgd momentum nan": (dict(optimizer=1, momentum=float("nan")), {}),
+    "sgd dampening > 1": (dict(optimizer=1, momentum=0.9, dampening=1.5), {}),
+    "sgd nesterov with dampening": (dict(optimizer=1, momentum=0.9, dampening=0.1, nesterov=1), {}),
+    "sgd nesterov without momentum": (dict(optimizer=1, nesterov=1), {}),
+    "sgd nesterov = 2": (dict(optimizer=1, momentum=0.9, nesterov=2), {}),
+    "sgd null m": (dict(optimizer=1, momentum=0.9), dict(m=None)),
 }
 
 
@@ -314,3 +327,11 @@ def test_step_range_rejects_bad_ranges():
         assert rc == z.ZERO_EINVAL, (begin, end)
     # an empty range is valid and launches nothing
     assert lib.zero_step_range(C.byref(hp), A, arr, C.byref(st), 1, 8, 8, None) == z.ZERO_OK
+
+
+def test_sgd_ignores_adam_fields_and_allows_null_v():
+    """SGD ignores beta1/beta2/eps (here invalid for Adam) and may leave v NULL;
+    the call is rejected only for t = 0 here, so nothing is launched."""
+    hp = _hp(optimizer=1, momentum=0.9, beta1=5.0, beta2=-1.0, eps=0.0)
+    rc, msg = _call_step(hp, v=None, t=0)
+    assert rc == z.ZERO_EINVAL and "t must be" in msg

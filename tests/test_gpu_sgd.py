@@ -1,0 +1,133 @@
+"""GPU parity of the momentum-SGD variant of the fused step (bar as for Adam:
+fp64 bit-exact, fp32 within 1e-6 * max(1, |ref|), bf16 within 1 ulp)."""
+import numpy as np
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import zero_sharded_optimizer_amd as z  # noqa: E402
+from zero_sharded_optimizer_amd import synth  # noqa: E402
+from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
+from oracle.compare import compare  # noqa: E402
+from gpu_cases import host, kinds, say  # noqa: E402
+
+W = synth.WORKLOADS
+BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"]}
+VARIANTS = {  # momentum, dampening, nesterov, weight decay
+    "momentum": (0.9, 0.0, False, 0.0),
+    "dampened+decay": (0.9, 0.1, False, 0.01),
+    "nesterov+decay": (0.8, 0.0, True, 0.05),
+    "plain+decay": (0.0, 0.0, False, 0.1),
+}
+
+
+def sgd_setup(wl, mom, damp, nest, wd, mask=None):
+    param, master0 = synth.make_params(wl, "cuda")
+    a, b = wl.shard
+    L = b - a
+    sdt = synth.state_dtype(wl)
+    need_master = wl.mode == MODE_MIXED or wl.rank >= 0
+    st = z.States(torch.empty(L, dtype=sdt, device="cuda") if need_master else None,
+                  torch.empty(L, dtype=sdt, device="cuda"), None)
+    hp = z.HParams(n=wl.n, n_workers=wl.n_workers, mode=wl.mode, lr=wl.lr, beta1=0.0, beta2=0.0,
+                   eps=0.0, weight_decay=wd, rank=wl.rank, wd_mask=mask, optimizer=z.ZERO_OPT_SGD,
+                   momentum=mom, dampening=damp, nesterov=nest)
+    z.zero_init_states(hp, param, st)
+    if master0 is not None:
+        st.master.copy_(master0)
+        param[a:b].copy_(master0.to(param.dtype))
+    return hp, param, st
+
+
+def run_sgd(oracle, wl, variant, steps):
+    mom, damp, nest, wd = VARIANTS[variant]
+    say(f"[case] sgd {variant} {wl.name} mode={wl.mode} n={wl.n} N={wl.n_workers} rank={wl.rank}")
+    flags = synth.decay_flags(wl)
+    mask = z.wd_mask_from_flags(flags) if flags is not None and wd else None
+    dec = None if flags is None else flags.astype(np.uint8)
+    hp, param, st = sgd_setup(wl, mom, damp, nest, wd, mask)
+    p_h, b_h = host(param), host(st.m)
+    mst_h = host(st.master) if st.master is not None else None
+    a, b = wl.shard
+    for t in range(1, steps + 1):
+        grads = synth.make_grads(wl, t, "cuda")
+        z.zero_step(hp, param, grads, st, t)
+        g_h = [host(g) for g in grads]
+        form = "rank" if wl.rank >= 0 else "sharded"
+        p_h, mst_h, b_h = oracle.sgd_step(wl.mode, p_h, g_h, mst_h, b_h, t, wl.lr, wd, mom, damp,
+                                          nest, dec, form=form, N=wl.n_workers, rank=wl.rank)
+    torch.cuda.synchronize()
+    pk, sk = kinds(wl)
+    out = [compare("param", host(param), p_h, pk)]
+    if mom:
+        out.append(compare("momentum buffer", host(st.m), b_h, sk))
+    if st.master is not None:
+        out.append(compare("master", host(st.master), mst_h, sk))
+    say("[done] " + "; ".join(f"{s['name']} bitexact {s['bitexact']}/{s['n']}" for s in out))
+
+
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED])
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+def test_sgd_full_mode(oracle, mode, variant):
+    run_sgd(oracle, synth.scaled(BASE[mode], 1_000_003, decay="all", worker_scale=None), variant, 4)
+
+
+@pytest.mark.parametrize("mode", [MODE_F32, MODE_MIXED])
+@pytest.mark.parametrize("n,N", [(9, 5), (4099, 3), (100_001, 64)])
+def test_sgd_edge_shapes(oracle, mode, n, N):
+    run_sgd(oracle, synth.scaled(BASE[mode], n, n_workers=N, worker_scale=None, decay="all"),
+            "nesterov+decay", 3)
+
+
+@pytest.mark.parametrize("rank", [0, 5])
+def test_sgd_rank_mode(oracle, rank):
+    wl = synth.scaled(W["mixed-rank0-of-8B-n8"], 8 * 125_001 + 3, rank=rank)
+    run_sgd(oracle, wl, "dampened+decay", 3)
+
+
+def test_sgd_gpt2_shaped_decay_mask(oracle):
+    shapes = synth.gpt2_small_shapes(vocab=1000, ctx=64, d=96, layers=2)
+    run_sgd(oracle, synth.scaled(W["gpt2s-fp32-n64"], 0, shapes=shapes), "momentum", 3)
+    run_sgd(oracle, synth.scaled(W["gpt2s-fp32-n64"], 0, shapes=shapes), "plain+decay", 2)
+
+
+def test_sgd_clipped_with_unreached_threshold_equals_unclipped():
+    wl = synth.scaled(W["fp32-320M-n8"], 300_007)
+    say("[case] sgd clipped == unclipped when the threshold is not reached")
+    hp, p1, s1 = sgd_setup(wl, 0.9, 0.0, False, 0.01)
+    _, p2, s2 = sgd_setup(wl, 0.9, 0.0, False, 0.01)
+    ws = torch.empty(z.zero_step_clipped_workspace_bytes(hp), dtype=torch.uint8, device="cuda")
+    for t in (1, 2, 3):
+        grads = synth.make_grads(wl, t, "cuda")
+        z.zero_step(hp, p1, grads, s1, t)
+        z.zero_step_clipped(hp, p2, grads, s2, t, 1e30, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(p1.view(torch.int32), p2.view(torch.int32))
+    assert torch.equal(s1.m.view(torch.int32), s2.m.view(torch.int32))
+
+
+def test_sgd_full_size_fp32_320M_n8(oracle):
+    """The fp32 320M-parameter 8-worker workload with momentum SGD, at full size,
+    compared on a sampled index set (exact per element: the step is elementwise)."""
+    wl = W["fp32-320M-n8"]
+    mom, damp, nest, wd = VARIANTS["nesterov+decay"]
+    say("[case] full-size sgd fp32-320M-n8")
+    hp, param, st = sgd_setup(wl, mom, damp, nest, wd)
+    idx = synth.sample_indices(wl, 1 << 20)
+    idx_d = torch.from_numpy(idx).to("cuda")
+    p_h = host(param[idx_d])
+    b_h = np.zeros(idx.size, np.float32)
+    for t in range(1, 6):
+        grads = synth.make_grads(wl, t, "cuda")
+        z.zero_step(hp, param, grads, st, t)
+        g_h = [host(g[idx_d]) for g in grads]
+        del grads
+        p_h, _, b_h = oracle.sgd_step(wl.mode, p_h, g_h, None, b_h, t, wl.lr, wd, mom, damp, nest,
+                                      form="full")
+    torch.cuda.synchronize()
+    compare("param", host(param[idx_d]), p_h, "f32")
+    compare("momentum buffer", host(st.m[idx_d]), b_h, "f32")

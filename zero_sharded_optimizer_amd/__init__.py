@@ -34,13 +34,15 @@ import numpy as np
 
 from . import _abi
 from ._abi import (ZERO_EHIP, ZERO_EINVAL, ZERO_EUNSUPPORTED, ZERO_MAX_WORKERS,  # noqa: F401
-                   ZERO_MODE_F32, ZERO_MODE_F64, ZERO_MODE_MIXED_BF16, ZERO_OK)
+                   ZERO_MODE_F32, ZERO_MODE_F64, ZERO_MODE_MIXED_BF16, ZERO_OK, ZERO_OPT_ADAM,
+                   ZERO_OPT_SGD)
 
 __all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
            "zero_memory_bytes", "zero_shard_bounds", "zero_last_error", "wd_mask_from_flags",
            "zero_mean_grad_workspace_bytes", "zero_mean_grad", "zero_step_mean",
            "zero_step_clipped_workspace_bytes", "zero_step_clipped", "zero_step_range",
-           "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MAX_WORKERS"]
+           "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MAX_WORKERS",
+           "ZERO_OPT_ADAM", "ZERO_OPT_SGD"]
 
 
 class ZeroError(RuntimeError):
@@ -52,7 +54,9 @@ class ZeroError(RuntimeError):
 
 @dataclass
 class HParams:
-    """Mirror of zero_hparams. No defaults for the optimizer's hyperparameters."""
+    """Mirror of zero_hparams. No defaults for Adam's hyperparameters; the SGD
+    fields are used only with optimizer=ZERO_OPT_SGD (then beta1/beta2/eps are
+    ignored and may be 0)."""
     n: int
     n_workers: int
     mode: int
@@ -63,13 +67,19 @@ class HParams:
     weight_decay: float = 0.0
     rank: int = -1
     wd_mask: object = None  # device int32/uint32 tensor of (n + 31) // 32 words, or None
+    optimizer: int = 0      # ZERO_OPT_ADAM or ZERO_OPT_SGD
+    momentum: float = 0.0
+    dampening: float = 0.0
+    nesterov: bool = False
 
     def to_c(self):
         return _abi.zero_hparams(
             n=int(self.n), n_workers=int(self.n_workers), rank=int(self.rank),
-            mode=int(self.mode), reserved=0, lr=float(self.lr), beta1=float(self.beta1),
-            beta2=float(self.beta2), eps=float(self.eps), weight_decay=float(self.weight_decay),
-            wd_mask=_addr(self.wd_mask))
+            mode=int(self.mode), optimizer=int(self.optimizer), lr=float(self.lr),
+            beta1=float(self.beta1), beta2=float(self.beta2), eps=float(self.eps),
+            weight_decay=float(self.weight_decay), wd_mask=_addr(self.wd_mask),
+            momentum=float(self.momentum), dampening=float(self.dampening),
+            nesterov=int(bool(self.nesterov)), reserved=0)
 
 
 @dataclass
@@ -148,7 +158,8 @@ def _check_common(hp, param, states):
     a, b = _shard_len(hp)
     _check_tensor(param, p_dt, hp.n, "param")
     _check_tensor(states.m, s_dt, b - a, "states.m")
-    _check_tensor(states.v, s_dt, b - a, "states.v")
+    if states.v is not None or hp.optimizer != ZERO_OPT_SGD:
+        _check_tensor(states.v, s_dt, b - a, "states.v")
     _check_tensor(states.master, s_dt, b - a, "states.master")
     if hp.weight_decay != 0.0 and hp.wd_mask is not None and not isinstance(hp.wd_mask, int):
         import torch

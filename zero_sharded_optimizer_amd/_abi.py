@@ -18,6 +18,9 @@ ZERO_MODE_F64 = 0
 ZERO_MODE_F32 = 1
 ZERO_MODE_MIXED_BF16 = 2
 
+ZERO_OPT_ADAM = 0
+ZERO_OPT_SGD = 1
+
 ZERO_MAX_WORKERS = 256
 
 STATUS_NAMES = {ZERO_OK: "ZERO_OK", ZERO_EINVAL: "ZERO_EINVAL",
@@ -30,13 +33,17 @@ class zero_hparams(C.Structure):
         ("n_workers", C.c_int32),
         ("rank", C.c_int32),
         ("mode", C.c_int32),
-        ("reserved", C.c_int32),
+        ("optimizer", C.c_int32),
         ("lr", C.c_double),
         ("beta1", C.c_double),
         ("beta2", C.c_double),
         ("eps", C.c_double),
         ("weight_decay", C.c_double),
         ("wd_mask", C.c_void_p),
+        ("momentum", C.c_double),
+        ("dampening", C.c_double),
+        ("nesterov", C.c_int32),
+        ("reserved", C.c_int32),
     ]
 
 

@@ -86,11 +86,24 @@ zero_status check_hparams(const zero_hparams* hp, bool for_step, Widths* wd, int
     *a = 0;
     *b = hp->n;
   }
+  if (hp->optimizer != ZERO_OPT_ADAM && hp->optimizer != ZERO_OPT_SGD)
+    return fail(ZERO_EINVAL, "unknown optimizer %d", hp->optimizer);
   if (!for_step) return ZERO_OK;
   if (!std::isfinite(hp->lr)) return fail(ZERO_EINVAL, "lr must be finite");
-  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return fail(ZERO_EINVAL, "beta1 must be in [0, 1)");
-  if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return fail(ZERO_EINVAL, "beta2 must be in [0, 1)");
-  if (!(std::isfinite(hp->eps) && hp->eps > 0.0)) return fail(ZERO_EINVAL, "eps must be finite and > 0");
+  if (hp->optimizer == ZERO_OPT_ADAM) {
+    if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0)) return fail(ZERO_EINVAL, "beta1 must be in [0, 1)");
+    if (!(hp->beta2 >= 0.0 && hp->beta2 < 1.0)) return fail(ZERO_EINVAL, "beta2 must be in [0, 1)");
+    if (!(std::isfinite(hp->eps) && hp->eps > 0.0))
+      return fail(ZERO_EINVAL, "eps must be finite and > 0");
+  } else {
+    if (!(std::isfinite(hp->momentum) && hp->momentum >= 0.0))
+      return fail(ZERO_EINVAL, "momentum must be finite and >= 0");
+    if (!(hp->dampening >= 0.0 && hp->dampening <= 1.0))
+      return fail(ZERO_EINVAL, "dampening must be in [0, 1]");
+    if (hp->nesterov != 0 && hp->nesterov != 1) return fail(ZERO_EINVAL, "nesterov must be 0 or 1");
+    if (hp->nesterov && !(hp->momentum > 0.0 && hp->dampening == 0.0))
+      return fail(ZERO_EINVAL, "nesterov needs momentum > 0 and dampening == 0");
+  }
   if (!(std::isfinite(hp->weight_decay) && hp->weight_decay >= 0.0))
     return fail(ZERO_EINVAL, "weight_decay must be finite and >= 0");
   if (hp->wd_mask != nullptr && !aligned(hp->wd_mask, 4))
@@ -102,8 +115,10 @@ zero_status check_hparams(const zero_hparams* hp, bool for_step, Widths* wd, int
 // and the role of the master pointer per mode.
 zero_status check_states(const zero_hparams* hp, const zero_states* st, const Widths& wd) {
   if (st == nullptr) return fail(ZERO_EINVAL, "states is NULL");
-  if (st->m == nullptr || st->v == nullptr) return fail(ZERO_EINVAL, "states.m / states.v is NULL");
-  if (!aligned(st->m, 16) || !aligned(st->v, 16))
+  const bool sgd = hp->optimizer == ZERO_OPT_SGD;
+  if (st->m == nullptr) return fail(ZERO_EINVAL, "states.m is NULL");
+  if (st->v == nullptr && !sgd) return fail(ZERO_EINVAL, "states.v is NULL");
+  if (!aligned(st->m, 16) || (st->v != nullptr && !aligned(st->v, 16)))
     return fail(ZERO_EINVAL, "states.m and states.v must be 16-byte aligned");
   const bool need_master = hp->mode == ZERO_MODE_MIXED_BF16 || hp->rank >= 0;
   if (need_master && st->master == nullptr)
@@ -181,7 +196,8 @@ zero_status zero_init_states(const zero_hparams* hp, const void* param, const ze
     return fail(ZERO_EINVAL, "param must be aligned to its element size");
   const int64_t len = b - a;
   const Range r_m{(uintptr_t)st->m, (uintptr_t)st->m + (uintptr_t)(len * wd.state), "m"};
-  const Range r_v{(uintptr_t)st->v, (uintptr_t)st->v + (uintptr_t)(len * wd.state), "v"};
+  const Range r_v{(uintptr_t)st->v, st->v ? (uintptr_t)st->v + (uintptr_t)(len * wd.state) : 0,
+                  "v"};
   const Range r_ms{(uintptr_t)st->master,
                    st->master ? (uintptr_t)st->master + (uintptr_t)(len * wd.state) : 0, "master"};
   const Range r_p{(uintptr_t)param + (uintptr_t)(a * wd.param),
@@ -242,7 +258,9 @@ zero_status build_step(const zero_hparams* hp, void* param, const void* const* g
   written[nw++] = {(uintptr_t)param + (uintptr_t)(a * wd.param),
                    (uintptr_t)param + (uintptr_t)(b * wd.param), "param"};
   written[nw++] = {(uintptr_t)st->m, (uintptr_t)st->m + (uintptr_t)(len * wd.state), "m"};
-  written[nw++] = {(uintptr_t)st->v, (uintptr_t)st->v + (uintptr_t)(len * wd.state), "v"};
+  const bool adam = hp->optimizer == ZERO_OPT_ADAM;
+  if (adam)
+    written[nw++] = {(uintptr_t)st->v, (uintptr_t)st->v + (uintptr_t)(len * wd.state), "v"};
   if (st->master)
     written[nw++] = {(uintptr_t)st->master, (uintptr_t)st->master + (uintptr_t)(len * wd.state),
                      "master"};
@@ -294,7 +312,13 @@ zero_status build_step(const zero_hparams* hp, void* param, const void* const* g
   la->n_workers_value = (double)ngp;
   la->clip_sumsq = nullptr;
   la->max_norm = 0.0;
-  if (!(la->bias1 > 0.0) || !(la->bias2 > 0.0))
+  la->optimizer = hp->optimizer;
+  la->momentum = hp->momentum;
+  la->one_minus_dampening = 1.0 - hp->dampening;
+  la->weight_decay = hp->weight_decay;
+  la->nesterov = hp->nesterov;
+  la->first = t == 1;
+  if (adam && (!(la->bias1 > 0.0) || !(la->bias2 > 0.0)))
     return fail(ZERO_EINVAL, "bias correction 1 - beta^t is not positive (beta = 0 is fine; "
                              "check beta and t)");
   return ZERO_OK;

@@ -109,6 +109,9 @@ struct GradSet {
 template <class S>
 struct Consts {
   S beta1, beta2, omb1, omb2, bias1, bias2, lr, eps, decay, nw;
+  // momentum SGD
+  S wd, mom, omd;
+  int has_mom, nesterov, first;
 };
 
 // ---------------------------------------------------------------------------
@@ -325,6 +328,38 @@ __device__ __forceinline__ void adam_element(S s, S& w, S& m, S& v, bool decay,
   v = v_new;
 }
 
+// Momentum SGD for one element, in the defined order (coupled decay, buffer
+// set to the first step's d, optional dampening and Nesterov).
+template <class S>
+__device__ __forceinline__ void sgd_element(S s, S& w, S& buf, bool decay, const Consts<S>& c,
+                                            bool clip, S coef) {
+  S d = s / c.nw;
+  if (clip) d = d * coef;
+  if (decay) {
+    const S dw = c.wd * w;
+    d = d + dw;
+  }
+  if (c.has_mom) {
+    S b;
+    if (c.first) {
+      b = d;
+    } else {
+      const S kept = c.mom * buf;
+      const S added = c.omd * d;
+      b = kept + added;
+    }
+    buf = b;
+    if (c.nesterov) {
+      const S nb = c.mom * b;
+      d = d + nb;
+    } else {
+      d = b;
+    }
+  }
+  const S step = c.lr * d;
+  w = w - step;
+}
+
 // Decay flags of elements j .. j+VEC-1 (bit e of the result is element j+e).
 template <int VEC>
 __device__ __forceinline__ uint32_t decay_bits(const uint32_t* __restrict__ mask,
@@ -338,7 +373,7 @@ __device__ __forceinline__ uint32_t decay_bits(const uint32_t* __restrict__ mask
 
 // The fused step. NFIX > 0: exactly NFIX workers; NFIX == 0: any N <= CAP,
 // loaded in batches of 8 workers. Each thread handles C groups of one tile.
-template <class M, int NFIX, int CAP, int BLOCK, int C>
+template <class M, int NFIX, int CAP, int BLOCK, int C, int OPT>
 __global__ void __launch_bounds__(BLOCK)
     zero_step_kernel(GradSet<CAP> gs, int nw, typename M::S* __restrict__ w,
                      typename M::S* __restrict__ m, typename M::S* __restrict__ v,
@@ -395,23 +430,27 @@ __global__ void __launch_bounds__(BLOCK)
     }
   }
 
-  // 2. Adam on the elements' own state, 3. all-gather write-back
+  // 2. the optimizer on the elements' own state, 3. all-gather write-back
 #pragma unroll
   for (int u = 0; u < C; ++u) {
     if (!live[u]) continue;
     const int64_t g = g0 + (int64_t)u * BLOCK;
     S wv[VEC], mv[VEC], vv[VEC];
     StateIO<M>::load(w, g, wv);
-    StateIO<M>::load(m, g, mv);
-    StateIO<M>::load(v, g, vv);
+    if (OPT == 0 || c.has_mom) StateIO<M>::load(m, g, mv);
+    if (OPT == 0) StateIO<M>::load(v, g, vv);
     uint32_t dbits = 0;
     if (decay_kind == 1) dbits = (1u << VEC) - 1u;
     else if (decay_kind == 2) dbits = decay_bits<VEC>(mask, mask_off + g * VEC);
 #pragma unroll
-    for (int e = 0; e < VEC; ++e)
-      adam_element<S>(s[u][e], wv[e], mv[e], vv[e], (dbits >> e) & 1u, c, clip, coef);
-    StateIO<M>::store(m, g, mv);
-    StateIO<M>::store(v, g, vv);
+    for (int e = 0; e < VEC; ++e) {
+      if constexpr (OPT == 0)
+        adam_element<S>(s[u][e], wv[e], mv[e], vv[e], (dbits >> e) & 1u, c, clip, coef);
+      else
+        sgd_element<S>(s[u][e], wv[e], mv[e], (dbits >> e) & 1u, c, clip, coef);
+    }
+    if (OPT == 0 || c.has_mom) StateIO<M>::store(m, g, mv);
+    if (OPT == 0) StateIO<M>::store(v, g, vv);
     StateIO<M>::store(w, g, wv);
     if (out != nullptr) {
       if (out_vec) {
@@ -429,16 +468,23 @@ __global__ void __launch_bounds__(BLOCK)
     typedef typename M::G G;
     S sum = grad_elem(reinterpret_cast<const G*>(gs.p[0]), i);
     for (int k = 1; k < N; ++k) sum = sum + grad_elem(reinterpret_cast<const G*>(gs.p[k]), i);
-    S wi = w[i], mi = m[i], vi = v[i];
     bool dec = decay_kind == 1;
     if (decay_kind == 2) {
       const int64_t bit = mask_off + i;
       dec = (mask[bit >> 5] >> (bit & 31)) & 1u;
     }
-    adam_element<S>(sum, wi, mi, vi, dec, c, clip, coef);
+    S wi = w[i];
+    if constexpr (OPT == 0) {
+      S mi = m[i], vi = v[i];
+      adam_element<S>(sum, wi, mi, vi, dec, c, clip, coef);
+      m[i] = mi;
+      v[i] = vi;
+    } else {
+      S bi = c.has_mom ? m[i] : S(0);
+      sgd_element<S>(sum, wi, bi, dec, c, clip, coef);
+      if (c.has_mom) m[i] = bi;
+    }
     w[i] = wi;
-    m[i] = mi;
-    v[i] = vi;
     if (out != nullptr) out[i] = OutIO<M>::conv(wi);
   }
 }
@@ -568,7 +614,7 @@ __global__ void __launch_bounds__(kInitBlock)
   const int64_t stride = (int64_t)gridDim.x * kInitBlock;
   for (int64_t i = (int64_t)blockIdx.x * kInitBlock + threadIdx.x; i < len; i += stride) {
     m[i] = S(0);
-    v[i] = S(0);
+    if (v != nullptr) v[i] = S(0);
     if (master != nullptr) {
       if constexpr (sizeof(typename M::P) == 2)
         master[i] = bf16_to_f32(param[i]);
@@ -606,6 +652,12 @@ Consts<S> round_consts(const zlaunch::StepArgs& a) {
   c.eps = (S)a.eps;
   c.decay = (S)a.decay_factor;
   c.nw = (S)a.n_workers_value;
+  c.wd = (S)a.weight_decay;
+  c.mom = (S)a.momentum;
+  c.omd = (S)a.one_minus_dampening;
+  c.has_mom = a.momentum != 0.0;
+  c.nesterov = a.nesterov;
+  c.first = a.first;
   return c;
 }
 
@@ -639,11 +691,18 @@ void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
   for (int k = 0; k < CAP; ++k) gs.p[k] = k < a.n_workers ? a.grads[k] : nullptr;
   const int out_vec =
       a.out != nullptr && (reinterpret_cast<uintptr_t>(a.out) % OutIO<M>::kAlign == 0);
-  hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C>), dim3((unsigned)blocks),
-                     dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
-                     static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
-                     out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
-                     a.decay_kind, a.clip_sumsq, a.max_norm);
+  if (a.optimizer == 0)
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0>), dim3((unsigned)blocks),
+                       dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
+                       static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
+                       out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
+                       a.decay_kind, a.clip_sumsq, a.max_norm);
+  else
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1>), dim3((unsigned)blocks),
+                       dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
+                       static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
+                       out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
+                       a.decay_kind, a.clip_sumsq, a.max_norm);
 }
 
 template <class M>

@@ -30,6 +30,11 @@ struct StepArgs {
   // Global-norm clipping: device pointer to the squared norm, or nullptr.
   const double* clip_sumsq;
   double max_norm;
+  // Optimizer: 0 Adam/AdamW, 1 momentum SGD (momentum, 1-dampening, weight
+  // decay in double; nesterov; first = t == 1).
+  int optimizer;
+  double momentum, one_minus_dampening, weight_decay;
+  int nesterov, first;
 };
 
 // The materialised reduce-scatter mean of one call's range.
