@@ -6,11 +6,11 @@
  * (scratchllm.com/problems/zero-sharded-optimizer), sections "The step", "The
  * shards" and "What to implement": N workers hold full-length local gradients;
  * the parameter indices are split into N shards by np.array_split; (1) a
- * reduce-scatter gives worker r the mean over all workers of the gradient on
- * its shard only, (2) worker r runs Adam on its shard with its own m and v,
+ * reduce-scatter gives worker r the average, over the workers, of the gradient
+ * entries in its own shard, (2) worker r runs Adam on its shard with its own m and v,
  * (3) an all-gather leaves the full updated parameter vector on every worker.
- * Per "Requirements" the result equals ordinary Adam on the full vector with
- * the mean gradient. Stages and memory follow "Data parallelism and ZeRO
+ * Per "Requirements" the outcome matches ordinary Adam over the whole vector
+ * driven by the averaged gradient. Stages and memory follow "Data parallelism and ZeRO
  * stages 1 to 3" (openlearn L11.3), sections "2. Principles" and "4. The
  * interface".
  *
@@ -194,8 +194,8 @@ zero_status zero_step_range(const zero_hparams* hp, void* param, const void* con
  * "Data parallelism and ZeRO stages 1 to 3", section "2. Principles": stage 1
  * keeps the averaged gradient in .grad ("Your emulation's bookkeeping"), and
  * the reduce-scatter of stage 2 leaves each rank its chunk of it; section
- * "Going further": sharded global-norm clipping is an all-reduce of the
- * squared chunk norms before the step. The clipping factor is
+ * "Going further": sharded global-norm clipping sums the chunks'
+ * squared norms across ranks ahead of the update. The clipping factor is
  * min(1, max_norm / (sqrt(sumsq) + 1e-6)) in double (the definition torch's
  * clip_grad_norm_ uses), rounded once to S and multiplied into the mean
  * gradient before the moments. The squared norm is summed in double in a fixed

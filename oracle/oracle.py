@@ -133,7 +133,7 @@ class Oracle:
 
     def full_step(self, mode, param, grads, master, m, v, t, lr, b1=0.9, b2=0.999,
                   eps=1e-8, wd=0.0, decay=None):
-        """Shard-free Adam on the full vector with the mean gradient."""
+        """Shard-free Adam over the whole vector driven by the averaged gradient."""
         return self._call_full(self.lib.orc_full_step, mode, param, grads, master, m, v,
                                t, lr, b1, b2, eps, wd, decay)
 

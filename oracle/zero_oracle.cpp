@@ -11,8 +11,8 @@
 //     "What to implement", "Requirements": N workers, shard i is
 //     np.array_split(np.arange(n), N)[i]; (1) reduce-scatter of the mean gradient,
 //     (2) Adam on each shard with that shard's own m and v, (3) all-gather of the
-//     updated shards; the result must equal ordinary Adam on the full vector with
-//     the mean gradient.
+//     updated shards; the outcome must match ordinary Adam over the whole vector
+//     driven by the averaged gradient.
 //   * "Data parallelism and ZeRO stages 1 to 3" (openlearn L11.3), section
 //     "2. Principles" (chunked elementwise update, reduce-scatter then divide by p,
 //     the memory table and the emulation's bookkeeping) and section "3. Worked
@@ -52,7 +52,7 @@
 //     coupled L2 decay, the buffer set to the first step's gradient, optional
 //     dampening and Nesterov; see sgd_update.
 //   * Global-norm clipping ("Data parallelism and ZeRO stages 1 to 3", section
-//     "Going further": an all-reduce of squared chunk norms before the step;
+//     "Going further": the squared norms of the chunks, summed across ranks ahead of the update;
 //     no formula): each shard's squared norm of its mean gradient, summed in
 //     index order in double, then summed over shards in rank order; the factor
 //     min(1, max_norm / (sqrt(sum) + 1e-6)) in double, as torch's
@@ -93,7 +93,7 @@ void split_bounds(int64_t n, int64_t N, int64_t r, int64_t* a, int64_t* b) {
   int64_t start = 0;
   for (int64_t k = 0; k < r; ++k) start += section_size(n, N, k);
 #if ORACLE_MUTANT == 2
-  // planted: a rank starting from the wrong chunk (ignores the extra elements)
+  // planted: a rank beginning at the neighbour's chunk (ignores the extra elements)
   start = r * (n / N);
 #endif
   *a = start;
@@ -410,8 +410,8 @@ void sharded_step(int mode, int64_t n, int64_t N, const void* param_in,
 }
 
 // ---------------------------------------------------------------------------
-// Shard-free reference: ordinary Adam on the full vector with the mean
-// gradient ("ZeRO-Sharded Adam Step", section "Requirements", first item).
+// Shard-free reference: ordinary Adam over the whole vector driven by the
+// averaged gradient ("ZeRO-Sharded Adam Step", section "Requirements", first item).
 // ---------------------------------------------------------------------------
 template <class S>
 void full_step(int mode, int64_t n, int64_t N, const void* param_in,
@@ -474,8 +474,8 @@ void rank_step(int mode, int64_t n, int64_t N, int64_t r, const void* param_in,
 // ---------------------------------------------------------------------------
 // Squared norm of one shard's mean gradient, summed in index order in double.
 // "Data parallelism and ZeRO stages 1 to 3", section "Going further": sharded
-// global-norm clipping is an all-reduce of the squared chunk norms before the
-// step.
+// global-norm clipping is the chunks' squared norms summed across ranks ahead of
+// the update.
 // ---------------------------------------------------------------------------
 template <class S>
 double shard_sumsq(const std::vector<S>& g) {

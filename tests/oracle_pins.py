@@ -280,7 +280,8 @@ def _case_for_mode(rng, mode, n, N):
 
 def pin_sharded_equals_shard_free(O):
     """ZeRO-Sharded Adam Step, 'Requirements': the sharded result equals ordinary Adam
-    on the full vector with the mean gradient, bit for bit, for every shard count."""
+    over the whole vector driven by the averaged gradient, bit for bit, for every
+    shard count."""
     rng = np.random.default_rng(17)
     for mode in (MODE_F64, MODE_F32, MODE_MIXED):
         for n, N in ((1, 1), (3, 5), (10, 4), (1031, 7), (4096, 64), (777, 2)):

@@ -2,7 +2,7 @@
 
 The mistakes follow the pitfall list of 'Data parallelism and ZeRO stages 1 to 3'
 (openlearn L11.3, section '5. Pitfalls': summing instead of averaging, a rank
-starting from the wrong chunk, no all-gather after the update, stage 2 keeping the
+beginning at another rank's chunk, no all-gather after the update, stage 2 keeping the
 full gradients, dropped hyperparameters) plus plausible slips in the Adam formula
 itself (exchanged betas, a dropped bias correction, eps inside the square root,
 coupled instead of decoupled decay, a wrong sign, an off-by-one step count, an

@@ -9,8 +9,9 @@
 //      buffer (bf16 in mixed precision, in place otherwise).
 // Because all logical workers share one HBM, the shard of an element only says
 // which worker "owns" it; the arithmetic of every element is the same
-// ("Data parallelism and ZeRO stages 1 to 3", section "2. Principles": the
-// chunked update equals the single-process update entry by entry). So the
+// ("Data parallelism and ZeRO stages 1 to 3", section "2. Principles": an
+// elementwise optimizer on a chunk reproduces the unsharded result for those
+// elements). So the
 // kernel streams the flat index space: each byte of every input is read from
 // HBM once and each output byte written once. No LDS, no atomics, no MFMA:
 // there is no contraction and no reuse, so the design is all about keeping
