@@ -56,8 +56,15 @@ def bytes_per_param_clipped(wl):
 
 
 def kernel_hash():
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace removed, so a
+    comment-only edit does not mark the measured traffic as stale."""
+    import re
+    with open(KERNEL_SRC) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    src = re.sub(r"\s+", "", src)
+    return hashlib.sha256(src.encode()).hexdigest()[:16]
 
 
 def load_traffic(workload, algo_bytes):
