@@ -1,0 +1,129 @@
+// Host-only driver for the sanitizer test: exercises the C ABI's host logic
+// (validation, shard bounds, memory model, workspace sizes) with the launch
+// layer replaced by stubs, so that it runs under AddressSanitizer and
+// UndefinedBehaviorSanitizer on a machine without a GPU. Any launch reaching the
+// stubs is counted, never executed.
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "zero_adam.h"
+#include "zero_launch.h"
+
+static int g_launches = 0;
+
+namespace zlaunch {
+const char* launch_step(const StepArgs&, void*) { ++g_launches; return nullptr; }
+const char* launch_init(const InitArgs&, void*) { ++g_launches; return nullptr; }
+const char* launch_step_mean(const StepArgs&, void*) { ++g_launches; return nullptr; }
+const char* launch_mean(const MeanArgs&, void*) { ++g_launches; return nullptr; }
+int64_t mean_partials(int, int64_t len) { return len / 1024 + 1; }
+}  // namespace zlaunch
+
+static int g_fail = 0;
+#define CHECK(c)                                                      \
+  do {                                                                \
+    if (!(c)) {                                                       \
+      std::fprintf(stderr, "FAIL %s:%d %s\n", __FILE__, __LINE__, #c); \
+      ++g_fail;                                                       \
+    }                                                                 \
+  } while (0)
+
+static zero_hparams hp(int64_t n, int32_t N, int32_t rank, int32_t mode) {
+  zero_hparams h;
+  std::memset(&h, 0, sizeof h);
+  h.n = n;
+  h.n_workers = N;
+  h.rank = rank;
+  h.mode = mode;
+  h.lr = 1e-3;
+  h.beta1 = 0.9;
+  h.beta2 = 0.999;
+  h.eps = 1e-8;
+  return h;
+}
+
+int main() {
+  // shard bounds: cover [0, n) exactly, numpy's rule
+  for (int64_t n = 0; n < 300; n += 7)
+    for (int32_t N = 1; N < 70; ++N) {
+      int64_t prev = 0;
+      for (int32_t r = 0; r < N; ++r) {
+        int64_t a, b;
+        CHECK(zero_shard_bounds(n, N, r, &a, &b) == ZERO_OK);
+        CHECK(a == prev && b >= a && b - a >= n / N && b - a <= n / N + 1);
+        prev = b;
+      }
+      CHECK(prev == n);
+    }
+  int64_t a, b;
+  CHECK(zero_shard_bounds(8000000000LL, 8, 7, &a, &b) == ZERO_OK && b == 8000000000LL);
+  CHECK(zero_shard_bounds(10, 0, 0, &a, &b) == ZERO_EINVAL && std::strlen(zero_last_error()) > 0);
+
+  // memory model over a wide range, including the largest counts
+  zero_mem m;
+  for (int32_t stage = 0; stage <= 3; ++stage)
+    for (int32_t mode = 0; mode <= 2; ++mode) {
+      CHECK(zero_memory_bytes(175000000000LL, 64, 63, stage, mode, 0, &m) == ZERO_OK);
+      CHECK(m.total == m.params + m.grads + m.optimizer);
+    }
+  CHECK(zero_memory_bytes(10, 4, 0, 4, 0, 0, &m) == ZERO_EINVAL);
+
+  // step validation with fake, aligned, non-overlapping addresses
+  const uintptr_t A = (uintptr_t)1 << 32;
+  const void* grads[256];
+  for (int k = 0; k < 256; ++k) grads[k] = (const void*)(A + ((uintptr_t)(3 + k) << 24));
+  zero_states st = {nullptr, (void*)(A + (1u << 24)), (void*)(A + (2u << 24))};
+  zero_hparams h = hp(1000, 4, -1, ZERO_MODE_F32);
+  CHECK(zero_step(&h, (void*)A, grads, &st, 1, nullptr) == ZERO_OK);
+  CHECK(zero_step(&h, (void*)A, grads, &st, 0, nullptr) == ZERO_EINVAL);
+  h.beta1 = 1.0;
+  CHECK(zero_step(&h, (void*)A, grads, &st, 1, nullptr) == ZERO_EINVAL);
+  h = hp(1000, 256, -1, ZERO_MODE_F32);
+  CHECK(zero_step(&h, (void*)A, grads, &st, 1, nullptr) == ZERO_OK);
+  h = hp(1000, 257, -1, ZERO_MODE_F32);
+  CHECK(zero_step(&h, (void*)A, grads, &st, 1, nullptr) == ZERO_EINVAL);
+  // rank mode, ragged shards, misaligned slot is fine
+  zero_states stm = {(void*)(A + ((uintptr_t)300 << 24)), (void*)(A + (1u << 24)), (void*)(A + (2u << 24))};
+  h = hp(8 * 1001 + 3, 8, 3, ZERO_MODE_MIXED_BF16);
+  CHECK(zero_step(&h, (void*)A, grads, &stm, 2, nullptr) == ZERO_OK);
+  CHECK(zero_step_range(&h, (void*)A, grads, &stm, 2, 8, 800, nullptr) == ZERO_OK);
+  CHECK(zero_step_range(&h, (void*)A, grads, &stm, 2, 4, 800, nullptr) == ZERO_EINVAL);
+  // empty shard: nothing launched, pointers may be NULL
+  const int before = g_launches;
+  h = hp(3, 5, 4, ZERO_MODE_F64);
+  CHECK(zero_step(&h, nullptr, nullptr, nullptr, 1, nullptr) == ZERO_OK);
+  CHECK(g_launches == before);
+  // SGD
+  h = hp(1000, 4, -1, ZERO_MODE_F32);
+  h.optimizer = ZERO_OPT_SGD;
+  h.momentum = 0.9;
+  zero_states sts = {nullptr, (void*)(A + (1u << 24)), nullptr};
+  CHECK(zero_step(&h, (void*)A, grads, &sts, 1, nullptr) == ZERO_OK);
+  h.nesterov = 1;
+  h.dampening = 0.5;
+  CHECK(zero_step(&h, (void*)A, grads, &sts, 1, nullptr) == ZERO_EINVAL);
+  // clipping and mean gradient
+  h = hp(100000, 8, -1, ZERO_MODE_F32);
+  size_t ws = 0;
+  CHECK(zero_step_clipped_workspace_bytes(&h, &ws) == ZERO_OK && ws >= 400000);
+  CHECK(zero_step_clipped(&h, (void*)A, grads, &st, 1, 1.0, nullptr, (void*)(A + ((uintptr_t)340 << 24)),
+                          ws, nullptr) == ZERO_OK);
+  CHECK(zero_step_clipped(&h, (void*)A, grads, &st, 1, NAN, nullptr, (void*)(A + ((uintptr_t)340 << 24)),
+                          ws, nullptr) == ZERO_EINVAL);
+  size_t mws = 0;
+  CHECK(zero_mean_grad_workspace_bytes(&h, &mws) == ZERO_OK);
+  CHECK(zero_mean_grad(&h, grads, (void*)(A + ((uintptr_t)350 << 24)), (double*)(A + ((uintptr_t)360 << 24)),
+                       (void*)(A + ((uintptr_t)361 << 24)), mws, nullptr) == ZERO_OK);
+  CHECK(zero_step_mean(&h, (void*)A, (void*)(A + ((uintptr_t)350 << 24)), &st, 1,
+                       (const double*)(A + ((uintptr_t)360 << 24)), 1.0, nullptr) == ZERO_OK);
+  // NULL everywhere
+  CHECK(zero_step(nullptr, nullptr, nullptr, nullptr, 1, nullptr) == ZERO_EINVAL);
+  CHECK(zero_init_states(nullptr, nullptr, nullptr, nullptr) == ZERO_EINVAL);
+  CHECK(zero_memory_bytes(1, 1, 0, 0, 0, 0, nullptr) == ZERO_EINVAL);
+
+  std::printf("host driver: %d launches reached the stubs, %d failures\n", g_launches, g_fail);
+  return g_fail == 0 ? 0 : 1;
+}
