@@ -72,8 +72,9 @@ def compare(name, got, ref, kind):
         stats["max_ulp"] = 0
         return stats
     assert kind == "f32", kind
-    diff = np.abs(got.astype(np.float64) - ref.astype(np.float64))
-    lim = F32_REL * np.maximum(1.0, np.abs(ref.astype(np.float64)))
+    with np.errstate(invalid="ignore", over="ignore"):  # inf - inf where both are inf
+        diff = np.abs(got.astype(np.float64) - ref.astype(np.float64))
+        lim = F32_REL * np.maximum(1.0, np.abs(ref.astype(np.float64)))
     bad = np.flatnonzero(~(same | (diff <= lim)))
     stats["max_abs"] = float(np.nanmax(diff, initial=0.0)) if n else 0.0
     stats["max_ulp"] = int(np.max(np.where(same, 0, ulp_distance(got, ref)), initial=0))
