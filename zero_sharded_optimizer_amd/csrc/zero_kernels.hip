@@ -41,14 +41,13 @@ namespace {
 // Cache policy and launch shape. The step touches every byte once, so loads
 // and stores carry the nontemporal hint (stream through the caches without
 // keeping the lines). The grid is not persistent: block b owns one tile of
-// BLOCK * C consecutive groups (thread t takes groups t, t + BLOCK, ...,
-// t + (C-1) * BLOCK of the tile, so every load instruction of a wave covers
-// 512 B or 1 KiB of one stream), and blocks retire and start in address order,
-// so the window of in-flight requests sweeps each stream front to back. A
+// BLOCK * C consecutive groups, and blocks retire and start in address order,
+// so the window of in-flight requests sweeps each stream front to back. Within
+// the tile a thread takes C groups, BLOCK or 64 groups apart (WC below), so
+// every load instruction of a wave covers 512 B or 1 KiB of one stream. A
 // thread issues the gradient loads of all its C groups before it adds any.
 // Measured on MI355X, this beats a grid-stride persistent loop by about 25 % on
-// the many-stream mix of the step; C > 1 helps when registers allow (fp32),
-// and costs occupancy where they do not (mixed precision).
+// the many-stream mix of the step.
 #ifndef ZERO_STEP_NT_LOAD
 #define ZERO_STEP_NT_LOAD 1
 #endif
@@ -58,10 +57,20 @@ namespace {
 // Any-N path (N not 1, 2, 4 or 8): gradient loads issued per batch (4, 8 and
 // 16 measured the same on MI355X).
 constexpr int kWideBatch = 8;
-// (BLOCK, C, PRELOAD) per mode; overridable at build time for tuning. PRELOAD 1:
-// a thread issues its state loads together with its gradient loads, before it
-// waits on any; 0: after the gradients are folded. Measured on MI355X, 1 gains
-// about 1 % in fp32 and loses about 6 % in mixed precision; fp64 is even.
+// Launch shape per mode: BLOCK threads, C groups per thread, PRELOAD, WC;
+// overridable at build time for tuning. PRELOAD 1: a thread issues its state
+// loads together with its gradient loads, before it waits on any; 0: after the
+// gradients are folded. WC 1: the C groups of a thread are 64 groups apart, so
+// each wave covers C * 64 consecutive groups; 0: BLOCK groups apart. F32W is
+// the fp32 shape for any N (not 1, 2, 4 or 8). Chosen by interleaved sweeps on
+// MI355X (same process, same buffers):
+//   fp32, N = 8:       512 x 2, PRELOAD, strided groups (WC and 4 groups lose
+//                      up to 1 %; 1024 threads lose 5 %);
+//   mixed, N = 8:      512 x 2, PRELOAD, WC: 4 % over 256 x 1 (PRELOAD alone at
+//                      256 x 1 loses 6 %);
+//   fp32, N = 64:      128 x 8, WC, no PRELOAD: 3 % over 512 x 2 (368 registers,
+//                      one wave per SIMD, 64 loads of 1 KiB in flight per wave);
+//   fp64 (1 M params): 256 x 1; launch-bound, every shape within noise.
 #ifndef ZERO_F64_BLOCK
 #define ZERO_F64_BLOCK 256
 #endif
@@ -70,6 +79,9 @@ constexpr int kWideBatch = 8;
 #endif
 #ifndef ZERO_F64_PRELOAD
 #define ZERO_F64_PRELOAD 0
+#endif
+#ifndef ZERO_F64_WC
+#define ZERO_F64_WC 0
 #endif
 #ifndef ZERO_F32_BLOCK
 #define ZERO_F32_BLOCK 512
@@ -80,14 +92,32 @@ constexpr int kWideBatch = 8;
 #ifndef ZERO_F32_PRELOAD
 #define ZERO_F32_PRELOAD 1
 #endif
+#ifndef ZERO_F32_WC
+#define ZERO_F32_WC 0
+#endif
+#ifndef ZERO_F32W_BLOCK
+#define ZERO_F32W_BLOCK 128
+#endif
+#ifndef ZERO_F32W_GROUPS
+#define ZERO_F32W_GROUPS 8
+#endif
+#ifndef ZERO_F32W_PRELOAD
+#define ZERO_F32W_PRELOAD 0
+#endif
+#ifndef ZERO_F32W_WC
+#define ZERO_F32W_WC 1
+#endif
 #ifndef ZERO_MIX_BLOCK
-#define ZERO_MIX_BLOCK 256
+#define ZERO_MIX_BLOCK 512
 #endif
 #ifndef ZERO_MIX_GROUPS
-#define ZERO_MIX_GROUPS 1
+#define ZERO_MIX_GROUPS 2
 #endif
 #ifndef ZERO_MIX_PRELOAD
-#define ZERO_MIX_PRELOAD 0
+#define ZERO_MIX_PRELOAD 1
+#endif
+#ifndef ZERO_MIX_WC
+#define ZERO_MIX_WC 1
 #endif
 
 constexpr int kInitBlock = 256;
@@ -409,7 +439,7 @@ __device__ __forceinline__ void load_states(typename M::S* __restrict__ w,
 // thread's groups may lie past the end (only in the last block of the grid);
 // otherwise no load is predicated, so the loads form one straight run with no
 // branches between them.
-template <class M, int NFIX, int CAP, int BLOCK, int C, int OPT, bool PRE, bool GUARD>
+template <class M, int NFIX, int CAP, int GS, int C, int OPT, bool PRE, bool GUARD>
 __device__ __forceinline__ void step_groups(
     const GradSet<CAP>& gs, int N, typename M::S* __restrict__ w, typename M::S* __restrict__ m,
     typename M::S* __restrict__ v, typename M::P* __restrict__ out, int out_vec, int64_t g0,
@@ -419,7 +449,7 @@ __device__ __forceinline__ void step_groups(
   constexpr int VEC = M::VEC;
   bool live[C];
 #pragma unroll
-  for (int u = 0; u < C; ++u) live[u] = !GUARD || g0 + (int64_t)u * BLOCK < ngroups;
+  for (int u = 0; u < C; ++u) live[u] = !GUARD || g0 + (int64_t)u * GS < ngroups;
   const bool use_m = OPT == 0 || c.has_mom;
 
   S s[C][VEC];
@@ -430,9 +460,9 @@ __device__ __forceinline__ void step_groups(
     for (int u = 0; u < C; ++u)
 #pragma unroll
       for (int k = 0; k < NFIX; ++k)
-        if (live[u]) raw[u][k].load(gs.p[k], g0 + (int64_t)u * BLOCK);
+        if (live[u]) raw[u][k].load(gs.p[k], g0 + (int64_t)u * GS);
     if constexpr (PRE)
-      load_states<M, C, OPT, GUARD>(w, m, v, g0, BLOCK, live, use_m, wv, mv, vv);
+      load_states<M, C, OPT, GUARD>(w, m, v, g0, GS, live, use_m, wv, mv, vv);
 #pragma unroll
     for (int u = 0; u < C; ++u) {
       raw[u][0].widen(s[u]);
@@ -441,11 +471,11 @@ __device__ __forceinline__ void step_groups(
     }
   } else {
     if constexpr (PRE)
-      load_states<M, C, OPT, GUARD>(w, m, v, g0, BLOCK, live, use_m, wv, mv, vv);
+      load_states<M, C, OPT, GUARD>(w, m, v, g0, GS, live, use_m, wv, mv, vv);
 #pragma unroll
     for (int u = 0; u < C; ++u) {
       GradRaw<M> r0;
-      if (live[u]) r0.load(gs.p[0], g0 + (int64_t)u * BLOCK);
+      if (live[u]) r0.load(gs.p[0], g0 + (int64_t)u * GS);
       r0.widen(s[u]);
     }
     constexpr int B = kWideBatch;
@@ -455,7 +485,7 @@ __device__ __forceinline__ void step_groups(
       for (int u = 0; u < C; ++u)
 #pragma unroll
         for (int j = 0; j < B; ++j)
-          if (k0 + j < N && live[u]) raw[u][j].load(gs.p[k0 + j], g0 + (int64_t)u * BLOCK);
+          if (k0 + j < N && live[u]) raw[u][j].load(gs.p[k0 + j], g0 + (int64_t)u * GS);
 #pragma unroll
       for (int u = 0; u < C; ++u)
 #pragma unroll
@@ -467,7 +497,7 @@ __device__ __forceinline__ void step_groups(
 #pragma unroll
   for (int u = 0; u < C; ++u) {
     if (!live[u]) continue;
-    const int64_t g = g0 + (int64_t)u * BLOCK;
+    const int64_t g = g0 + (int64_t)u * GS;
     if constexpr (!PRE) {
       StateIO<M>::load(w, g, wv[u]);
       if (use_m) StateIO<M>::load(m, g, mv[u]);
@@ -499,7 +529,7 @@ __device__ __forceinline__ void step_groups(
 
 // The fused step. NFIX > 0: exactly NFIX workers; NFIX == 0: any N <= CAP,
 // loaded in batches of 8 workers. Each thread handles C groups of one tile.
-template <class M, int NFIX, int CAP, int BLOCK, int C, int OPT, bool PRE>
+template <class M, int NFIX, int CAP, int BLOCK, int C, int OPT, bool PRE, bool WC>
 __global__ void __launch_bounds__(BLOCK)
     zero_step_kernel(GradSet<CAP> gs, int nw, typename M::S* __restrict__ w,
                      typename M::S* __restrict__ m, typename M::S* __restrict__ v,
@@ -510,16 +540,19 @@ __global__ void __launch_bounds__(BLOCK)
   typedef typename M::S S;
   constexpr int VEC = M::VEC;
   const int64_t ngroups = len / VEC;
-  const int64_t g0 = (int64_t)blockIdx.x * (BLOCK * C) + threadIdx.x;
+  constexpr int GS = WC ? 64 : BLOCK;
+  const int64_t g0 = WC ? (int64_t)blockIdx.x * (BLOCK * C) + (threadIdx.x / 64) * (64 * C) +
+                              (threadIdx.x % 64)
+                        : (int64_t)blockIdx.x * (BLOCK * C) + threadIdx.x;
   const bool clip = clip_sumsq != nullptr;
   const S coef = clip ? clip_coef<S>(clip_sumsq, max_norm) : S(1);
   const int N = NFIX > 0 ? NFIX : nw;
-  if (g0 + (int64_t)(C - 1) * BLOCK < ngroups)
-    step_groups<M, NFIX, CAP, BLOCK, C, OPT, PRE, false>(gs, N, w, m, v, out, out_vec, g0,
+  if (g0 + (int64_t)(C - 1) * GS < ngroups)
+    step_groups<M, NFIX, CAP, GS, C, OPT, PRE, false>(gs, N, w, m, v, out, out_vec, g0,
                                                          ngroups, c, mask, mask_off, decay_kind,
                                                          clip, coef);
   else if (g0 < ngroups)
-    step_groups<M, NFIX, CAP, BLOCK, C, OPT, PRE, true>(gs, N, w, m, v, out, out_vec, g0,
+    step_groups<M, NFIX, CAP, GS, C, OPT, PRE, true>(gs, N, w, m, v, out, out_vec, g0,
                                                         ngroups, c, mask, mask_off, decay_kind,
                                                         clip, coef);
 
@@ -727,25 +760,34 @@ struct Shape;
 template <>
 struct Shape<ModeF64> {
   static constexpr int BLOCK = ZERO_F64_BLOCK, C = ZERO_F64_GROUPS;
-  static constexpr bool PRE = ZERO_F64_PRELOAD;
+  static constexpr bool PRE = ZERO_F64_PRELOAD, WC = ZERO_F64_WC;
 };
 template <>
 struct Shape<ModeF32> {
   static constexpr int BLOCK = ZERO_F32_BLOCK, C = ZERO_F32_GROUPS;
-  static constexpr bool PRE = ZERO_F32_PRELOAD;
+  static constexpr bool PRE = ZERO_F32_PRELOAD, WC = ZERO_F32_WC;
 };
 template <>
 struct Shape<ModeMixed> {
   static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
-  static constexpr bool PRE = ZERO_MIX_PRELOAD;
+  static constexpr bool PRE = ZERO_MIX_PRELOAD, WC = ZERO_MIX_WC;
+};
+// the step kernel's shape for NFIX fixed workers (0: any N)
+template <class M, int NFIX>
+struct StepShape : Shape<M> {};
+template <>
+struct StepShape<ModeF32, 0> {
+  static constexpr int BLOCK = ZERO_F32W_BLOCK, C = ZERO_F32W_GROUPS;
+  static constexpr bool PRE = ZERO_F32W_PRELOAD, WC = ZERO_F32W_WC;
 };
 
 template <class M, int NFIX, int CAP>
 void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
   typedef typename M::S S;
   typedef typename M::P P;
-  constexpr int BLOCK = Shape<M>::BLOCK, C = Shape<M>::C;
-  constexpr bool PRE = Shape<M>::PRE;
+  typedef StepShape<M, NFIX> SH;
+  constexpr int BLOCK = SH::BLOCK, C = SH::C;
+  constexpr bool PRE = SH::PRE, WC = SH::WC;
   // one tile of BLOCK * C groups per block; at least one block for the
   // leftover elements
   const int64_t ngroups = a.len / M::VEC;
@@ -757,13 +799,13 @@ void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
   const int out_vec =
       a.out != nullptr && (reinterpret_cast<uintptr_t>(a.out) % OutIO<M>::kAlign == 0);
   if (a.optimizer == 0)
-    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0, PRE>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0, PRE, WC>), dim3((unsigned)blocks),
                        dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
                        static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
                        out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
                        a.decay_kind, a.clip_sumsq, a.max_norm);
   else
-    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, PRE>), dim3((unsigned)blocks),
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, PRE, WC>), dim3((unsigned)blocks),
                        dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
                        static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
                        out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
@@ -787,7 +829,7 @@ void launch_mode(const zlaunch::StepArgs& a, hipStream_t st) {
 template <>
 struct Shape<ModeMixedMean> {
   static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
-  static constexpr bool PRE = ZERO_MIX_PRELOAD;
+  static constexpr bool PRE = ZERO_MIX_PRELOAD, WC = ZERO_MIX_WC;
 };
 
 template <class M>
