@@ -220,6 +220,95 @@ def copy_ceiling(nbytes=4 << 30, reps=10):
     return 2 * nbytes / (ms * 1e-3) / 1e9
 
 
+CEIL_SHAPES = ("512x2", "512x2 wave-contiguous", "256x4 wave-contiguous", "256x1")
+
+
+def _zceil():
+    """The streaming-ceiling library (built next to libzero.so)."""
+    import ctypes
+    path = os.path.join(ROOT, "zero_sharded_optimizer_amd", "libzceil.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER
+    lib.zceil_streams.restype = ctypes.c_int
+    lib.zceil_streams.argtypes = [P(ctypes.c_void_p), P(ctypes.c_int32), ctypes.c_int32,
+                                  P(ctypes.c_void_p), P(ctypes.c_int32), ctypes.c_int32,
+                                  ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p]
+    return lib
+
+
+def _time_streams(lib, in_w, out_w, ngroups, reps=10):
+    """Best GB/s of zceil_streams over its launch shapes, on one set of fresh
+    buffers: len(in_w) streams read and len(out_w) written, ngroups groups of
+    in_w[i] / out_w[o] bytes each; per shape the mean over reps launches (HIP
+    events on the launch stream). Returns (GB/s, shape name)."""
+    import ctypes
+    import torch
+    ins = [torch.empty(ngroups * w, dtype=torch.uint8, device="cuda") for w in in_w]
+    outs = [torch.empty(ngroups * w, dtype=torch.uint8, device="cuda") for w in out_w]
+    pin = (ctypes.c_void_p * len(ins))(*[t.data_ptr() for t in ins])
+    pout = (ctypes.c_void_p * len(outs))(*[t.data_ptr() for t in outs])
+    win = (ctypes.c_int32 * len(in_w))(*in_w)
+    wout = (ctypes.c_int32 * len(out_w))(*out_w)
+    stream = torch.cuda.current_stream()
+    nbytes = ngroups * (sum(in_w) + sum(out_w))
+    best = (0.0, None)
+    for shape, name in enumerate(CEIL_SHAPES):
+        def go():
+            rc = lib.zceil_streams(pin, win, len(in_w), pout, wout, len(out_w), ngroups, shape,
+                                   ctypes.c_void_p(stream.cuda_stream))
+            if rc != 0:
+                raise RuntimeError(f"zceil_streams returned {rc}")
+
+        go()
+        go()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record(stream)
+        for _ in range(reps):
+            go()
+        e.record(stream)
+        torch.cuda.synchronize()
+        gbps = nbytes / (s.elapsed_time(e) / reps * 1e-3) / 1e9
+        best = max(best, (gbps, name))
+    del ins, outs
+    torch.cuda.empty_cache()
+    return best
+
+
+def stream_ceilings(wl):
+    """What the memory system delivers, measured in the same run with kernels
+    that move bytes and do no arithmetic (zceil_streams; best of the launch
+    shapes the step uses): a copy of 4 GiB; the workload's N gradient streams
+    read and one 16-byte stream written; and the step's own stream mix at the
+    workload's size (N gradient streams and 3 state streams read, 3 state
+    streams and, in mixed precision, the bf16 copy written)."""
+    lib = _zceil()
+    a, b = wl.shard
+    vec = 2 if wl.mode == 0 else 4
+    ngroups = (b - a) // vec
+    gw = 8 if wl.mode == 2 else 16  # bytes of one group of one gradient stream
+    N = wl.n_workers
+    out = {}
+    out["copy_GBps"], out["copy_shape"] = _time_streams(lib, [16], [16], (4 << 30) // 16)
+    if N <= 16:
+        out["read_n_write_1_GBps"], out["read_n_write_1_shape"] = _time_streams(
+            lib, [gw] * N, [16], ngroups)
+    else:
+        out["read_n_write_1_GBps"] = None
+    writes = [16, 16, 16] + ([8] if wl.mode == 2 else [])
+    out["step_streams"] = (f"{N} x {gw} B + 3 x 16 B read, {len(writes)} streams "
+                           f"({'+'.join(str(w) for w in writes)} B) written per group")
+    if N + 3 <= 16:
+        out["step_streams_GBps"], out["step_streams_shape"] = _time_streams(
+            lib, [gw] * N + [16] * 3, writes, ngroups)
+    else:
+        out["step_streams_GBps"] = None
+        out["step_streams"] += f"; not measured: {N + 3} input streams, the kernel takes 16"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -227,7 +316,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-copy-ceiling", action="store_true")
+    ap.add_argument("--no-copy-ceiling", action="store_true",
+                    help="skip the copy and streaming-ceiling measurements")
     ap.add_argument("--clip", type=float, default=None, metavar="FRACTION",
                     help="time the clipped step (zero_step_clipped) with max_norm set to "
                          "FRACTION times the first step's global gradient norm")
@@ -340,6 +430,9 @@ def main():
     del grads, param, st
     torch.cuda.empty_cache()
     copy_gbps = None if args.no_copy_ceiling else copy_ceiling()
+    ceil = None if args.no_copy_ceiling else stream_ceilings(wl)
+    if ceil is not None and ceil["step_streams_GBps"]:
+        ceil["step_frac_of_step_streams"] = achieved / ceil["step_streams_GBps"]
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
 
     out = {
@@ -367,6 +460,7 @@ def main():
         "kernel_ms_mean": avg_ms,
         "kernel_ms_min": min(kern_ms),
         "copy_ceiling_GBps": copy_gbps,
+        "stream_ceilings": ceil,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "cpu_baseline": cpu,

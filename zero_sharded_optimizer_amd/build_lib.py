@@ -1,4 +1,6 @@
-"""Builds libzero.so, the C-ABI library of the fused step, for gfx950.
+"""Builds libzero.so, the C-ABI library of the fused step, for gfx950, and
+libzceil.so, the streaming-ceiling kernels that bench.py measures the memory
+system with.
 
 The host layer (zero_abi.cpp) is compiled with g++; the kernels
 (zero_kernels.hip) with hipcc for gfx950. Both with multiply-add contraction
@@ -15,6 +17,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libzero.so")
+CEIL_LIB = os.path.join(HERE, "libzceil.so")
 BUILD = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -50,6 +53,12 @@ def build(verbose=False):
             print(" ".join(cmd), flush=True)
         _run(cmd)
     os.replace(LIB + ".tmp", LIB)
+    ceil = [HIPCC, *HIP_FLAGS, "-shared", os.path.join(CSRC, "stream_ceiling.hip"), "-o",
+            CEIL_LIB + ".tmp"]
+    if verbose:
+        print(" ".join(ceil), flush=True)
+    _run(ceil)
+    os.replace(CEIL_LIB + ".tmp", CEIL_LIB)
     return LIB
 
 

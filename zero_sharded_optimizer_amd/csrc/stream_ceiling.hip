@@ -1,0 +1,153 @@
+// Streaming ceiling kernels, used to measure what the memory system delivers
+// for a given mix of streams; not part of the optimizer's interface.
+//
+// zceil_streams reads nin streams and writes nout streams, group by group, with
+// the fused step's access pattern and no floating-point arithmetic: each group
+// index g reads 8 or 16 bytes of every input stream (as the step reads a bf16 or
+// an fp32/fp64 group), folds them with XOR so that no load is dead, and writes
+// 8 or 16 bytes of the result to every output stream. The launch shapes are
+// those the step uses (BLOCK threads, C groups per thread, BLOCK or 64 groups
+// apart), all loads of a thread are issued before any is used, and loads and
+// stores carry the nontemporal hint. With one input and one output it is a
+// copy; with the step's own streams it is the step without its arithmetic.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kMaxIn = 16;
+constexpr int kMaxOut = 4;
+constexpr int kShapes = 4;  // shape 0: 512 x 2, 512 apart; 1: 512 x 2, 64 apart;
+                            // 2: 256 x 4, 64 apart; 3: 256 x 1
+
+struct Streams {
+  const void* in[kMaxIn];
+  void* out[kMaxOut];
+};
+
+template <int NIN, int NOUT, int BLOCK, int C, bool WC>
+__global__ void __launch_bounds__(BLOCK)
+    ceiling_kernel(Streams s, uint32_t in_wide, uint32_t out_wide, int64_t ngroups) {
+  constexpr int GS = WC ? 64 : BLOCK;
+  const int64_t g0 = WC ? (int64_t)blockIdx.x * (BLOCK * C) + (threadIdx.x / 64) * (64 * C) +
+                              (threadIdx.x % 64)
+                        : (int64_t)blockIdx.x * (BLOCK * C) + threadIdx.x;
+  u32x4 r[C][NIN];
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    const int64_t g = g0 + (int64_t)u * GS;
+    if (g >= ngroups) continue;
+#pragma unroll
+    for (int i = 0; i < NIN; ++i) {
+      if ((in_wide >> i) & 1u) {
+        r[u][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(s.in[i]) + g);
+      } else {
+        const u32x2 h = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(s.in[i]) + g);
+        r[u][i] = u32x4{h.x, h.y, 0u, 0u};
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    const int64_t g = g0 + (int64_t)u * GS;
+    if (g >= ngroups) continue;
+    u32x4 acc = r[u][0];
+#pragma unroll
+    for (int i = 1; i < NIN; ++i) acc ^= r[u][i];
+#pragma unroll
+    for (int o = 0; o < NOUT; ++o) {
+      if ((out_wide >> o) & 1u)
+        __builtin_nontemporal_store(acc, reinterpret_cast<u32x4*>(s.out[o]) + g);
+      else
+        __builtin_nontemporal_store(u32x2{acc.x, acc.y}, reinterpret_cast<u32x2*>(s.out[o]) + g);
+    }
+  }
+}
+
+template <int NIN, int NOUT, int BLOCK, int C, bool WC>
+hipError_t launch(const Streams& s, uint32_t in_wide, uint32_t out_wide, int64_t ngroups,
+                  hipStream_t st) {
+  const int64_t per_block = (int64_t)BLOCK * C;
+  const int64_t blocks = (ngroups + per_block - 1) / per_block;
+  hipLaunchKernelGGL((ceiling_kernel<NIN, NOUT, BLOCK, C, WC>), dim3((unsigned)blocks),
+                     dim3(BLOCK), 0, st, s, in_wide, out_wide, ngroups);
+  return hipGetLastError();
+}
+
+template <int NIN, int NOUT>
+hipError_t launch_shape(int shape, const Streams& s, uint32_t iw, uint32_t ow, int64_t ng,
+                        hipStream_t st) {
+  switch (shape) {
+    case 0: return launch<NIN, NOUT, 512, 2, false>(s, iw, ow, ng, st);
+    case 1: return launch<NIN, NOUT, 512, 2, true>(s, iw, ow, ng, st);
+    case 2: return launch<NIN, NOUT, 256, 4, true>(s, iw, ow, ng, st);
+    default: return launch<NIN, NOUT, 256, 1, false>(s, iw, ow, ng, st);
+  }
+}
+
+template <int NIN>
+hipError_t launch_out(int nout, int shape, const Streams& s, uint32_t iw, uint32_t ow,
+                      int64_t ng, hipStream_t st) {
+  switch (nout) {
+    case 1: return launch_shape<NIN, 1>(shape, s, iw, ow, ng, st);
+    case 2: return launch_shape<NIN, 2>(shape, s, iw, ow, ng, st);
+    case 3: return launch_shape<NIN, 3>(shape, s, iw, ow, ng, st);
+    default: return launch_shape<NIN, 4>(shape, s, iw, ow, ng, st);
+  }
+}
+
+template <int NIN>
+hipError_t launch_in(int nin, int nout, int shape, const Streams& s, uint32_t iw, uint32_t ow,
+                     int64_t ng, hipStream_t st) {
+  if constexpr (NIN > kMaxIn) {
+    return hipErrorInvalidValue;
+  } else {
+    if (nin == NIN) return launch_out<NIN>(nout, shape, s, iw, ow, ng, st);
+    return launch_in<NIN + 1>(nin, nout, shape, s, iw, ow, ng, st);
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+// Reads in[0..nin) and writes out[0..nout) over ngroups groups; in_width[i] and
+// out_width[o] are the bytes per group of each stream (8 or 16), so stream i
+// holds ngroups * in_width[i] bytes. Device pointers, aligned to their width;
+// 1 <= nin <= 16, 1 <= nout <= 4, ngroups >= 0; shape selects the launch
+// shape: 0 = 512 threads x 2 groups 512 apart, 1 = 512 x 2 groups 64 apart,
+// 2 = 256 x 4 groups 64 apart, 3 = 256 x 1. Launches on `stream` (a
+// hipStream_t, or NULL) and returns at once. Returns 0, -1 for an invalid
+// argument (nothing launched), or -3 for a HIP launch error.
+int zceil_streams(const void* const* in, const int32_t* in_width, int32_t nin, void* const* out,
+                  const int32_t* out_width, int32_t nout, int64_t ngroups, int32_t shape,
+                  void* stream) {
+  if (in == nullptr || in_width == nullptr || out == nullptr || out_width == nullptr) return -1;
+  if (nin < 1 || nin > kMaxIn || nout < 1 || nout > kMaxOut || ngroups < 0) return -1;
+  if (shape < 0 || shape >= kShapes) return -1;
+  if (ngroups == 0) return 0;
+  if (ngroups > (int64_t)0x7FFFFFFF * 256) return -1;
+  Streams s{};
+  uint32_t iw = 0, ow = 0;
+  for (int i = 0; i < nin; ++i) {
+    if (in[i] == nullptr || (in_width[i] != 8 && in_width[i] != 16)) return -1;
+    if (reinterpret_cast<uintptr_t>(in[i]) % in_width[i] != 0) return -1;
+    s.in[i] = in[i];
+    if (in_width[i] == 16) iw |= 1u << i;
+  }
+  for (int o = 0; o < nout; ++o) {
+    if (out[o] == nullptr || (out_width[o] != 8 && out_width[o] != 16)) return -1;
+    if (reinterpret_cast<uintptr_t>(out[o]) % out_width[o] != 0) return -1;
+    s.out[o] = out[o];
+    if (out_width[o] == 16) ow |= 1u << o;
+  }
+  const hipError_t e =
+      launch_in<1>(nin, nout, shape, s, iw, ow, ngroups, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? 0 : -3;
+}
+
+}  // extern "C"
