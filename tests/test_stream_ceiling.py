@@ -39,26 +39,27 @@ def test_exports_and_rejects_bad_arguments_before_any_launch():
     fake = [1 << 32, (1 << 32) + (1 << 24)]
     assert _call(lib, [], [], fake[:1], [16], 10) == -1                 # no inputs
     assert _call(lib, fake[:1], [16], [], [], 10) == -1                 # no outputs
-    assert _call(lib, fake[:1] * 17, [16] * 17, fake[1:], [16], 10) == -1  # 17 inputs
+    assert _call(lib, fake[:1] * 129, [16] * 129, fake[1:], [16], 10) == -1  # 129 inputs
     assert _call(lib, fake[:1], [12], fake[1:], [16], 10) == -1         # width not 8 or 16
     assert _call(lib, [fake[0] + 8], [16], fake[1:], [16], 10) == -1    # misaligned
     assert _call(lib, [0], [16], fake[1:], [16], 10) == -1              # NULL stream pointer
     assert _call(lib, fake[:1], [16], fake[1:], [16], -1) == -1         # negative size
-    assert _call(lib, fake[:1], [16], fake[1:], [16], 10, shape=4) == -1  # no such shape
+    assert _call(lib, fake[:1], [16], fake[1:], [16], 10, shape=5) == -1  # no such shape
     assert _call(lib, fake[:1], [16], fake[1:], [16], 0) == 0           # empty: nothing to do
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("shape", [0, 1, 2, 3])
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("nin", [5, 21, 40])
 @pytest.mark.parametrize("ngroups", [1, 1023, 1024 * 3 + 517])
-def test_xor_of_the_inputs_reaches_every_output(ngroups, shape):
+def test_xor_of_the_inputs_reaches_every_output(ngroups, nin, shape):
     torch = pytest.importorskip("torch")
     if not torch.cuda.is_available():
         pytest.skip("needs a GPU")
-    print(f"[case] zceil_streams ngroups={ngroups} shape={shape}", flush=True)
+    print(f"[case] zceil_streams ngroups={ngroups} nin={nin} shape={shape}", flush=True)
     lib = _lib()
     rng = np.random.default_rng(ngroups)
-    win, wout = [16, 8, 16, 8, 16], [16, 8, 16]
+    win, wout = ([16, 8, 16, 8, 16] * 8)[:nin], [16, 8, 16]
     tail = 64  # guard bytes after each output
     ins_h = [rng.integers(0, 256, ngroups * w, dtype=np.uint8) for w in win]
     ins = [torch.from_numpy(x).cuda() for x in ins_h]
