@@ -102,6 +102,12 @@ int main() {
   h.momentum = 0.9;
   zero_states sts = {nullptr, (void*)(A + (1u << 24)), nullptr};
   CHECK(zero_step(&h, (void*)A, grads, &sts, 1, nullptr) == ZERO_OK);
+  CHECK(zero_step_range(&h, (void*)A, grads, &sts, 2, 8, 800, nullptr) == ZERO_OK);
+  size_t wsg = 0;
+  CHECK(zero_step_clipped_workspace_bytes(&h, &wsg) == ZERO_OK);
+  // the SGD state has no v: a workspace at a low address overlaps nothing
+  CHECK(zero_step_clipped(&h, (void*)A, grads, &sts, 1, 1.0, nullptr, (void*)(uintptr_t)256, wsg,
+                          nullptr) == ZERO_OK);
   h.nesterov = 1;
   h.dampening = 0.5;
   CHECK(zero_step(&h, (void*)A, grads, &sts, 1, nullptr) == ZERO_EINVAL);

@@ -390,7 +390,7 @@ zero_status zero_step_range(const zero_hparams* hp, void* param, const void* con
     la.grads[k] = static_cast<const char*>(la.grads[k]) + begin * wd.grad;
   la.w = static_cast<char*>(la.w) + begin * wd.state;
   la.m = static_cast<char*>(la.m) + begin * wd.state;
-  la.v = static_cast<char*>(la.v) + begin * wd.state;
+  if (la.v) la.v = static_cast<char*>(la.v) + begin * wd.state;  // NULL for SGD
   if (la.out) la.out = static_cast<char*>(la.out) + begin * wd.param;
   la.mask_bit_offset += begin;
   la.len = end - begin;
@@ -525,7 +525,7 @@ zero_status zero_step_clipped(const zero_hparams* hp, void* param, const void* c
   const Range others[4] = {
       {(uintptr_t)param, (uintptr_t)param + (uintptr_t)(hp->n * wd.param), "param"},
       {(uintptr_t)st->m, (uintptr_t)st->m + (uintptr_t)(len * wd.state), "m"},
-      {(uintptr_t)st->v, (uintptr_t)st->v + (uintptr_t)(len * wd.state), "v"},
+      {(uintptr_t)st->v, st->v ? (uintptr_t)st->v + (uintptr_t)(len * wd.state) : 0, "v"},
       {(uintptr_t)st->master, st->master ? (uintptr_t)st->master + (uintptr_t)(len * wd.state) : 0,
        "master"}};
   for (const Range& o : others)
