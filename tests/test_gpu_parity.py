@@ -222,3 +222,26 @@ def test_full_size_rank0_share_of_8B(oracle):
 def test_full_size_gpt2s_n64(oracle):
     run_sampled(oracle, W["gpt2s-fp32-n64"], steps=100, count=1 << 18,
                 compare_steps=[1, 2, 50])
+
+
+# -- maximum sizes: byte offsets past 2^32 and element indexes past 2^31 ------
+def test_buffers_past_4_GiB_any_N(oracle):
+    """fp32 with N = 3 (the any-N kernel): every buffer holds 4.4 GB, so byte
+    offsets within one buffer pass 2^32."""
+    wl = synth.scaled(W["fp32-320M-n8"], 1_100_000_003, n_workers=3)
+    run_sampled(oracle, wl, steps=2, count=1 << 18)
+
+
+def test_more_than_2_31_elements_mixed(oracle):
+    """Mixed precision with N = 2 over 2.2e9 elements: element indexes pass
+    2^31 and the fp32 state buffers hold 8.8 GB."""
+    wl = synth.scaled(W["mixed-1B-n8"], 2_200_000_005, n_workers=2)
+    run_sampled(oracle, wl, steps=2, count=1 << 18)
+
+
+def test_last_rank_share_of_8B(oracle):
+    """Rank 7 of n = 8e9: its slot in the gathered bf16 buffer starts 14 GB in;
+    everything outside the slot stays unchanged."""
+    wl = synth.scaled(W["mixed-rank0-of-8B-n8"], 8_000_000_000, rank=7,
+                      name="mixed-rank7-of-8B-n8")
+    run_sampled(oracle, wl, steps=2, count=1 << 18)

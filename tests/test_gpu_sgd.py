@@ -131,3 +131,24 @@ def test_sgd_full_size_fp32_320M_n8(oracle):
     torch.cuda.synchronize()
     compare("param", host(param[idx_d]), p_h, "f32")
     compare("momentum buffer", host(st.m[idx_d]), b_h, "f32")
+
+
+@pytest.mark.parametrize("mode", [MODE_F32, MODE_MIXED])
+def test_sgd_buckets_equal_one_shot(mode):
+    """The SGD state has no v: the bucketed step (zero_step_range) must still
+    give the one-shot SGD step's result bit for bit."""
+    wl = synth.scaled(BASE[mode], 300_017)
+    say(f"[case] sgd buckets mode={mode} n={wl.n}")
+    hp, p_one, s_one = sgd_setup(wl, *VARIANTS["nesterov+decay"])
+    _, p_bkt, s_bkt = sgd_setup(wl, *VARIANTS["nesterov+decay"])
+    edges = list(range(0, wl.n, 65_536)) + [wl.n]
+    for t in (1, 2, 3):
+        grads = synth.make_grads(wl, t, "cuda")
+        z.zero_step(hp, p_one, grads, s_one, t)
+        for lo, hi in reversed(list(zip(edges[:-1], edges[1:]))):
+            z.zero_step_range(hp, p_bkt, grads, s_bkt, t, lo, hi)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(p_one), host(p_bkt))
+    assert np.array_equal(host(s_one.m), host(s_bkt.m))
+    if s_one.master is not None:
+        assert np.array_equal(host(s_one.master), host(s_bkt.master))
