@@ -138,23 +138,31 @@ def pmc_summary(workload, fetch_dir, write_dir, cmd):
     return out
 
 
-def kt_summary(workload, kt_dir, cmd):
+def kt_summary(workload, kt_dir, cmd, variant=None):
     """Per-kernel durations from rocprofv3 --kernel-trace --stats, as
-    profiles/kernel_trace_<workload>.md."""
+    profiles/kernel_trace_<workload>[_<variant>].md (variant: e.g. "clip" for a
+    --clip run)."""
     import csv
     import glob
     f = glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
     rows = list(csv.DictReader(open(f)))
-    path = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.md")
+    label = workload if not variant else f"{workload}_{variant}"
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{label}.md")
     os.makedirs(os.path.dirname(path), exist_ok=True)
     with open(path, "w") as fh:
-        fh.write(f"# rocprofv3 kernel statistics, workload {workload}\n\n")
+        fh.write(f"# rocprofv3 kernel statistics, workload {label}\n\n")
         fh.write(f"Command (run from the repository root on one MI355X):\n\n```\n{cmd}\n```\n\n")
+        fh.write("Template arguments of `zero_step_kernel`: mode, fixed worker count (0: any "
+                 "N), gradient-pointer capacity, threads per block, groups per thread, "
+                 "optimizer (0 Adam, 1 SGD), state loads issued with the gradient loads, "
+                 "groups 64 apart (wave-contiguous).\n\n")
         fh.write("| kernel | calls | average ns | min ns | max ns | % of GPU time |\n|---|---|---|---|---|---|\n")
         for r in rows:
-            name = r["Name"]
-            if STEP_KERNEL in name:
-                name = name.split("(")[0] + "<" + name.split("<", 1)[1].split(">(")[0] + ">"
+            name = r["Name"].replace("(anonymous namespace)::", "")
+            if name.startswith("void "):
+                name = name[5:]
+            cut = name.find(">(")
+            name = name[:cut + 1] if cut >= 0 else name.split("(")[0]
             name = name[:110]
             fh.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
                      f"{r['MaxNs']} | {float(r['Percentage']):.2f} |\n")
@@ -324,12 +332,14 @@ def main():
     ap.add_argument("--kt-summary", metavar="KT_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run into profiles/ and exit")
     ap.add_argument("--cmd", default="", help="the profiling command, recorded in the summary")
+    ap.add_argument("--variant", default=None,
+                    help="with --kt-summary: a suffix for the summary's name (e.g. clip)")
     args = ap.parse_args()
     if args.pmc_summary:
         print(json.dumps(pmc_summary(args.workload, *args.pmc_summary, args.cmd)))
         return
     if args.kt_summary:
-        print(kt_summary(args.workload, args.kt_summary, args.cmd))
+        print(kt_summary(args.workload, args.kt_summary, args.cmd, args.variant))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (all logical workers live in one GPU's HBM); "
