@@ -319,6 +319,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --bucket-mib: capture the buckets once into a HIP graph "
+                         "(zero_step_range_dev, step scalars in device memory) and replay it "
+                         "each step")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip the copy and streaming-ceiling measurements")
     ap.add_argument("--clip", type=float, default=None, metavar="FRACTION",
@@ -398,8 +402,32 @@ def main():
         edges = list(range(0, L, size)) + [L]
         buckets = list(reversed(list(zip(edges[:-1], edges[1:]))))
 
+    graph = None
+    if args.graph:
+        if buckets is None or args.clip is not None:
+            print("--graph needs --bucket-mib (and no --clip)", file=sys.stderr)
+            sys.exit(2)
+        import numpy as np
+        # every step's scalars, prepared up front (they depend only on t)
+        total = args.warmup + args.steps
+        scal_all = torch.from_numpy(np.concatenate(
+            [z.zero_step_scalars(hp, t) for t in range(1, total + 1)])).cuda()
+        scal = torch.empty(z.STEP_SCALARS_BYTES, dtype=torch.uint8, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for lo, hi in buckets:
+                    z.zero_step_range_dev(hp, param, grads, st, scal, lo, hi)
+        torch.cuda.synchronize()
+
     def one_step(t, stream=None):
-        if buckets is not None:
+        if graph is not None:
+            k = z.STEP_SCALARS_BYTES
+            scal.copy_(scal_all[(t - 1) * k:t * k])
+            graph.replay()
+        elif buckets is not None:
             for lo, hi in buckets:
                 z.zero_step_range(hp, param, grads, st, t, lo, hi, stream=stream)
         elif max_norm is None:
@@ -460,7 +488,8 @@ def main():
                    **({} if max_norm is None else
                       {"clipped": True, "clip_fraction": args.clip, "max_norm": max_norm}),
                    **({} if buckets is None else
-                      {"bucket_mib": args.bucket_mib, "buckets": len(buckets)})},
+                      {"bucket_mib": args.bucket_mib, "buckets": len(buckets)}),
+                   **({"graph": True} if graph is not None else {})},
         "achieved_GBps": achieved,
         "kernel_ms_mean": avg_ms,
         "kernel_ms_median": sorted(kern_ms)[len(kern_ms) // 2],

@@ -190,6 +190,38 @@ zero_status zero_step_range(const zero_hparams* hp, void* param, const void* con
                             const zero_states* states, int64_t t, int64_t begin, int64_t end,
                             void* stream);
 
+/* ---- Step scalars in device memory, for captured launches -----------------
+ * zero_step and zero_step_range bake the step-dependent scalars (1 - b1^t,
+ * 1 - b2^t, and for SGD whether t == 1) into the launch. A launch captured
+ * into a HIP graph would then replay step t forever. zero_step_range_dev
+ * takes them from a small device buffer instead, so one captured launch (or
+ * a captured sequence of buckets) serves every step: before each replay the
+ * caller writes the next step's scalars into that buffer. */
+
+/* The step-dependent scalars of step t; 24 bytes, 8-byte aligned. */
+typedef struct {
+  double bias1; /* 1 - beta1^t, formed in double */
+  double bias2; /* 1 - beta2^t, formed in double */
+  int64_t t;    /* the 1-based step number */
+} zero_step_scalars;
+
+/* Host-only; touches no device. Fills *out for step t exactly as zero_step
+ * forms these values. Errors as zero_step for the hyperparameters and t. */
+zero_status zero_step_scalars_fill(const zero_hparams* hp, int64_t t, zero_step_scalars* out);
+
+/* zero_step_range with the step's scalars read by the kernel from
+ * dev_scalars: a device pointer (8-byte aligned, not overlapping any buffer
+ * the step writes) holding the zero_step_scalars that zero_step_scalars_fill
+ * produced for the step being run. The host validates everything else as for
+ * zero_step_range (with t = 1); the device values are used as given, so the
+ * buffer must hold a filled value whenever the launch runs. The result is bit
+ * for bit that of zero_step_range with the same t. For graph capture
+ * (hipStreamBeginCapture, or torch.cuda.graph): the launch enqueues one kernel
+ * and makes no allocation, copy, set or synchronisation. */
+zero_status zero_step_range_dev(const zero_hparams* hp, void* param, const void* const* grads,
+                                const zero_states* states, const zero_step_scalars* dev_scalars,
+                                int64_t begin, int64_t end, void* stream);
+
 /* ---- The materialised reduce-scatter mean and global-norm clipping ----------
  * "Data parallelism and ZeRO stages 1 to 3", section "2. Principles": stage 1
  * keeps the averaged gradient in .grad ("Your emulation's bookkeeping"), and

@@ -335,3 +335,38 @@ def test_sgd_ignores_adam_fields_and_allows_null_v():
     hp = _hp(optimizer=1, momentum=0.9, beta1=5.0, beta2=-1.0, eps=0.0)
     rc, msg = _call_step(hp, v=None, t=0)
     assert rc == z.ZERO_EINVAL and "t must be" in msg
+
+
+def test_step_scalars_fill_matches_the_step_formula():
+    """zero_step_scalars_fill forms 1 - beta^t in double exactly as the step
+    does (C pow, as Python's float ** is), and rejects what zero_step rejects."""
+    hp = _hp()
+    for t in (1, 2, 3, 10, 1000, 10 ** 6):
+        b = z.zero_step_scalars(z.HParams(n=1000, n_workers=4, mode=1, lr=1e-3, beta1=0.9,
+                                          beta2=0.999, eps=1e-8), t)
+        bias1, bias2 = b[:16].view(np.float64)
+        assert bias1 == 1.0 - 0.9 ** t and bias2 == 1.0 - 0.999 ** t
+        assert int(b[16:].view(np.int64)[0]) == t
+    lib = _abi.load()
+    out = _abi.zero_step_scalars()
+    assert lib.zero_step_scalars_fill(C.byref(hp), 0, C.byref(out)) == z.ZERO_EINVAL
+    assert lib.zero_step_scalars_fill(C.byref(hp), 1, None) == z.ZERO_EINVAL
+    assert lib.zero_step_scalars_fill(C.byref(_hp(beta1=1.0)), 1, C.byref(out)) == z.ZERO_EINVAL
+    assert lib.zero_step_scalars_fill(None, 1, C.byref(out)) == z.ZERO_EINVAL
+    assert C.sizeof(_abi.zero_step_scalars) == 24 == z.STEP_SCALARS_BYTES
+
+
+def test_step_range_dev_rejects_before_any_launch():
+    lib = _abi.load()
+    st = _abi.zero_states(master=None, m=A + (1 << 24), v=A + (2 << 24))
+    arr = (C.c_void_p * 4)(*[A + ((3 + k) << 24) for k in range(4)])
+    hp = _hp()
+    ok_scal = A + (40 << 24)
+    for scal, begin, end in ((None, 0, 8), (ok_scal + 4, 0, 8),  # NULL, misaligned scalars
+                             (A + (1 << 24) + 8, 0, 8),           # scalars inside m
+                             (ok_scal, -8, 10), (ok_scal, 4, 100)):  # bad ranges
+        rc = lib.zero_step_range_dev(C.byref(hp), A, arr, C.byref(st), scal, begin, end, None)
+        assert rc == z.ZERO_EINVAL, (scal, begin, end)
+    # an empty range is valid and launches nothing
+    assert lib.zero_step_range_dev(C.byref(hp), A, arr, C.byref(st), ok_scal, 8, 8,
+                                   None) == z.ZERO_OK

@@ -23,6 +23,11 @@ workers sharing one GPU:
                                             optionally clipped by the global norm
   zero_step_clipped(hp, param, grads, states, t, max_norm, sumsq, workspace)
                                          -> both, as one clipped step
+  zero_step_scalars(hp, t)               -> the step-dependent scalars of step t
+  zero_step_range_dev(hp, param, grads, states, scalars, begin, end)
+                                         -> zero_step_range with those scalars
+                                            read from device memory (for launches
+                                            captured into a graph and replayed)
   zero_memory_bytes(...)                 -> per-rank memory by ZeRO stage
   zero_shard_bounds(n, N, r)             -> np.array_split shard [a, b)
 """
@@ -42,7 +47,8 @@ __all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
            "zero_mean_grad_workspace_bytes", "zero_mean_grad", "zero_step_mean",
            "zero_step_clipped_workspace_bytes", "zero_step_clipped", "zero_step_range",
            "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MAX_WORKERS",
-           "ZERO_OPT_ADAM", "ZERO_OPT_SGD"]
+           "ZERO_OPT_ADAM", "ZERO_OPT_SGD", "zero_step_scalars", "zero_step_range_dev",
+           "STEP_SCALARS_BYTES"]
 
 
 class ZeroError(RuntimeError):
@@ -216,6 +222,45 @@ def zero_step_range(hp: HParams, param, grads: Sequence, states: States, t: int,
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
     st = lib.zero_step_range(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t), int(begin),
                              int(end), _stream_handle(stream, states.m))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+STEP_SCALARS_BYTES = C.sizeof(_abi.zero_step_scalars)
+
+
+def zero_step_scalars(hp: HParams, t: int) -> np.ndarray:
+    """The step-dependent scalars of step t (host-side, no device work), as the
+    STEP_SCALARS_BYTES bytes of a zero_step_scalars: copy them into the device
+    buffer that zero_step_range_dev reads before the launch (or the replay)."""
+    lib = _abi.load()
+    out = _abi.zero_step_scalars()
+    c_hp = hp.to_c()
+    st = lib.zero_step_scalars_fill(C.byref(c_hp), int(t), C.byref(out))
+    if st != ZERO_OK:
+        _raise(st)
+    return np.frombuffer(bytes(out), dtype=np.uint8).copy()
+
+
+def zero_step_range_dev(hp: HParams, param, grads: Sequence, states: States, scalars,
+                        begin: int, end: int, stream=None) -> None:
+    """Enqueue zero_step_range with the step scalars read on the device from
+    `scalars` (a device tensor of >= STEP_SCALARS_BYTES bytes holding
+    zero_step_scalars(hp, t) when the launch runs). Safe to capture into a
+    graph: one kernel, no allocation, copy or synchronisation."""
+    chk = _check_common(hp, param, states)
+    if chk is not None:
+        g_dt, glen = chk
+        if len(grads) != hp.n_workers:
+            raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
+        for k, g in enumerate(grads):
+            _check_tensor(g, g_dt, glen, f"grads[{k}]")
+    _check_bytes(scalars, STEP_SCALARS_BYTES, "scalars")
+    lib = _abi.load()
+    c_hp, c_st = hp.to_c(), states.to_c()
+    arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
+    st = lib.zero_step_range_dev(C.byref(c_hp), _addr(param), arr, C.byref(c_st), _addr(scalars),
+                                 int(begin), int(end), _stream_handle(stream, states.m))
     if st != ZERO_OK:
         _raise(st)
 

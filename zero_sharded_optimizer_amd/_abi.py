@@ -51,6 +51,10 @@ class zero_states(C.Structure):
     _fields_ = [("master", C.c_void_p), ("m", C.c_void_p), ("v", C.c_void_p)]
 
 
+class zero_step_scalars(C.Structure):
+    _fields_ = [("bias1", C.c_double), ("bias2", C.c_double), ("t", C.c_int64)]
+
+
 class zero_mem(C.Structure):
     _fields_ = [("params", C.c_int64), ("grads", C.c_int64), ("optimizer", C.c_int64),
                 ("total", C.c_int64)]
@@ -59,7 +63,7 @@ class zero_mem(C.Structure):
 EXPORTED = ("zero_init_states", "zero_step", "zero_memory_bytes", "zero_shard_bounds",
             "zero_last_error", "zero_mean_grad_workspace_bytes", "zero_mean_grad",
             "zero_step_mean", "zero_step_clipped_workspace_bytes", "zero_step_clipped",
-            "zero_step_range")
+            "zero_step_range", "zero_step_scalars_fill", "zero_step_range_dev")
 
 _lib = None
 
@@ -108,6 +112,13 @@ def load(path=None):
                                       C.POINTER(zero_states), C.c_int64, C.c_double, C.c_void_p,
                                       C.c_void_p, C.c_size_t, C.c_void_p]
     lib.zero_step_clipped.restype = C.c_int
+    lib.zero_step_scalars_fill.argtypes = [C.POINTER(zero_hparams), C.c_int64,
+                                           C.POINTER(zero_step_scalars)]
+    lib.zero_step_scalars_fill.restype = C.c_int
+    lib.zero_step_range_dev.argtypes = [C.POINTER(zero_hparams), C.c_void_p,
+                                        C.POINTER(C.c_void_p), C.POINTER(zero_states), C.c_void_p,
+                                        C.c_int64, C.c_int64, C.c_void_p]
+    lib.zero_step_range_dev.restype = C.c_int
     lib.zero_last_error.argtypes = []
     lib.zero_last_error.restype = C.c_char_p
     if path is None:

@@ -5,12 +5,18 @@
 
 #include <cmath>
 #include <cstdarg>
+#include <cstddef>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
 #include <string>
 
 #include "zero_launch.h"
+
+static_assert(sizeof(zero_step_scalars) == sizeof(zlaunch::DynScalars) &&
+                  offsetof(zero_step_scalars, bias2) == offsetof(zlaunch::DynScalars, bias2) &&
+                  offsetof(zero_step_scalars, t) == offsetof(zlaunch::DynScalars, t),
+              "zero_step_scalars and zlaunch::DynScalars must share one layout");
 
 namespace {
 
@@ -40,6 +46,9 @@ void shard_range(int64_t n, int64_t N, int64_t r, int64_t* a, int64_t* b) {
   *a = r * q + (r < rho ? r : rho);
   *b = *a + q + (r < rho ? 1 : 0);
 }
+
+// 1 - beta^t in double: the bias correction of step t.
+double bias_correction(double beta, int64_t t) { return 1.0 - std::pow(beta, (double)t); }
 
 struct Widths {
   int64_t param, grad, state, optimizer;
@@ -299,13 +308,12 @@ zero_status build_step(const zero_hparams* hp, void* param, const void* const* g
   la->mask = decays ? hp->wd_mask : nullptr;
   la->mask_bit_offset = a;
   // Step scalars: formed in double, rounded to the state type by the launch.
-  const double tt = (double)t;
   la->beta1 = hp->beta1;
   la->beta2 = hp->beta2;
   la->one_minus_beta1 = 1.0 - hp->beta1;
   la->one_minus_beta2 = 1.0 - hp->beta2;
-  la->bias1 = 1.0 - std::pow(hp->beta1, tt);
-  la->bias2 = 1.0 - std::pow(hp->beta2, tt);
+  la->bias1 = bias_correction(hp->beta1, t);
+  la->bias2 = bias_correction(hp->beta2, t);
   la->lr = hp->lr;
   la->eps = hp->eps;
   la->decay_factor = 1.0 - hp->lr * hp->weight_decay;
@@ -325,6 +333,40 @@ zero_status build_step(const zero_hparams* hp, void* param, const void* const* g
 }
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// Validation and launch arguments shared by zero_step_range and
+// zero_step_range_dev: the range [begin, end) of the call's index space as
+// offset views of the full-length buffers.
+zero_status build_range(const zero_hparams* hp, void* param, const void* const* grads,
+                        const zero_states* st, int64_t t, int64_t begin, int64_t end,
+                        zlaunch::StepArgs* la, bool* nothing) {
+  bool empty = false;
+  int64_t a, b;
+  if (hp == nullptr) return fail(ZERO_EINVAL, "hparams is NULL");
+  Widths wd;
+  if (!mode_widths(hp->mode, &wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
+  const int N = hp->n_workers >= 1 && hp->n_workers <= ZERO_MAX_WORKERS ? hp->n_workers : 0;
+  zero_status s = build_step(hp, param, grads, N, wd.grad, st, t, la, &empty, &a, &b);
+  if (s != ZERO_OK) return s;
+  const int64_t len = b - a;
+  if (begin < 0 || end < begin || end > len)
+    return fail(ZERO_EINVAL, "need 0 <= begin <= end <= %lld, got [%lld, %lld)", (long long)len,
+                (long long)begin, (long long)end);
+  if (begin % 8 != 0)
+    return fail(ZERO_EINVAL, "begin must be a multiple of 8, got %lld", (long long)begin);
+  *nothing = empty || begin == end;
+  if (*nothing) return ZERO_OK;
+  // Elementwise: the sub-range is the same step on offset views.
+  for (int k = 0; k < la->n_workers; ++k)
+    la->grads[k] = static_cast<const char*>(la->grads[k]) + begin * wd.grad;
+  la->w = static_cast<char*>(la->w) + begin * wd.state;
+  la->m = static_cast<char*>(la->m) + begin * wd.state;
+  if (la->v) la->v = static_cast<char*>(la->v) + begin * wd.state;  // NULL for SGD
+  if (la->out) la->out = static_cast<char*>(la->out) + begin * wd.param;
+  la->mask_bit_offset += begin;
+  la->len = end - begin;
+  return ZERO_OK;
+}
 
 // Workspace of zero_step_clipped: the mean gradient, the block partials, the
 // squared norm.
@@ -370,30 +412,53 @@ zero_status zero_step_range(const zero_hparams* hp, void* param, const void* con
                             const zero_states* st, int64_t t, int64_t begin, int64_t end,
                             void* stream) {
   zlaunch::StepArgs la;
-  bool empty = false;
-  int64_t a, b;
-  if (hp == nullptr) return fail(ZERO_EINVAL, "hparams is NULL");
+  bool nothing = false;
+  zero_status s = build_range(hp, param, grads, st, t, begin, end, &la, &nothing);
+  if (s != ZERO_OK || nothing) return s == ZERO_OK ? ok() : s;
+  const char* err = zlaunch::launch_step(la, stream);
+  if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
+  return ok();
+}
+
+zero_status zero_step_scalars_fill(const zero_hparams* hp, int64_t t, zero_step_scalars* out) {
   Widths wd;
-  if (!mode_widths(hp->mode, &wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
-  const int N = hp->n_workers >= 1 && hp->n_workers <= ZERO_MAX_WORKERS ? hp->n_workers : 0;
-  zero_status s = build_step(hp, param, grads, N, wd.grad, st, t, &la, &empty, &a, &b);
+  int64_t a = 0, b = 0;
+  if (out == nullptr) return fail(ZERO_EINVAL, "out is NULL");
+  zero_status s = check_hparams(hp, true, &wd, &a, &b);
   if (s != ZERO_OK) return s;
-  const int64_t len = b - a;
-  if (begin < 0 || end < begin || end > len)
-    return fail(ZERO_EINVAL, "need 0 <= begin <= end <= %lld, got [%lld, %lld)", (long long)len,
-                (long long)begin, (long long)end);
-  if (begin % 8 != 0)
-    return fail(ZERO_EINVAL, "begin must be a multiple of 8, got %lld", (long long)begin);
-  if (empty || begin == end) return ok();
-  // Elementwise: the sub-range is the same step on offset views.
-  for (int k = 0; k < la.n_workers; ++k)
-    la.grads[k] = static_cast<const char*>(la.grads[k]) + begin * wd.grad;
-  la.w = static_cast<char*>(la.w) + begin * wd.state;
-  la.m = static_cast<char*>(la.m) + begin * wd.state;
-  if (la.v) la.v = static_cast<char*>(la.v) + begin * wd.state;  // NULL for SGD
-  if (la.out) la.out = static_cast<char*>(la.out) + begin * wd.param;
-  la.mask_bit_offset += begin;
-  la.len = end - begin;
+  if (t < 1) return fail(ZERO_EINVAL, "t must be >= 1 (1-based step number), got %lld", (long long)t);
+  const double b1 = bias_correction(hp->beta1, t), b2 = bias_correction(hp->beta2, t);
+  if (hp->optimizer == ZERO_OPT_ADAM && (!(b1 > 0.0) || !(b2 > 0.0)))
+    return fail(ZERO_EINVAL, "bias correction 1 - beta^t is not positive (check beta and t)");
+  out->bias1 = b1;
+  out->bias2 = b2;
+  out->t = t;
+  return ok();
+}
+
+zero_status zero_step_range_dev(const zero_hparams* hp, void* param, const void* const* grads,
+                                const zero_states* st, const zero_step_scalars* dev_scalars,
+                                int64_t begin, int64_t end, void* stream) {
+  zlaunch::StepArgs la;
+  bool nothing = false;
+  if (dev_scalars == nullptr || !aligned(dev_scalars, 8))
+    return fail(ZERO_EINVAL, "dev_scalars must be non-NULL and 8-byte aligned");
+  // validated as step 1; the kernel takes the step-dependent values from dev_scalars
+  zero_status s = build_range(hp, param, grads, st, 1, begin, end, &la, &nothing);
+  if (s != ZERO_OK || nothing) return s == ZERO_OK ? ok() : s;
+  const Range rd{(uintptr_t)dev_scalars, (uintptr_t)dev_scalars + sizeof(zero_step_scalars),
+                 "dev_scalars"};
+  Widths wd;
+  mode_widths(hp->mode, &wd);
+  const Range written[4] = {
+      {(uintptr_t)la.w, (uintptr_t)la.w + (uintptr_t)(la.len * wd.state), "w"},
+      {(uintptr_t)la.m, (uintptr_t)la.m + (uintptr_t)(la.len * wd.state), "m"},
+      {(uintptr_t)la.v, la.v ? (uintptr_t)la.v + (uintptr_t)(la.len * wd.state) : 0, "v"},
+      {(uintptr_t)la.out, la.out ? (uintptr_t)la.out + (uintptr_t)(la.len * wd.param) : 0,
+       "param"}};
+  for (const Range& r : written)
+    if (overlaps(rd, r)) return fail(ZERO_EINVAL, "dev_scalars overlaps %s", r.name);
+  la.dyn = dev_scalars;
   const char* err = zlaunch::launch_step(la, stream);
   if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
   return ok();

@@ -536,9 +536,14 @@ __global__ void __launch_bounds__(BLOCK)
                      typename M::P* __restrict__ out, int out_vec, int64_t len,
                      Consts<typename M::S> c, const uint32_t* __restrict__ mask,
                      int64_t mask_off, int decay_kind, const double* __restrict__ clip_sumsq,
-                     double max_norm) {
+                     double max_norm, const zlaunch::DynScalars* __restrict__ dyn) {
   typedef typename M::S S;
   constexpr int VEC = M::VEC;
+  if (dyn != nullptr) {  // step-dependent scalars from device memory, rounded as on the host
+    c.bias1 = (S)dyn->bias1;
+    c.bias2 = (S)dyn->bias2;
+    c.first = dyn->t == 1;
+  }
   const int64_t ngroups = len / VEC;
   constexpr int GS = WC ? 64 : BLOCK;
   const int64_t g0 = WC ? (int64_t)blockIdx.x * (BLOCK * C) + (threadIdx.x / 64) * (64 * C) +
@@ -803,13 +808,15 @@ void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
                        dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
                        static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
                        out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
-                       a.decay_kind, a.clip_sumsq, a.max_norm);
+                       a.decay_kind, a.clip_sumsq, a.max_norm,
+                       static_cast<const zlaunch::DynScalars*>(a.dyn));
   else
     hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, PRE, WC>), dim3((unsigned)blocks),
                        dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
                        static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
                        out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
-                       a.decay_kind, a.clip_sumsq, a.max_norm);
+                       a.decay_kind, a.clip_sumsq, a.max_norm,
+                       static_cast<const zlaunch::DynScalars*>(a.dyn));
 }
 
 template <class M>

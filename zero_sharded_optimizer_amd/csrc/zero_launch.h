@@ -35,6 +35,16 @@ struct StepArgs {
   int optimizer;
   double momentum, one_minus_dampening, weight_decay;
   int nesterov, first;
+  // Device copy of the step-dependent scalars (DynScalars), or nullptr. When
+  // set, the kernel takes bias1, bias2 and first from it instead of the
+  // values above, so a captured launch can be replayed for later steps.
+  const void* dyn;
+};
+
+// Layout of the device step scalars (zero_step_scalars in zero_adam.h).
+struct DynScalars {
+  double bias1, bias2;  // 1 - beta1^t, 1 - beta2^t, formed in double
+  int64_t t;            // the 1-based step number
 };
 
 // The materialised reduce-scatter mean of one call's range.
