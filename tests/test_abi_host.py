@@ -370,3 +370,17 @@ def test_step_range_dev_rejects_before_any_launch():
     # an empty range is valid and launches nothing
     assert lib.zero_step_range_dev(C.byref(hp), A, arr, C.byref(st), ok_scal, 8, 8,
                                    None) == z.ZERO_OK
+
+
+def test_input_recipe_shard_matches_numpy_array_split():
+    """The input generator's rank chunks are numpy's array_split sections."""
+    from dataclasses import replace
+    from zero_sharded_optimizer_amd import synth
+    base = synth.WORKLOADS["mixed-rank0-of-8B-n8"]
+    for n in (1, 5, 17, 100, 1001):
+        for N in (1, 3, 8, 64):
+            sizes = [s.size for s in np.array_split(np.arange(n), N)]
+            starts = np.cumsum([0] + sizes[:-1])
+            for r in range(N):
+                a, b = replace(base, n=n, n_workers=N, rank=r).shard
+                assert (a, b) == (starts[r], starts[r] + sizes[r])

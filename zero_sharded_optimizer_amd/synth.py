@@ -41,7 +41,9 @@ class Workload:
 
     @property
     def shard(self):
-        """[a, b) of the elements this call updates."""
+        """[a, b) of the elements this call updates: the bounds of
+        np.array_split(np.arange(n), N)[rank], which the input recipe needs to
+        draw a rank's gradient chunks (tests check it against numpy itself)."""
         if self.rank < 0:
             return 0, self.n
         q, rho = divmod(self.n, self.n_workers)
