@@ -448,8 +448,8 @@ zero_status zero_step_range_dev(const zero_hparams* hp, void* param, const void*
   if (s != ZERO_OK || nothing) return s == ZERO_OK ? ok() : s;
   const Range rd{(uintptr_t)dev_scalars, (uintptr_t)dev_scalars + sizeof(zero_step_scalars),
                  "dev_scalars"};
-  Widths wd;
-  mode_widths(hp->mode, &wd);
+  Widths wd{};
+  if (!mode_widths(hp->mode, &wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
   const Range written[4] = {
       {(uintptr_t)la.w, (uintptr_t)la.w + (uintptr_t)(la.len * wd.state), "w"},
       {(uintptr_t)la.m, (uintptr_t)la.m + (uintptr_t)(la.len * wd.state), "m"},
