@@ -91,6 +91,12 @@ int main() {
   CHECK(zero_step(&h, (void*)A, grads, &stm, 2, nullptr) == ZERO_OK);
   CHECK(zero_step_range(&h, (void*)A, grads, &stm, 2, 8, 800, nullptr) == ZERO_OK);
   CHECK(zero_step_range(&h, (void*)A, grads, &stm, 2, 4, 800, nullptr) == ZERO_EINVAL);
+  // step scalars in device memory
+  zero_step_scalars sc;
+  CHECK(zero_step_scalars_fill(&h, 3, &sc) == ZERO_OK && sc.t == 3);
+  const zero_step_scalars* dsc = (const zero_step_scalars*)(A + ((uintptr_t)400 << 24));
+  CHECK(zero_step_range_dev(&h, (void*)A, grads, &stm, dsc, 8, 800, nullptr) == ZERO_OK);
+  CHECK(zero_step_range_dev(&h, (void*)A, grads, &stm, nullptr, 8, 800, nullptr) == ZERO_EINVAL);
   // empty shard: nothing launched, pointers may be NULL
   const int before = g_launches;
   h = hp(3, 5, 4, ZERO_MODE_F64);
