@@ -3,9 +3,11 @@
 Each case draws a mode, an optimizer (Adam/AdamW, or momentum SGD with or
 without dampening and Nesterov), n from 1 to ~3e5, N up to 256 (N > n included),
 full or rank mode, no decay / decay everywhere / a random per-element mask, a
-call path (one zero_step; buckets of zero_step_range in a random order; or
-buckets of zero_step_range_dev with the step scalars in device memory) and 1-3
-steps, and compares every element with the oracle at the parity bar of
+call path (one zero_step; buckets of zero_step_range in a random order;
+buckets of zero_step_range_dev with the step scalars in device memory; the
+materialised mean then zero_step_mean; or zero_step_clipped with a threshold
+never reached, whose factor is exactly 1) and 1-3 steps, and compares every
+element with the oracle's unclipped step at the parity bar of
 oracle/compare.py. Inputs are drawn on the host with numpy and uploaded."""
 import numpy as np
 import pytest
@@ -51,7 +53,9 @@ def _draw(seed):
     c["rank"] = -1 if rng.random() < 0.6 else int(rng.integers(0, c["N"]))
     c["decay"] = str(rng.choice(["none", "all", "mask"]))
     c["wd"] = 0.0 if c["decay"] == "none" else float(rng.choice([0.01, 0.1]))
-    c["path"] = str(rng.choice(["step", "range", "range_dev"]))
+    c["path"] = str(rng.choice(["step", "range", "range_dev", "split", "clip1"]))
+    if c["path"] == "clip1" and c["rank"] >= 0:
+        c["path"] = "split"  # a clipped step needs every shard: full mode only
     c["steps"] = int(rng.integers(1, 4))
     mom = float(rng.choice([0.0, 0.9]))
     damp = float(rng.choice([0.0, 0.1])) if mom else 0.0
@@ -111,6 +115,14 @@ def test_random_configuration_matches_the_oracle(oracle, seed):
         grads = [_device(g, mode) for g in g_h]
         if c["path"] == "step":
             z.zero_step(hp, param, grads, st, t)
+        elif c["path"] == "split":  # materialised mean, then the step from it
+            mean = torch.empty(L, dtype=sdt, device="cuda")
+            z.zero_mean_grad(hp, grads, mean)
+            z.zero_step_mean(hp, param, mean, st, t)
+        elif c["path"] == "clip1":  # clipped, threshold never reached: factor exactly 1
+            ws = torch.empty(z.zero_step_clipped_workspace_bytes(hp), dtype=torch.uint8,
+                             device="cuda")
+            z.zero_step_clipped(hp, param, grads, st, t, 1e30, ws)
         else:
             if c["path"] == "range_dev":
                 scal.copy_(torch.from_numpy(z.zero_step_scalars(hp, t)))
