@@ -209,6 +209,73 @@ def cpu_baseline(wl, target_s=12.0, sample_n=1 << 22):
                       f"steps, single-threaded C++ oracle, {el:.1f} s"}
 
 
+def cpu_threads():
+    """Host threads to use: the CPUs this process may run on, at most 16 (one
+    GPU's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n, int(os.environ.get("OMP_NUM_THREADS", n))))
+
+
+def cpu_baseline_threads(wl, target_s=8.0, sample_n=1 << 22):
+    """The same oracle, unchanged, on the same sample split into one slice per
+    host thread (the step is elementwise, so the slices are independent; the
+    oracle's C code runs without Python's lock). Elements stepped per second
+    over all threads."""
+    import threading
+    import numpy as np
+    import torch
+    from oracle import Oracle
+    from zero_sharded_optimizer_amd import synth
+    O = Oracle()
+    small = synth.scaled(wl, min(sample_n, wl.length), rank=-1, shapes=(),
+                         decay="all" if wl.decay == "all" else "none")
+    n = small.n
+
+    def host(x):
+        if x.dtype == torch.bfloat16:
+            return x.view(torch.int16).cpu().numpy().view(np.uint16).copy()
+        return x.cpu().numpy().copy()
+
+    param = host(synth.make_params(small, "cuda")[0])
+    grads = [host(g) for g in synth.make_grads(small, 1, "cuda")]
+    dec = synth.decay_flags(wl)[:n].astype(np.uint8) if wl.decay == "2d" else None
+    T = min(cpu_threads(), n)
+    edges = [n * i // T for i in range(T + 1)]
+    done = [0] * T
+    start = threading.Barrier(T + 1)
+
+    def work(i):
+        lo, hi = edges[i], edges[i + 1]
+        p = param[lo:hi].copy()
+        g = [x[lo:hi].copy() for x in grads]
+        d = None if dec is None else dec[lo:hi].copy()
+        mst, m, v = O.init_states(small.mode, p)
+        start.wait()
+        t0 = time.perf_counter()
+        steps = 0
+        while time.perf_counter() - t0 < target_s:
+            p, mst, m, v = O.zero_step(small.mode, p, g, mst, m, v, steps + 1, small.lr,
+                                       small.beta1, small.beta2, small.eps,
+                                       small.weight_decay, d)
+            steps += 1
+        done[i] = steps * (hi - lo)
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(T)]
+    for th in threads:
+        th.start()
+    start.wait()
+    t0 = time.perf_counter()
+    for th in threads:
+        th.join()
+    el = time.perf_counter() - t0
+    return {"value": sum(done) / el, "unit": "params/s", "cores": T, "kind": "oracle",
+            "sample": f"first {n} elements of the workload in {T} slices, one per host "
+                      f"thread, {wl.n_workers} workers, unchanged C++ oracle, {el:.1f} s"}
+
+
 def copy_ceiling(nbytes=4 << 30, reps=10):
     """A plain device copy of nbytes: read + write bytes over the time, GB/s."""
     import torch
@@ -467,6 +534,7 @@ def main():
     if ceil is not None and ceil["step_streams_GBps"]:
         ceil["step_frac_of_step_streams"] = achieved / ceil["step_streams_GBps"]
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
+    cpu_mt = None if args.no_cpu_baseline else cpu_baseline_threads(wl)
 
     out = {
         "metric": METRIC,
@@ -499,6 +567,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
         "cpu_baseline": cpu,
+        "cpu_baseline_threads": cpu_mt,
     }
     print(json.dumps(out), flush=True)
 
