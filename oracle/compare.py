@@ -4,7 +4,7 @@
   fp32 (master / parameter, m, v): |got - ref| <= 1e-6 * max(1, |ref|); the
                                    number of bit-identical elements and the
                                    largest distance in ulps are reported too.
-  bf16 (gathered parameters):    at most 1 bf16 ulp from the oracle's rounded
+  bf16 / fp16 (gathered parameters): at most 1 ulp from the oracle's rounded
                                    value (distance between the ordered bit
                                    patterns).
 NaN on both sides counts as equal.
@@ -41,21 +41,22 @@ def ulp_distance(got, ref):
 
 
 def compare(name, got, ref, kind):
-    """kind: 'exact', 'f32', or 'bf16'. Returns a stats dict; raises
+    """kind: 'exact', 'f32', 'bf16' or 'fp16'. Returns a stats dict; raises
     AssertionError when the bar is not met."""
     got = np.ascontiguousarray(got)
     ref = np.ascontiguousarray(ref)
     assert got.shape == ref.shape, (name, got.shape, ref.shape)
     n = got.size
-    if kind == "bf16":
+    if kind in ("bf16", "fp16"):
         assert got.dtype == np.uint16 and ref.dtype == np.uint16
-        nan_g = (got & 0x7FFF) > 0x7F80
-        nan_r = (ref & 0x7FFF) > 0x7F80
+        inf_bits = 0x7F80 if kind == "bf16" else 0x7C00
+        nan_g = (got & 0x7FFF) > inf_bits
+        nan_r = (ref & 0x7FFF) > inf_bits
         d = ulp_distance(got, ref)
         d = np.where(nan_g & nan_r, 0, d)
         bad = np.flatnonzero((d > 1) | (nan_g != nan_r))
         stats = dict(name=name, n=n, bitexact=int(np.sum(d == 0)), max_ulp=int(d.max(initial=0)))
-        assert bad.size == 0, (f"{name}: {bad.size} of {n} bf16 elements beyond 1 ulp; "
+        assert bad.size == 0, (f"{name}: {bad.size} of {n} {kind} elements beyond 1 ulp; "
                                f"first at {bad[:5]}: got {got[bad[:5]]} ref {ref[bad[:5]]}")
         return stats
     gv = got.view(np.uint8).reshape(n, -1) if n else got

@@ -1,9 +1,10 @@
 """ctypes front end of the CPU oracle (test infrastructure only).
 
 Arrays are numpy arrays. Modes: MODE_F64 (fp64 parameters, gradients and
-moments; the parameter is its own master), MODE_F32 (the same in fp32) and
+moments; the parameter is its own master), MODE_F32 (the same in fp32),
 MODE_MIXED (bf16 parameters and gradients as uint16 bit patterns, fp32 master,
-m and v). Every step function is functional: it returns new arrays and leaves
+m and v) and MODE_MIXED_F16 (the same with fp16 bit patterns). Every step
+function is functional: it returns new arrays and leaves
 its inputs untouched, as the problem statement's zero_step returns
 (new_param, new_states).
 """
@@ -14,9 +15,12 @@ import numpy as np
 
 from . import build_oracle
 
-MODE_F64, MODE_F32, MODE_MIXED = 0, 1, 2
-_PARAM_DT = {MODE_F64: np.float64, MODE_F32: np.float32, MODE_MIXED: np.uint16}
-_STATE_DT = {MODE_F64: np.float64, MODE_F32: np.float32, MODE_MIXED: np.float32}
+MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16 = 0, 1, 2, 3
+MIXED_MODES = (MODE_MIXED, MODE_MIXED_F16)
+_PARAM_DT = {MODE_F64: np.float64, MODE_F32: np.float32, MODE_MIXED: np.uint16,
+             MODE_MIXED_F16: np.uint16}
+_STATE_DT = {MODE_F64: np.float64, MODE_F32: np.float32, MODE_MIXED: np.float32,
+             MODE_MIXED_F16: np.float32}
 
 _i64, _i32, _dbl, _vp = C.c_int64, C.c_int, C.c_double, C.c_void_p
 
@@ -43,6 +47,8 @@ class Oracle:
         lib.orc_owner.argtypes = [_i64, _i64, _i64]
         lib.orc_owner.restype = _i64
         lib.orc_bf16_round.argtypes = [_vp, _vp, _i64]
+        lib.orc_fp16_round.argtypes = [_vp, _vp, _i64]
+        lib.orc_fp16_widen.argtypes = [_vp, _vp, _i64]
         lib.orc_init_states.argtypes = [_i32, _i64, _vp, _vp, _vp, _vp]
         step_args = [_i32, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                      _i64, _dbl, _dbl, _dbl, _dbl, _dbl, _vp]
@@ -87,6 +93,20 @@ class Oracle:
         self.lib.orc_bf16_round(_ptr(x), _ptr(out), x.size)
         return out
 
+    def fp16_round(self, x):
+        """IEEE binary16 bit patterns of float32 values, rounded to nearest even."""
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        out = np.empty(x.shape, dtype=np.uint16)
+        self.lib.orc_fp16_round(_ptr(x), _ptr(out), x.size)
+        return out
+
+    def fp16_widen(self, h):
+        """float32 values of fp16 bit patterns (exact)."""
+        h = np.ascontiguousarray(h, dtype=np.uint16)
+        out = np.empty(h.shape, dtype=np.float32)
+        self.lib.orc_fp16_widen(_ptr(h), _ptr(out), h.size)
+        return out
+
     # -- states ---------------------------------------------------------------
     def init_states(self, mode, param):
         param = np.ascontiguousarray(param, dtype=_PARAM_DT[mode])
@@ -94,7 +114,7 @@ class Oracle:
         sdt = _STATE_DT[mode]
         m = np.empty(n, sdt)
         v = np.empty(n, sdt)
-        master = np.empty(n, np.float32) if mode == MODE_MIXED else None
+        master = np.empty(n, np.float32) if mode in MIXED_MODES else None
         self.lib.orc_init_states(mode, n, _ptr(param), _ptr(master), _ptr(m), _ptr(v))
         return master, m, v
 
@@ -106,7 +126,7 @@ class Oracle:
         m = np.ascontiguousarray(m, dtype=sdt)
         v = np.ascontiguousarray(v, dtype=sdt)
         if master is not None:
-            master = np.ascontiguousarray(master, dtype=np.float32 if mode == MODE_MIXED else sdt)
+            master = np.ascontiguousarray(master, dtype=np.float32 if mode in MIXED_MODES else sdt)
         return param, grads, master, m, v
 
     def _call_full(self, fn, mode, param, grads, master, m, v, t, lr, b1, b2, eps, wd, decay):
@@ -115,7 +135,7 @@ class Oracle:
         for g in grads:
             assert g.size == n
         p_out = np.empty_like(param)
-        mst_out = np.empty(n, np.float32) if mode == MODE_MIXED else None
+        mst_out = np.empty(n, np.float32) if mode in MIXED_MODES else None
         m_out, v_out = np.empty_like(m), np.empty_like(v)
         dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.uint8)
         rc = fn(mode, n, N, _ptr(param), _ptr_array(grads), _ptr(master), _ptr(m), _ptr(v),
@@ -175,12 +195,12 @@ class Oracle:
         n = param.size
         N = len(grads) if N is None else N
         if master is not None:
-            master = np.ascontiguousarray(master, dtype=np.float32 if mode == MODE_MIXED else sdt)
+            master = np.ascontiguousarray(master, dtype=np.float32 if mode in MIXED_MODES else sdt)
         p_out = np.empty_like(param)
         if f == 2:
             mst_out = np.empty_like(master)
         else:
-            mst_out = np.empty(n, np.float32) if mode == MODE_MIXED else None
+            mst_out = np.empty(n, np.float32) if mode in MIXED_MODES else None
         b_out = np.empty_like(buf)
         dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.uint8)
         rc = self.lib.orc_sgd_step(f, mode, n, N, rank, _ptr(param), _ptr_array(grads),
@@ -226,12 +246,12 @@ class Oracle:
         v = np.ascontiguousarray(v, dtype=sdt)
         n = param.size
         if master is not None:
-            master = np.ascontiguousarray(master, dtype=np.float32 if mode == MODE_MIXED else sdt)
+            master = np.ascontiguousarray(master, dtype=np.float32 if mode in MIXED_MODES else sdt)
         p_out = np.empty_like(param)
         if rank >= 0:
             mst_out = np.empty_like(master)
         else:
-            mst_out = np.empty(n, np.float32) if mode == MODE_MIXED else None
+            mst_out = np.empty(n, np.float32) if mode in MIXED_MODES else None
         m_out, v_out = np.empty_like(m), np.empty_like(v)
         dec = None if decay is None else np.ascontiguousarray(decay, dtype=np.uint8)
         cs = None if clip_sumsq is None else C.byref(_dbl(float(clip_sumsq)))

@@ -47,6 +47,11 @@
 //     and rounded once to S.
 //   * bf16 write-back in mixed precision: round to nearest, ties to even; NaN
 //     becomes the quiet NaN 0x7FC0.
+//   * fp16 mixed precision ("Data parallelism and ZeRO optimization", section
+//     "Memory Consumption Analysis": fp16 parameters and gradients, fp32
+//     master, momentum and variance): the same step with IEEE binary16
+//     parameters and gradients; write-back rounds to nearest, ties to even,
+//     with gradual underflow and overflow to infinity; NaN becomes 0x7E00.
 //   * Momentum SGD (the other wrapped optimizer of "Data parallelism and ZeRO
 //     stages 1 to 3"; no formula printed): torch.optim.SGD's definition with
 //     coupled L2 decay, the buffer set to the first step's gradient, optional
@@ -136,6 +141,56 @@ uint16_t bf16_round(float x) {
 }
 
 float bf16_widen(uint16_t h) { return bits_float((uint32_t)h << 16); }
+
+// ---------------------------------------------------------------------------
+// IEEE binary16 (fp16), from the definition: 1 sign bit, 5 exponent bits (bias
+// 15), 10 fraction bits; exponent field 0 holds the subnormals k * 2^-24
+// (k < 1024), field 31 infinity and NaN. The representable magnitudes near a
+// value a are a grid of spacing 2^(e-10) in the binade [2^e, 2^(e+1)),
+// e in [-14, 15], and of spacing 2^-24 below 2^-14.
+// ---------------------------------------------------------------------------
+float fp16_widen(uint16_t h) {
+  const int e = (h >> 10) & 0x1F;
+  const int f = h & 0x3FF;
+  double mag;
+  if (e == 0) mag = std::ldexp((double)f, -24);
+  else if (e == 31) mag = f ? NAN : INFINITY;
+  else mag = std::ldexp((double)(1024 + f), e - 25);
+  return (float)((h & 0x8000) ? -mag : mag);
+}
+
+// Round to nearest fp16, ties to the value with an even last fraction bit.
+// Magnitudes from the midpoint between 65504 and 2^16 upwards overflow to
+// infinity, as the grid step past 65504 is 2^16.
+uint16_t fp16_round(float x) {
+  if (std::isnan(x)) return 0x7E00;
+  const uint16_t sign = std::signbit(x) ? 0x8000 : 0;
+  if (std::isinf(x)) return sign | 0x7C00;
+  const double a = std::fabs((double)x);
+  if (a == 0.0) return sign;
+  int e2;
+  std::frexp(a, &e2);  // a = f * 2^e2, f in [0.5, 1): a is in the binade [2^(e2-1), 2^e2)
+  const int binade = e2 - 1 < -14 ? -14 : e2 - 1;
+  const double q = std::ldexp(1.0, binade - 10);  // grid spacing around a
+  const double k = std::floor(a / q);             // a / q is exact: q is a power of two
+  const double dlo = a - k * q, dhi = (k + 1.0) * q - a;
+  double r;
+#if ORACLE_MUTANT == 19
+  r = k;  // planted: truncation instead of rounding
+#else
+  if (dlo < dhi) r = k;
+  else if (dhi < dlo) r = k + 1.0;
+  else r = std::fmod(k, 2.0) == 0.0 ? k : k + 1.0;
+#endif
+  const double v = r * q;
+  if (v >= 65536.0) return sign | 0x7C00;
+  if (v < std::ldexp(1.0, -14)) return sign | (uint16_t)(v / std::ldexp(1.0, -24));
+  int ev;
+  std::frexp(v, &ev);  // v in [2^(ev-1), 2^ev)
+  const int field = ev - 1 + 15;
+  const uint16_t frac = (uint16_t)(v / std::ldexp(1.0, ev - 1 - 10) - 1024.0);
+  return sign | (uint16_t)(field << 10) | frac;
+}
 
 // ---------------------------------------------------------------------------
 // Per-step scalars, formed in double and rounded once to S.
@@ -308,13 +363,17 @@ void opt_update(S* w, const S* g, S* m, S* v, int64_t len, const StepConsts<S>& 
 }
 
 // Element access by mode. mode 0: fp64 everywhere. mode 1: fp32 everywhere.
-// mode 2: bf16 gradients and gathered parameters, fp32 master/m/v.
-enum { MODE_F64 = 0, MODE_F32 = 1, MODE_MIXED = 2 };
+// mode 2: bf16 gradients and gathered parameters, fp32 master/m/v. mode 3: the
+// same with fp16 in place of bf16.
+enum { MODE_F64 = 0, MODE_F32 = 1, MODE_MIXED = 2, MODE_MIXED_F16 = 3 };
+
+bool is_mixed(int mode) { return mode == MODE_MIXED || mode == MODE_MIXED_F16; }
 
 template <class S>
 S load_grad(const void* g, int64_t i, int mode) {
   if (mode == MODE_F64) return (S)((const double*)g)[i];
   if (mode == MODE_F32) return (S)((const float*)g)[i];
+  if (mode == MODE_MIXED_F16) return (S)fp16_widen(((const uint16_t*)g)[i]);
   return (S)bf16_widen(((const uint16_t*)g)[i]);
 }
 
@@ -323,6 +382,7 @@ template <class S>
 void store_param(void* p, int64_t i, S w, int mode) {
   if (mode == MODE_F64) ((double*)p)[i] = (double)w;
   else if (mode == MODE_F32) ((float*)p)[i] = (float)w;
+  else if (mode == MODE_MIXED_F16) ((uint16_t*)p)[i] = fp16_round((float)w);
   else ((uint16_t*)p)[i] = bf16_round((float)w);
 }
 
@@ -330,7 +390,7 @@ void store_param(void* p, int64_t i, S w, int mode) {
 // or the separate fp32 master copy in mixed mode.
 template <class S>
 S load_master(const void* param, const void* master, int64_t i, int mode) {
-  if (mode == MODE_MIXED) return ((const float*)master)[i];
+  if (is_mixed(mode)) return ((const float*)master)[i];
   if (mode == MODE_F64) return (S)((const double*)param)[i];
   return (S)((const float*)param)[i];
 }
@@ -402,7 +462,7 @@ void sharded_step(int mode, int64_t n, int64_t N, const void* param_in,
 #endif
     for (int64_t j = 0; j < len; ++j) {
       store_param<S>(param_out, a + j, w[j], mode);
-      if (mode == MODE_MIXED) ((float*)master_out)[a + j] = (float)w[j];
+      if (is_mixed(mode)) ((float*)master_out)[a + j] = (float)w[j];
       m_out[a + j] = m[j];
       v_out[a + j] = v[j];
     }
@@ -431,7 +491,7 @@ void full_step(int mode, int64_t n, int64_t N, const void* param_in,
   opt_update<S>(w.data(), gbar.data(), m.data(), v.data(), n, c, decay, (S)wd, o, t, lr, wd);
   for (int64_t i = 0; i < n; ++i) {
     store_param<S>(param_out, i, w[(size_t)i], mode);
-    if (mode == MODE_MIXED) ((float*)master_out)[i] = (float)w[(size_t)i];
+    if (is_mixed(mode)) ((float*)master_out)[i] = (float)w[(size_t)i];
     m_out[i] = m[(size_t)i];
     v_out[i] = v[(size_t)i];
   }
@@ -562,7 +622,7 @@ void step_from_mean(int mode, int64_t n, int64_t N, int64_t r, const void* param
     for (int64_t j = 0; j < len; ++j) {
       store_param<S>(param_out, a + j, w[(size_t)j], mode);
       if (r >= 0) ((S*)master_out)[j] = w[(size_t)j];
-      else if (mode == MODE_MIXED) ((float*)master_out)[a + j] = (float)w[(size_t)j];
+      else if (is_mixed(mode)) ((float*)master_out)[a + j] = (float)w[(size_t)j];
       m_out[a - base + j] = m[(size_t)j];
       v_out[a - base + j] = v[(size_t)j];
     }
@@ -594,6 +654,14 @@ void orc_bf16_round(const float* x, uint16_t* out, int64_t len) {
   for (int64_t i = 0; i < len; ++i) out[i] = bf16_round(x[i]);
 }
 
+// fp16 rounding of each of len floats, and the exact widening back.
+void orc_fp16_round(const float* x, uint16_t* out, int64_t len) {
+  for (int64_t i = 0; i < len; ++i) out[i] = fp16_round(x[i]);
+}
+void orc_fp16_widen(const uint16_t* h, float* out, int64_t len) {
+  for (int64_t i = 0; i < len; ++i) out[i] = fp16_widen(h[i]);
+}
+
 // init_states ("ZeRO-Sharded Adam Step", section "What to implement"): m and v
 // of zeros; in mixed mode the fp32 master is the exact widening of the bf16
 // parameters. len elements (full n, or one shard).
@@ -602,9 +670,10 @@ void orc_init_states(int mode, int64_t len, const void* param, void* master,
   const size_t s = mode == MODE_F64 ? 8 : 4;
   std::memset(m, 0, (size_t)len * s);
   std::memset(v, 0, (size_t)len * s);
-  if (mode == MODE_MIXED && master) {
+  if (is_mixed(mode) && master) {
     for (int64_t i = 0; i < len; ++i)
-      ((float*)master)[i] = bf16_widen(((const uint16_t*)param)[i]);
+      ((float*)master)[i] = mode == MODE_MIXED_F16 ? fp16_widen(((const uint16_t*)param)[i])
+                                                   : bf16_widen(((const uint16_t*)param)[i]);
   }
 }
 
@@ -619,7 +688,7 @@ int orc_zero_step(int mode, int64_t n, int64_t N, const void* param_in,
     sharded_step<double>(mode, n, N, param_in, grads, master_in, (const double*)m_in,
                          (const double*)v_in, param_out, master_out, (double*)m_out,
                          (double*)v_out, t, lr, b1, b2, eps, wd, decay);
-  else if (mode == MODE_F32 || mode == MODE_MIXED)
+  else if (mode == MODE_F32 || is_mixed(mode))
     sharded_step<float>(mode, n, N, param_in, grads, master_in, (const float*)m_in,
                         (const float*)v_in, param_out, master_out, (float*)m_out,
                         (float*)v_out, t, lr, b1, b2, eps, wd, decay);
@@ -639,7 +708,7 @@ int orc_full_step(int mode, int64_t n, int64_t N, const void* param_in,
     full_step<double>(mode, n, N, param_in, grads, master_in, (const double*)m_in,
                       (const double*)v_in, param_out, master_out, (double*)m_out,
                       (double*)v_out, t, lr, b1, b2, eps, wd, decay);
-  else if (mode == MODE_F32 || mode == MODE_MIXED)
+  else if (mode == MODE_F32 || is_mixed(mode))
     full_step<float>(mode, n, N, param_in, grads, master_in, (const float*)m_in,
                      (const float*)v_in, param_out, master_out, (float*)m_out,
                      (float*)v_out, t, lr, b1, b2, eps, wd, decay);
@@ -661,7 +730,7 @@ int orc_rank_step(int mode, int64_t n, int64_t N, int64_t r, const void* param_i
                       (const double*)m_in, (const double*)v_in, param_out,
                       (double*)master_out, (double*)m_out, (double*)v_out, t, lr, b1,
                       b2, eps, wd, decay);
-  else if (mode == MODE_F32 || mode == MODE_MIXED)
+  else if (mode == MODE_F32 || is_mixed(mode))
     rank_step<float>(mode, n, N, r, param_in, chunk_grads, (const float*)master_in,
                      (const float*)m_in, (const float*)v_in, param_out,
                      (float*)master_out, (float*)m_out, (float*)v_out, t, lr, b1, b2,
@@ -678,7 +747,7 @@ int orc_mean_grad(int mode, int64_t n, int64_t N, int64_t rank, const void* cons
   if (n < 0 || N < 1 || rank >= N) return -1;
   if (mode == MODE_F64)
     mean_grad<double>(mode, n, N, rank, grads, (double*)mean_out, sumsq_out);
-  else if (mode == MODE_F32 || mode == MODE_MIXED)
+  else if (mode == MODE_F32 || is_mixed(mode))
     mean_grad<float>(mode, n, N, rank, grads, (float*)mean_out, sumsq_out);
   else
     return -1;
@@ -698,7 +767,7 @@ int orc_step_mean(int mode, int64_t n, int64_t N, int64_t rank, const void* para
                            (const double*)m_in, (const double*)v_in, param_out, master_out,
                            (double*)m_out, (double*)v_out, t, lr, b1, b2, eps, wd, decay,
                            clip_sumsq, max_norm);
-  else if (mode == MODE_F32 || mode == MODE_MIXED)
+  else if (mode == MODE_F32 || is_mixed(mode))
     step_from_mean<float>(mode, n, N, rank, param_in, (const float*)mean, master_in,
                           (const float*)m_in, (const float*)v_in, param_out, master_out,
                           (float*)m_out, (float*)v_out, t, lr, b1, b2, eps, wd, decay,
@@ -740,7 +809,7 @@ int orc_sgd_step(int form, int mode, int64_t n, int64_t N, int64_t rank, const v
       rank_step<S>(mode, n, N, rank, param_in, grads, (const S*)master_in, (const S*)buf_in,
                    (const S*)vin.data(), param_out, (S*)master_out, (S*)buf_out, (S*)vout.data(),
                    t, lr, 0.9, 0.9, 1.0, wd, decay, o);
-  } else if (mode == MODE_F32 || mode == MODE_MIXED) {
+  } else if (mode == MODE_F32 || is_mixed(mode)) {
     typedef float S;
     if (form == 0)
       sharded_step<S>(mode, n, N, param_in, grads, master_in, (const S*)buf_in, (const S*)vin.data(),

@@ -6,7 +6,7 @@ disagrees with what the pages or the mathematics fix:
   * values the pages print for their worked examples (tests/golden/),
   * closed forms (first-step move, constant-gradient trajectory, memory),
   * special cases that reduce to a library routine (torch.optim.Adam/AdamW with
-    one worker, numpy.array_split, torch's bf16 conversion),
+    one worker, numpy.array_split, torch's bf16 and numpy's fp16 conversions),
   * invariants the pages state (sharded equals shard-free, a rank's share
     equals the shard of the full step).
 
@@ -19,7 +19,7 @@ import os
 
 import numpy as np
 
-from oracle import MODE_F32, MODE_F64, MODE_MIXED
+from oracle import MIXED_MODES, MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
@@ -38,6 +38,17 @@ def _bf16_bits(x_f32):
 
 def _widen(bits):
     return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def _fp16_bits(x_f32):
+    """Round-to-nearest-even IEEE binary16 bits of fp32 values, via numpy's
+    conversion (a library routine)."""
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x_f32, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _fp16_widen(bits):
+    return np.ascontiguousarray(bits, dtype=np.uint16).view(np.float16).astype(np.float32)
 
 
 # ---------------------------------------------------------------------------
@@ -275,6 +286,8 @@ def _case_for_mode(rng, mode, n, N):
     grads = [(1e-3 * rng.standard_normal(n)).astype(np.float32) for _ in range(N)]
     if mode == MODE_MIXED:
         return _bf16_bits(w), [_bf16_bits(g) for g in grads]
+    if mode == MODE_MIXED_F16:
+        return _fp16_bits(w), [_fp16_bits(g) for g in grads]
     return w, grads
 
 
@@ -283,7 +296,7 @@ def pin_sharded_equals_shard_free(O):
     over the whole vector driven by the averaged gradient, bit for bit, for every
     shard count."""
     rng = np.random.default_rng(17)
-    for mode in (MODE_F64, MODE_F32, MODE_MIXED):
+    for mode in (MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16):
         for n, N in ((1, 1), (3, 5), (10, 4), (1031, 7), (4096, 64), (777, 2)):
             w, _ = _case_for_mode(rng, mode, n, 1)
             mst, m, v = O.init_states(mode, w)
@@ -298,7 +311,7 @@ def pin_sharded_equals_shard_free(O):
                                                1e-8, 0.1, decay=flags)
                 assert np.array_equal(ws.view(np.uint8), wf.view(np.uint8)), (mode, n, N, t)
                 assert np.array_equal(ms, mf) and np.array_equal(vs, vf), (mode, n, N, t)
-                if mode == MODE_MIXED:
+                if mode in MIXED_MODES:
                     assert np.array_equal(msts, mstf)
 
 
@@ -307,7 +320,7 @@ def pin_rank_share_equals_shard(O):
     step restricted to that rank's shard (openlearn L11.3, section '2. Principles',
     stage 2), and leaves every other element of the gathered vector as it was."""
     rng = np.random.default_rng(18)
-    for mode in (MODE_F64, MODE_F32, MODE_MIXED):
+    for mode in (MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16):
         for n, N in ((1031, 8), (10, 4), (3, 5)):
             w, grads = _case_for_mode(rng, mode, n, N)
             mst, m, v = O.init_states(mode, w)
@@ -319,8 +332,8 @@ def pin_rank_share_equals_shard(O):
                                                            0.9, 0.95, 1e-8, 0.1, decay=flags)
             for r in range(N):
                 a, b = O.split_bounds(n, N, r)
-                master_r = (mst if mode == MODE_MIXED else w)[a:b]
-                if mode != MODE_MIXED:
+                master_r = (mst if mode in MIXED_MODES else w)[a:b]
+                if mode not in MIXED_MODES:
                     master_r = master_r.astype(w.dtype)
                 chunks = [g[a:b] for g in grads]
                 pw, pm, rm, rv = O.rank_step(mode, N, r, w, chunks, master_r, m[a:b], v[a:b], 2,
@@ -329,7 +342,7 @@ def pin_rank_share_equals_shard(O):
                 assert np.array_equal(pw[:a].view(np.uint8), w[:a].view(np.uint8))
                 assert np.array_equal(pw[b:].view(np.uint8), w[b:].view(np.uint8))
                 assert np.array_equal(rm, full_m[a:b]) and np.array_equal(rv, full_v[a:b])
-                full_master = full_mst if mode == MODE_MIXED else full_w
+                full_master = full_mst if mode in MIXED_MODES else full_w
                 assert np.array_equal(pm.view(np.uint8),
                                       full_master[a:b].astype(pm.dtype).view(np.uint8))
 
@@ -377,6 +390,62 @@ def pin_mixed_precision(O):
         w64, _, m64, v64 = O.zero_step(MODE_F64, w64, [_widen(g).astype(np.float64) for g in gb],
                                        None, m64, v64, t, 1e-4, 0.9, 0.95, 1e-8)
         assert np.array_equal(p, _bf16_bits(mst))
+        assert np.all(np.abs(mst - w64) <= 1e-6 * np.maximum(1, np.abs(w64)))
+        assert np.allclose(m, m64, rtol=1e-5, atol=2e-6 * np.abs(m64).max())
+
+
+def pin_fp16_rounding(O):
+    """The oracle's fp16 rounding equals numpy's round-to-nearest-even float32 ->
+    float16 conversion (gradual underflow, overflow to infinity), and its widening
+    equals numpy's float16 -> float32 for all 65536 bit patterns."""
+    rng = np.random.default_rng(21)
+    x = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (1e-3 * rng.standard_normal(20000)).astype(np.float32),
+        np.ldexp(rng.standard_normal(8000), rng.integers(-30, 18, 8000)).astype(np.float32),
+        np.array([0.0, -0.0, np.inf, -np.inf, 65504.0, 65519.0, 65520.0, 65536.0, -65520.0,
+                  2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25,
+                  1e-45, 3.4028235e38], np.float32),
+    ])
+    # exact ties: a finite fp16 value plus half its ulp, both parities, normal and subnormal
+    h = rng.integers(1, 0x7BFF, 6000).astype(np.uint16)
+    lo = _fp16_widen(h).astype(np.float64)
+    hi = _fp16_widen(h + 1).astype(np.float64)
+    ties = ((lo + hi) / 2).astype(np.float32)
+    x = np.concatenate([x, ties, -ties, np.nextafter(ties, np.float32(0)),
+                        np.nextafter(ties, np.float32(np.inf))])
+    got = O.fp16_round(x)
+    ref = _fp16_bits(x)
+    assert np.array_equal(got, ref), np.flatnonzero(got != ref)[:10]
+    assert O.fp16_round(np.array([np.nan], np.float32))[0] == 0x7E00
+    allh = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    wid = O.fp16_widen(allh)
+    refw = _fp16_widen(allh)
+    nan = np.isnan(refw)
+    assert np.array_equal(np.isnan(wid), nan)
+    assert np.array_equal(wid[~nan].view(np.uint32), refw[~nan].view(np.uint32))
+    assert np.array_equal(O.fp16_round(wid[~nan]), allh[~nan])  # exact round trip
+
+
+def pin_mixed_f16_precision(O):
+    """fp16 mixed mode: the master starts as the exact widening of the fp16
+    parameters, the gathered output is the fp16 rounding of the master, and the
+    master follows the fp64 trajectory within fp32 rounding."""
+    rng = np.random.default_rng(22)
+    n, N, T = 2048, 8, 5
+    p_bits = _fp16_bits((0.02 * rng.standard_normal(n)).astype(np.float32))
+    mst, m, v = O.init_states(MODE_MIXED_F16, p_bits)
+    assert np.array_equal(mst, _fp16_widen(p_bits)) and not m.any() and not v.any()
+    w64 = _fp16_widen(p_bits).astype(np.float64)
+    _, m64, v64 = O.init_states(MODE_F64, w64)
+    p = p_bits
+    for t in range(1, T + 1):
+        gb = [_fp16_bits((1e-3 * rng.standard_normal(n)).astype(np.float32)) for _ in range(N)]
+        p, mst, m, v = O.zero_step(MODE_MIXED_F16, p, gb, mst, m, v, t, 1e-4, 0.9, 0.95, 1e-8)
+        w64, _, m64, v64 = O.zero_step(MODE_F64, w64,
+                                       [_fp16_widen(g).astype(np.float64) for g in gb],
+                                       None, m64, v64, t, 1e-4, 0.9, 0.95, 1e-8)
+        assert np.array_equal(p, _fp16_bits(mst))
         assert np.all(np.abs(mst - w64) <= 1e-6 * np.maximum(1, np.abs(w64)))
         assert np.allclose(m, m64, rtol=1e-5, atol=2e-6 * np.abs(m64).max())
 
@@ -487,7 +556,7 @@ def pin_step_from_mean_equals_step(O):
     step from the mean gradient, unclipped or clipped with a threshold the norm does
     not reach, equals the fused step bit for bit, in every mode."""
     rng = np.random.default_rng(22)
-    for mode in (MODE_F64, MODE_F32, MODE_MIXED):
+    for mode in (MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16):
         n, N = 3001, 5
         w, grads = _case_for_mode(rng, mode, n, N)
         mst, m, v = O.init_states(mode, w)
@@ -603,7 +672,7 @@ def pin_sgd_constant_gradient(O):
 
 def pin_sgd_sharded_equals_shard_free_and_rank_share(O):
     rng = np.random.default_rng(27)
-    for mode in (MODE_F64, MODE_F32, MODE_MIXED):
+    for mode in (MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16):
         n, N = 2051, 7
         w, _ = _case_for_mode(rng, mode, n, 1)
         mst, buf, _ = O.init_states(mode, w)
@@ -617,7 +686,7 @@ def pin_sgd_sharded_equals_shard_free_and_rank_share(O):
             assert np.array_equal(a_p.view(np.uint8), f_p.view(np.uint8)) and np.array_equal(a_b, f_b)
             for r in (0, N // 2, N - 1):
                 lo, hi = O.split_bounds(n, N, r)
-                master_r = (ms_ if mode == MODE_MIXED else ws)[lo:hi].astype(bs.dtype)
+                master_r = (ms_ if mode in MIXED_MODES else ws)[lo:hi].astype(bs.dtype)
                 r_p, r_m, r_b = O.sgd_step(mode, ws, [g[lo:hi] for g in grads], master_r,
                                            bs[lo:hi], *args, form="rank", N=N, rank=r)
                 assert np.array_equal(r_p[lo:hi].view(np.uint8), a_p[lo:hi].view(np.uint8))
@@ -642,6 +711,8 @@ ALL_PINS = [
     pin_rank_share_equals_shard,
     pin_bf16_rounding,
     pin_mixed_precision,
+    pin_fp16_rounding,
+    pin_mixed_f16_precision,
     pin_memory_byte_table,
     pin_memory_closed_forms,
     pin_mean_grad_worked_example,

@@ -6,7 +6,7 @@ beginning at another rank's chunk, no all-gather after the update, stage 2 keepi
 full gradients, dropped hyperparameters) plus plausible slips in the Adam formula
 itself (exchanged betas, a dropped bias correction, eps inside the square root,
 coupled instead of decoupled decay, a wrong sign, an off-by-one step count, an
-inverted decay mask, truncating instead of rounding to bf16, an unclamped or
+inverted decay mask, truncating instead of rounding to bf16 or fp16, an unclamped or
 wrongly normed clipping factor). The mistakes are
 planted in the oracle on the CPU only.
 """
@@ -34,6 +34,7 @@ MUTANTS = {
     16: "1-norm instead of squared norm",
     17: "SGD momentum buffer starting at zero",
     18: "SGD with decoupled instead of coupled decay",
+    19: "fp16 truncation",
 }
 
 
