@@ -33,14 +33,14 @@ KERNEL_SRC = os.path.join(ROOT, "zero_sharded_optimizer_amd", "csrc", "zero_kern
 def bytes_per_param(wl):
     """Algorithmic HBM bytes per updated parameter: every worker's gradient read
     once; master (or in-place parameter), m and v read once and written once; the
-    gathered parameter written once when it is a separate buffer (bf16 in mixed
-    mode, the rank's slot in rank mode); one decay-mask bit when a mask is used."""
+    gathered parameter written once when it is a separate buffer (bf16 or fp16
+    in the mixed modes, the rank's slot in rank mode); one decay-mask bit when a mask is used."""
     from zero_sharded_optimizer_amd import synth
-    g = {0: 8, 1: 4, 2: 2}[wl.mode]
+    g = {0: 8, 1: 4, 2: 2, 3: 2}[wl.mode]
     s = 8 if wl.mode == 0 else 4
     p = g
     b = wl.n_workers * g + 6 * s
-    if wl.mode == 2 or wl.rank >= 0:
+    if wl.mode in (2, 3) or wl.rank >= 0:
         b += p
     if synth.decay_flags(wl) is not None:
         b += 1 / 8
@@ -185,7 +185,7 @@ def cpu_baseline(wl, target_s=12.0, sample_n=1 << 22):
     assert n > 0
 
     def host(x):
-        if x.dtype == torch.bfloat16:
+        if x.dtype in (torch.bfloat16, torch.float16):
             return x.view(torch.int16).cpu().numpy().view(np.uint16).copy()
         return x.cpu().numpy().copy()
 
@@ -235,7 +235,7 @@ def cpu_baseline_threads(wl, target_s=8.0, sample_n=1 << 22):
     n = small.n
 
     def host(x):
-        if x.dtype == torch.bfloat16:
+        if x.dtype in (torch.bfloat16, torch.float16):
             return x.view(torch.int16).cpu().numpy().view(np.uint16).copy()
         return x.cpu().numpy().copy()
 
@@ -365,13 +365,13 @@ def stream_ceilings(wl):
     a, b = wl.shard
     vec = 2 if wl.mode == 0 else 4
     ngroups = (b - a) // vec
-    gw = 8 if wl.mode == 2 else 16  # bytes of one group of one gradient stream
+    gw = 8 if wl.mode in (2, 3) else 16  # bytes of one group of one gradient stream
     N = wl.n_workers
     out = {}
     out["copy_GBps"], out["copy_shape"] = _time_streams(lib, [16], [16], (4 << 30) // 16)
     out["read_n_write_1_GBps"], out["read_n_write_1_shape"] = _time_streams(
         lib, [gw] * N, [16], ngroups)
-    writes = [16, 16, 16] + ([8] if wl.mode == 2 else [])
+    writes = [16, 16, 16] + ([8] if wl.mode in (2, 3) else [])
     out["step_streams"] = (f"{N} x {gw} B + 3 x 16 B read, {len(writes)} streams "
                            f"({'+'.join(str(w) for w in writes)} B) written per group")
     out["step_streams_GBps"], out["step_streams_shape"] = _time_streams(
@@ -432,7 +432,7 @@ def main():
     # resident inputs
     param, master0 = synth.make_params(wl, "cuda")
     sdt = synth.state_dtype(wl)
-    need_master = wl.mode == 2 or wl.rank >= 0
+    need_master = wl.mode in (2, 3) or wl.rank >= 0
     st = z.States(torch.empty(L, dtype=sdt, device="cuda") if need_master else None,
                   torch.empty(L, dtype=sdt, device="cuda"), torch.empty(L, dtype=sdt, device="cuda"))
     flags = synth.decay_flags(wl)
@@ -464,7 +464,7 @@ def main():
 
     buckets = None
     if args.bucket_mib is not None:
-        gbytes = {0: 8, 1: 4, 2: 2}[wl.mode]
+        gbytes = {0: 8, 1: 4, 2: 2, 3: 2}[wl.mode]
         size = max(8, int(args.bucket_mib * (1 << 20)) // gbytes // 8 * 8)
         edges = list(range(0, L, size)) + [L]
         buckets = list(reversed(list(zip(edges[:-1], edges[1:]))))
@@ -525,7 +525,7 @@ def main():
     algo_bytes = bpp * L
     achieved = algo_bytes / (avg_ms * 1e-3) / 1e9
     traffic = load_traffic(wl.name, algo_bytes) if max_norm is None and buckets is None else None
-    dtype = {0: "f64", 1: "f32", 2: "bf16+f32"}[wl.mode]
+    dtype = {0: "f64", 1: "f32", 2: "bf16+f32", 3: "f16+f32"}[wl.mode]
 
     del grads, param, st
     torch.cuda.empty_cache()

@@ -29,8 +29,8 @@
  *     w   = w * (1 - lr*wd)                  where decay applies
  *     w   = w - lr*(mh/den)
  * 1-b1, 1-b2, 1-b1^t, 1-b2^t and 1-lr*wd are formed in double on the host and
- * rounded once to S. In mixed mode the gathered parameter is the bf16
- * round-to-nearest-even of w (NaN stored as 0x7FC0).
+ * rounded once to S. In mixed mode the gathered parameter is the bf16 (or
+ * fp16) round-to-nearest-even of w (NaN stored as 0x7FC0, or 0x7E00).
  *
  * Conventions shared by every function:
  *   - All device buffers are owned by the caller; the library never allocates,
@@ -69,7 +69,12 @@ typedef enum {
   ZERO_MODE_F32 = 1,
   /* bf16 parameters and gradients, fp32 master, m and v (K = 12, same section;
    * "Data Parallelism & ZeRO", section "ZeRO, stage by stage"). */
-  ZERO_MODE_MIXED_BF16 = 2
+  ZERO_MODE_MIXED_BF16 = 2,
+  /* IEEE fp16 parameters and gradients, fp32 master, m and v (K = 12; "Data
+   * parallelism and ZeRO optimization", section "Memory Consumption
+   * Analysis"). The gathered parameter is the fp16 round-to-nearest-even of w,
+   * with gradual underflow and overflow to infinity (NaN stored as 0x7E00). */
+  ZERO_MODE_MIXED_F16 = 3
 } zero_mode;
 
 typedef enum {
@@ -127,7 +132,7 @@ typedef struct {
  *   Full mode (rank == -1): m and v hold n elements of S; worker r's shard is
  *     the view [a_r, b_r) of each (the N per-worker (m_shard, v_shard) pairs of
  *     "What to implement", laid back to back). master holds n fp32 values in
- *     mixed mode and must be NULL in fp64/fp32 mode, where the parameter is
+ *     the mixed modes and must be NULL in fp64/fp32 mode, where the parameter is
  *     updated in place and is its own master.
  *   Rank mode (rank == r): m, v and master each hold c_r = b_r - a_r elements
  *     of S: only worker r's shard. master is required in every mode (the rank's
@@ -140,9 +145,9 @@ typedef struct {
 } zero_states;
 
 /* init_states ("What to implement"): zero m and v, and set the master copy
- * from the parameters (exact bf16 -> fp32 widening in mixed mode, a copy in
+ * from the parameters (exact bf16/fp16 -> fp32 widening in the mixed modes, a copy in
  * rank mode's fp64/fp32 master). `param` is the gathered parameter vector of n
- * elements (bf16 in mixed mode, else S), read-only; in rank mode only
+ * elements (bf16/fp16 in the mixed modes, else S), read-only; in rank mode only
  * [a_r, b_r) of it is read. Enqueued on `stream`. An empty rank shard
  * enqueues nothing and touches no buffer (they may be NULL). Errors as for
  * zero_step, without the step scalars and t. */
@@ -150,12 +155,12 @@ zero_status zero_init_states(const zero_hparams* hp, const void* param,
                              const zero_states* states, void* stream);
 
 /* zero_step ("What to implement"; "The step" items 1-3): one fused step.
- *   param: the gathered parameter vector, n elements (bf16 in mixed mode,
+ *   param: the gathered parameter vector, n elements (bf16/fp16 in the mixed modes,
  *     else S), updated in place. Full mode: every element is rewritten; it
  *     must be 16-byte aligned. Rank mode: only [a_r, b_r) is written; it must
  *     be aligned to its element size.
  *   grads: host array of N device pointers, in rank order, read-only, each
- *     16-byte aligned (elements of G = bf16 in mixed mode, else S). Full mode:
+ *     16-byte aligned (elements of G = bf16/fp16 in the mixed modes, else S). Full mode:
  *     worker k's full local gradient, n elements. Rank mode: the chunk
  *     g_k[a_r:b_r) that worker k contributes to shard r, c_r elements.
  *     Gradient buffers may alias one another but not any buffer the step
@@ -307,7 +312,7 @@ typedef struct {
  *     stage 3: B c,  B c,        2 B c   (the chunk is the parameter storage)
  * Errors: ZERO_EINVAL for n < 1, N < 1, rank outside [0, N), stage outside
  * [0, 3], an unknown mode or convention, or a NULL out; ZERO_EUNSUPPORTED for
- * convention 1 in mixed mode. */
+ * convention 1 in the mixed modes. */
 zero_status zero_memory_bytes(int64_t n, int32_t n_workers, int32_t rank, int32_t stage,
                               int32_t mode, int32_t convention, zero_mem* out);
 

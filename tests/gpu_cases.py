@@ -5,7 +5,7 @@ import numpy as np
 
 import zero_sharded_optimizer_amd as z
 from zero_sharded_optimizer_amd import synth
-from oracle import MODE_F64, MODE_MIXED
+from oracle import MIXED_MODES, MODE_F64, MODE_MIXED
 from oracle.compare import compare
 
 
@@ -15,7 +15,7 @@ def say(msg):
 
 def host(x):
     import torch
-    if x.dtype == torch.bfloat16:
+    if x.dtype in (torch.bfloat16, torch.float16):
         return x.view(torch.int16).cpu().numpy().view(np.uint16).copy()
     return x.cpu().numpy().copy()
 
@@ -24,8 +24,8 @@ def kinds(wl):
     """(param kind, state kind) of the parity bar for a workload's mode."""
     if wl.mode == MODE_F64:
         return "exact", "exact"
-    if wl.mode == MODE_MIXED:
-        return "bf16", "f32"
+    if wl.mode in MIXED_MODES:
+        return ("bf16" if wl.mode == MODE_MIXED else "fp16"), "f32"
     return "f32", "f32"
 
 
@@ -44,7 +44,7 @@ def setup(wl):
     sdt = synth.state_dtype(wl)
     flags = synth.decay_flags(wl)
     mask = z.wd_mask_from_flags(flags) if flags is not None else None
-    need_master = wl.mode == MODE_MIXED or wl.rank >= 0
+    need_master = wl.mode in MIXED_MODES or wl.rank >= 0
     st = z.States(master=torch.empty(L, dtype=sdt, device="cuda") if need_master else None,
                   m=torch.empty(L, dtype=sdt, device="cuda"),
                   v=torch.empty(L, dtype=sdt, device="cuda"))

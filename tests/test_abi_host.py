@@ -73,7 +73,8 @@ def test_shard_bounds_rejects(args):
 
 
 # -- memory model -------------------------------------------------------------
-WIDTH = {z.ZERO_MODE_MIXED_BF16: (2, 2, 12), z.ZERO_MODE_F32: (4, 4, 8), z.ZERO_MODE_F64: (8, 8, 16)}
+WIDTH = {z.ZERO_MODE_MIXED_BF16: (2, 2, 12), z.ZERO_MODE_MIXED_F16: (2, 2, 12),
+         z.ZERO_MODE_F32: (4, 4, 8), z.ZERO_MODE_F64: (8, 8, 16)}
 
 
 def test_memory_bytes_agrees_with_oracle(oracle):
@@ -83,11 +84,11 @@ def test_memory_bytes_agrees_with_oracle(oracle):
         N = int(rng.integers(1, 100))
         r = int(rng.integers(0, N))
         stage = int(rng.integers(0, 4))
-        mode = int(rng.integers(0, 3))
+        mode = int(rng.integers(0, 4))
         P, G, K = WIDTH[mode]
         got = z.zero_memory_bytes(n, N, r, stage, mode, 0)
         assert got == oracle.memory_bytes(n, N, r, stage, P, G, K, 0)
-        if mode != z.ZERO_MODE_MIXED_BF16:
+        if mode not in (z.ZERO_MODE_MIXED_BF16, z.ZERO_MODE_MIXED_F16):
             got = z.zero_memory_bytes(n, N, r, stage, mode, 1)
             assert got == oracle.memory_bytes(n, N, r, stage, P, G, K, 1)
 
@@ -124,9 +125,10 @@ def test_memory_bytes_closed_forms():
     ((10, 4, 4, 1, 0, 0), z.ZERO_EINVAL),
     ((10, 4, 0, 4, 0, 0), z.ZERO_EINVAL),     # stage 4
     ((10, 4, 0, -1, 0, 0), z.ZERO_EINVAL),
-    ((10, 4, 0, 1, 3, 0), z.ZERO_EINVAL),     # unknown mode
+    ((10, 4, 0, 1, 4, 0), z.ZERO_EINVAL),     # unknown mode
     ((10, 4, 0, 1, 0, 2), z.ZERO_EINVAL),     # unknown convention
     ((10, 4, 0, 1, 2, 1), z.ZERO_EUNSUPPORTED),
+    ((10, 4, 0, 1, 3, 1), z.ZERO_EUNSUPPORTED),
 ])
 def test_memory_bytes_rejects(args, status):
     with pytest.raises(z.ZeroError) as e:

@@ -16,16 +16,17 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
-from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
+from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from oracle.compare import compare  # noqa: E402
 from gpu_cases import host, kinds, say, setup  # noqa: E402
 
 W = synth.WORKLOADS
-BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"]}
+BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"],
+        MODE_MIXED_F16: W["mixed-fp16-1B-n8"]}
 
 
 def _bits(x):
-    return x.view({torch.bfloat16: torch.int16, torch.float64: torch.int64,
+    return x.view({torch.bfloat16: torch.int16, torch.float16: torch.int16, torch.float64: torch.int64,
                    torch.float32: torch.int32}[x.dtype])
 
 
@@ -53,7 +54,7 @@ def _check_vs_oracle(oracle, wl, param, st, p0, g_hist):
     compare("v", host(st.v), v, sk)
 
 
-@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED])
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16])
 @pytest.mark.parametrize("bucket", [65_536, 1000, 1_000_008])
 def test_buckets_in_reverse_order_equal_one_shot(oracle, mode, bucket):
     wl = synth.scaled(BASE[mode], 1_000_003, weight_decay=0.05, decay="all")

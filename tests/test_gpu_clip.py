@@ -26,12 +26,13 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
-from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
+from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from oracle.compare import compare  # noqa: E402
 from gpu_cases import host, kinds, say, setup  # noqa: E402
 
 W = synth.WORKLOADS
-BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"]}
+BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"],
+        MODE_MIXED_F16: W["mixed-fp16-1B-n8"]}
 
 
 def _dev_double(x=0.0):
@@ -46,7 +47,7 @@ def sumsq_close(got, ref, n):
     return abs(got - ref) <= 2 * n * 2.0 ** -53 * abs(ref) + 1e-300
 
 
-@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED])
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16])
 @pytest.mark.parametrize("n,N", [(1_000_003, 8), (4099, 3), (9, 5), (3, 5), (100_001, 64)])
 def test_mean_grad_full_and_rank_mode(oracle, mode, n, N):
     say(f"[case] mean grad mode={mode} n={n} N={N}")
@@ -81,7 +82,7 @@ def test_mean_grad_full_and_rank_mode(oracle, mode, n, N):
             assert sr.item() == 0.0
 
 
-@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED])
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16])
 def test_step_from_mean_is_bit_identical_to_the_fused_step(oracle, mode):
     say(f"[case] step from mean == fused step, mode={mode}")
     wl = synth.scaled(BASE[mode], 300_007, weight_decay=0.1, decay="all")
@@ -102,7 +103,7 @@ def test_step_from_mean_is_bit_identical_to_the_fused_step(oracle, mode):
         z.zero_step_clipped(hp, p3, grads, s3, t, 1e30, ws_clip)
     torch.cuda.synchronize()
     for x, y, w in ((p1, p2, p3), (s1.m, s2.m, s3.m), (s1.v, s2.v, s3.v)):
-        bits = torch.int16 if x.dtype == torch.bfloat16 else (
+        bits = torch.int16 if x.dtype in (torch.bfloat16, torch.float16) else (
             torch.int64 if x.dtype == torch.float64 else torch.int32)
         assert torch.equal(x.view(bits), y.view(bits)) and torch.equal(x.view(bits), w.view(bits))
 
@@ -150,7 +151,7 @@ def _run_clipped(oracle, wl, steps, max_norm_of, full_compare=True):
     return clipped
 
 
-@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED])
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16])
 def test_clipped_steps_against_the_oracle(oracle, mode):
     wl = synth.scaled(BASE[mode], 500_009, weight_decay=0.05, decay="all")
     # threshold below the norm on odd steps (clipping), above on even ones

@@ -1,6 +1,6 @@
 """Seeded random configurations of the step against the oracle.
 
-Each case draws a mode, an optimizer (Adam/AdamW, or momentum SGD with or
+Each case draws a mode (fp64, fp32, bf16 or fp16 mixed precision), an optimizer (Adam/AdamW, or momentum SGD with or
 without dampening and Nesterov), n from 1 to ~3e5, N up to 256 (N > n included),
 full or rank mode, no decay / decay everywhere / a random per-element mask, a
 call path (one zero_step; buckets of zero_step_range in a random order;
@@ -19,12 +19,13 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
-from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
+from oracle import MIXED_MODES, MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from oracle.compare import compare  # noqa: E402
 from gpu_cases import host, say  # noqa: E402
 
 _PDT = {MODE_F64: np.float64, MODE_F32: np.float32}
-_SDT = {MODE_F64: torch.float64, MODE_F32: torch.float32, MODE_MIXED: torch.float32}
+_SDT = {MODE_F64: torch.float64, MODE_F32: torch.float32, MODE_MIXED: torch.float32,
+        MODE_MIXED_F16: torch.float32}
 
 
 def _bf16_bits(x):
@@ -32,21 +33,30 @@ def _bf16_bits(x):
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
+def _fp16_bits(x):
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def _half_bits(mode, x):
+    return _bf16_bits(x) if mode == MODE_MIXED else _fp16_bits(x)
+
+
 def _host_values(rng, mode, size, scale):
     x = scale * rng.standard_normal(size)
-    return _bf16_bits(x) if mode == MODE_MIXED else x.astype(_PDT[mode])
+    return _half_bits(mode, x) if mode in MIXED_MODES else x.astype(_PDT[mode])
 
 
 def _device(x, mode):
-    if mode == MODE_MIXED:
-        return torch.from_numpy(x.view(np.int16).copy()).view(torch.bfloat16).cuda()
+    if mode in MIXED_MODES:
+        dt = torch.bfloat16 if mode == MODE_MIXED else torch.float16
+        return torch.from_numpy(x.view(np.int16).copy()).view(dt).cuda()
     return torch.from_numpy(x.copy()).cuda()
 
 
 def _draw(seed):
     rng = np.random.default_rng(1000 + seed)
     c = dict(seed=seed)
-    c["mode"] = int(rng.choice([MODE_F64, MODE_F32, MODE_MIXED]))
+    c["mode"] = int(rng.choice([MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16]))
     c["sgd"] = bool(rng.random() < 0.35)
     c["n"] = int(np.exp(rng.uniform(0.0, np.log(300_000))))
     c["N"] = int(rng.choice([1, 2, 3, 4, 5, 7, 8, 9, 16, 33, 64, 100, 256]))
@@ -93,10 +103,10 @@ def test_random_configuration_matches_the_oracle(oracle, seed):
     sdt = _SDT[mode]
     npsdt = np.float64 if mode == MODE_F64 else np.float32
     p_h = _host_values(rng, mode, n, 0.5)
-    need_master = mode == MODE_MIXED or rank >= 0
+    need_master = mode in MIXED_MODES or rank >= 0
     if rank >= 0:  # the rank's master, and its slot as the rounding of it
         mst_h = (0.5 * rng.standard_normal(L)).astype(npsdt)
-        p_h[a:b] = _bf16_bits(mst_h) if mode == MODE_MIXED else mst_h.astype(_PDT[mode])
+        p_h[a:b] = _half_bits(mode, mst_h) if mode in MIXED_MODES else mst_h.astype(_PDT[mode])
     param = _device(p_h, mode)
     st = z.States(torch.empty(L, dtype=sdt, device="cuda") if need_master else None,
                   torch.empty(L, dtype=sdt, device="cuda"),
@@ -142,7 +152,7 @@ def test_random_configuration_matches_the_oracle(oracle, seed):
             o_p, o_mst, o_m, o_v = oracle.zero_step(mode, o_p, g_h, o_mst, o_m, o_v, t, lr, 0.9,
                                                     0.99, 1e-8, c["wd"], dec)
     torch.cuda.synchronize()
-    pk = "exact" if mode == MODE_F64 else ("bf16" if mode == MODE_MIXED else "f32")
+    pk = {MODE_F64: "exact", MODE_F32: "f32", MODE_MIXED: "bf16", MODE_MIXED_F16: "fp16"}[mode]
     sk = "exact" if mode == MODE_F64 else "f32"
     compare("param", host(param), o_p, pk)
     if not c["sgd"] or mom:

@@ -20,15 +20,16 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
-from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
+from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from gpu_cases import say, setup  # noqa: E402
 
 W = synth.WORKLOADS
-BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"]}
+BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"],
+        MODE_MIXED_F16: W["mixed-fp16-1B-n8"]}
 
 
 def _bits(x):
-    return x.view({torch.bfloat16: torch.int16, torch.float64: torch.int64,
+    return x.view({torch.bfloat16: torch.int16, torch.float16: torch.int16, torch.float64: torch.int64,
                    torch.float32: torch.int32}[x.dtype])
 
 
@@ -57,6 +58,7 @@ def _sgd(hp):
 CASES = {
     "fp64": (MODE_F64, -1, False), "fp32": (MODE_F32, -1, False),
     "mixed": (MODE_MIXED, -1, False), "mixed-rank3": (MODE_MIXED, 3, False),
+    "fp16": (MODE_MIXED_F16, -1, False), "fp16-rank5": (MODE_MIXED_F16, 5, False),
     "fp32-sgd": (MODE_F32, -1, True), "mixed-sgd": (MODE_MIXED, -1, True),
 }
 
@@ -90,7 +92,7 @@ def test_device_scalars_equal_the_eager_step(name):
         _same_state(p_ref, s_ref, p_dev, s_dev)
 
 
-@pytest.mark.parametrize("name", ["fp32", "mixed", "fp32-sgd", "mixed-rank3"])
+@pytest.mark.parametrize("name", ["fp32", "mixed", "fp32-sgd", "mixed-rank3", "fp16"])
 def test_captured_buckets_replay_for_later_steps(name):
     wl, hp, p_ref, s_ref, p_dev, s_dev = _pair(name)
     say(f"[case] graph of buckets, {name}")

@@ -17,7 +17,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
-from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
+from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from gpu_cases import host, run_full, run_sampled, say, setup  # noqa: E402
 
 W = synth.WORKLOADS
@@ -84,6 +84,11 @@ def test_mixed_n8_bf16(oracle, n):
     run_full(oracle, synth.scaled(W["mixed-1B-n8"], n), steps=5)
 
 
+@pytest.mark.parametrize("n", [2_000_003, 4096])
+def test_mixed_n8_fp16(oracle, n):
+    run_full(oracle, synth.scaled(W["mixed-fp16-1B-n8"], n), steps=5)
+
+
 @pytest.mark.parametrize("rank", [0, 3, 7])
 def test_mixed_rank_share_adamw(oracle, rank):
     """One rank's share: chunk gradients and shard-local master/m/v; ragged
@@ -92,7 +97,7 @@ def test_mixed_rank_share_adamw(oracle, rank):
     run_full(oracle, wl, steps=4)
 
 
-@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32])
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED_F16])
 def test_rank_share_other_modes(oracle, mode):
     base = W["fp32-320M-n8"]
     wl = synth.scaled(base, 5 * 100_003 + 3, rank=2, mode=mode, n_workers=5, weight_decay=0.05,
@@ -113,13 +118,14 @@ def test_gpt2_shaped_tensor_list_n64_decay_mask(oracle):
 
 
 # -- edge cases ---------------------------------------------------------------
-@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED])
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16])
 @pytest.mark.parametrize("n,N", [(1, 1), (3, 5), (7, 2), (9, 3), (17, 100), (1029, 256),
                                  (100_001, 64), (65_537, 6)])
 def test_edge_shapes(oracle, mode, n, N):
     """Tiny and ragged vectors, N > n (empty shards), N not a power of two, and
     the largest N the call accepts."""
-    base = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"]}[mode]
+    base = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"],
+            MODE_MIXED_F16: W["mixed-fp16-1B-n8"]}[mode]
     wl = synth.scaled(base, n, n_workers=N, worker_scale=None, zero_frac=0.0)
     run_full(oracle, wl, steps=3)
 
@@ -213,6 +219,10 @@ def test_full_size_fp32_320M_n8(oracle):
 
 def test_full_size_mixed_1B_n8(oracle):
     run_sampled(oracle, W["mixed-1B-n8"], steps=10, count=1 << 20, compare_steps=[1, 5])
+
+
+def test_full_size_mixed_fp16_1B_n8(oracle):
+    run_sampled(oracle, W["mixed-fp16-1B-n8"], steps=10, count=1 << 20, compare_steps=[1, 5])
 
 
 def test_full_size_rank0_share_of_8B(oracle):

@@ -11,12 +11,13 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
-from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
+from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from oracle.compare import compare  # noqa: E402
 from gpu_cases import host, kinds, say  # noqa: E402
 
 W = synth.WORKLOADS
-BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"]}
+BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"],
+        MODE_MIXED_F16: W["mixed-fp16-1B-n8"]}
 VARIANTS = {  # momentum, dampening, nesterov, weight decay
     "momentum": (0.9, 0.0, False, 0.0),
     "dampened+decay": (0.9, 0.1, False, 0.01),
@@ -30,7 +31,7 @@ def sgd_setup(wl, mom, damp, nest, wd, mask=None):
     a, b = wl.shard
     L = b - a
     sdt = synth.state_dtype(wl)
-    need_master = wl.mode == MODE_MIXED or wl.rank >= 0
+    need_master = wl.mode in (MODE_MIXED, MODE_MIXED_F16) or wl.rank >= 0
     st = z.States(torch.empty(L, dtype=sdt, device="cuda") if need_master else None,
                   torch.empty(L, dtype=sdt, device="cuda"), None)
     hp = z.HParams(n=wl.n, n_workers=wl.n_workers, mode=wl.mode, lr=wl.lr, beta1=0.0, beta2=0.0,
@@ -70,7 +71,7 @@ def run_sgd(oracle, wl, variant, steps):
     say("[done] " + "; ".join(f"{s['name']} bitexact {s['bitexact']}/{s['n']}" for s in out))
 
 
-@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED])
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16])
 @pytest.mark.parametrize("variant", sorted(VARIANTS))
 def test_sgd_full_mode(oracle, mode, variant):
     run_sgd(oracle, synth.scaled(BASE[mode], 1_000_003, decay="all", worker_scale=None), variant, 4)

@@ -13,7 +13,7 @@ if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
-from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
+from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from oracle.compare import compare  # noqa: E402
 from gpu_cases import host, say  # noqa: E402
 
@@ -29,13 +29,18 @@ def _bf16_bits(x):
     return t.view(torch.int16).numpy().view(np.uint16).copy()
 
 
-@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED])
+def _fp16_bits(x):
+    with np.errstate(over="ignore"):
+        return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16])
 def test_special_values_match_the_oracle(oracle, mode):
     say(f"[case] special values mode={mode}")
     rng = np.random.default_rng(31)
     n, N = 4099, 4
     fdt = np.float64 if mode == MODE_F64 else np.float32
-    sp = _specials(fdt)
+    sp = _specials(np.float16 if mode == MODE_MIXED_F16 else fdt).astype(fdt)
     grads = [(1e-3 * rng.standard_normal(n)).astype(fdt) for _ in range(N)]
     # plant special values in different workers at different places
     for k in range(N):
@@ -43,18 +48,20 @@ def test_special_values_match_the_oracle(oracle, mode):
         grads[k][pos] = np.tile(sp, 3)[: pos.size]
     w0 = rng.standard_normal(n).astype(fdt)
     w0[:sp.size] = sp  # special parameters too
-    if mode == MODE_MIXED:
-        p_h = _bf16_bits(w0)
-        g_h = [_bf16_bits(g) for g in grads]
-        tdt = torch.bfloat16
-        p_d = torch.from_numpy(p_h.view(np.int16)).view(tdt).cuda()
-        g_d = [torch.from_numpy(g.view(np.int16)).view(tdt).cuda() for g in g_h]
+    if mode in (MODE_MIXED, MODE_MIXED_F16):
+        bits = _bf16_bits if mode == MODE_MIXED else _fp16_bits
+        p_h = bits(w0)
+        g_h = [bits(g) for g in grads]
+        tdt = torch.bfloat16 if mode == MODE_MIXED else torch.float16
+        p_d = torch.from_numpy(p_h.view(np.int16).copy()).view(tdt).cuda()
+        g_d = [torch.from_numpy(g.view(np.int16).copy()).view(tdt).cuda() for g in g_h]
     else:
         p_h, g_h = w0, grads
         p_d = torch.from_numpy(w0.copy()).cuda()
         g_d = [torch.from_numpy(g.copy()).cuda() for g in grads]
     sdt = torch.float64 if mode == MODE_F64 else torch.float32
-    st = z.States(torch.empty(n, dtype=sdt, device="cuda") if mode == MODE_MIXED else None,
+    mixed = mode in (MODE_MIXED, MODE_MIXED_F16)
+    st = z.States(torch.empty(n, dtype=sdt, device="cuda") if mixed else None,
                   torch.empty(n, dtype=sdt, device="cuda"), torch.empty(n, dtype=sdt, device="cuda"))
     hp = z.HParams(n=n, n_workers=N, mode=mode, lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8,
                    weight_decay=0.1)
@@ -67,10 +74,10 @@ def test_special_values_match_the_oracle(oracle, mode):
     torch.cuda.synchronize()
     kind = "exact" if mode == MODE_F64 else "f32"
     got_p = host(p_d)
-    if mode == MODE_MIXED:
-        compare("param", got_p, p_h, "bf16")
+    if mixed:
+        compare("param", got_p, p_h, "bf16" if mode == MODE_MIXED else "fp16")
         nan_out = got_p[np.isnan(mst)]
-        assert nan_out.size > 0 and np.all(nan_out == 0x7FC0)
+        assert nan_out.size > 0 and np.all(nan_out == (0x7FC0 if mode == MODE_MIXED else 0x7E00))
         compare("master", host(st.master), mst, kind)
     else:
         compare("param", got_p, p_h, kind)
@@ -99,3 +106,40 @@ def test_subnormal_gradients_are_not_flushed(oracle):
     m = host(st.m)
     assert np.all(m > 0) and np.array_equal(m, ref[2])
     assert np.array_equal(host(p_d), ref[0])
+
+
+@pytest.mark.parametrize("case", ["overflow", "underflow"])
+def test_fp16_gathered_copy_overflows_and_underflows(oracle, case):
+    """fp16 mixed precision: masters pushed past 65504 give an fp16 infinity in the
+    gathered copy while the fp32 master stays finite; masters moved by tiny
+    steps near 3e-6 give fp16 subnormals; both as the oracle rounds them."""
+    say(f"[case] fp16 {case} of the gathered copy")
+    rng = np.random.default_rng(32)
+    n, N = 8192, 2
+    mag, lr = (65500.0, 16.0) if case == "overflow" else (3e-6, 1e-6)
+    w0 = (mag * np.where(rng.random(n) < 0.5, -1.0, 1.0)).astype(np.float32)
+    p_h = _fp16_bits(w0)
+    push = -np.sign(w0) if case == "overflow" else np.where(rng.random(n) < 0.5, -1.0, 1.0)
+    g_h = [_fp16_bits((push * 1e-2 * rng.random(n)).astype(np.float32)) for _ in range(N)]
+    p_d = torch.from_numpy(p_h.view(np.int16).copy()).view(torch.float16).cuda()
+    g_d = [torch.from_numpy(g.view(np.int16).copy()).view(torch.float16).cuda() for g in g_h]
+    st = z.States(torch.empty(n, device="cuda"), torch.empty(n, device="cuda"),
+                  torch.empty(n, device="cuda"))
+    hp = z.HParams(n=n, n_workers=N, mode=MODE_MIXED_F16, lr=lr, beta1=0.9, beta2=0.999, eps=1e-8)
+    z.zero_init_states(hp, p_d, st)
+    mst, m, v = oracle.init_states(MODE_MIXED_F16, p_h)
+    for t in (1, 2):
+        z.zero_step(hp, p_d, g_d, st, t)
+        p_h, mst, m, v = oracle.zero_step(MODE_MIXED_F16, p_h, g_h, mst, m, v, t, lr, 0.9, 0.999,
+                                          1e-8)
+    torch.cuda.synchronize()
+    got = host(p_d)
+    compare("param", got, p_h, "fp16")
+    compare("master", host(st.master), mst, "f32")
+    assert np.all(np.isfinite(mst))
+    if case == "overflow":
+        assert np.all((p_h & 0x7FFF) == 0x7C00)  # every gathered value is an infinity
+    else:
+        sub = ((p_h & 0x7C00) == 0) & ((p_h & 0x3FF) != 0)
+        assert sub.mean() > 0.9  # fp16 subnormals
+    assert np.array_equal(got, p_h)

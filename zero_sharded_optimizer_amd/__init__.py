@@ -39,14 +39,16 @@ import numpy as np
 
 from . import _abi
 from ._abi import (ZERO_EHIP, ZERO_EINVAL, ZERO_EUNSUPPORTED, ZERO_MAX_WORKERS,  # noqa: F401
-                   ZERO_MODE_F32, ZERO_MODE_F64, ZERO_MODE_MIXED_BF16, ZERO_OK, ZERO_OPT_ADAM,
+                   ZERO_MODE_F32, ZERO_MODE_F64, ZERO_MODE_MIXED_BF16, ZERO_MODE_MIXED_F16, ZERO_OK,
+                   ZERO_OPT_ADAM,
                    ZERO_OPT_SGD)
 
 __all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
            "zero_memory_bytes", "zero_shard_bounds", "zero_last_error", "wd_mask_from_flags",
            "zero_mean_grad_workspace_bytes", "zero_mean_grad", "zero_step_mean",
            "zero_step_clipped_workspace_bytes", "zero_step_clipped", "zero_step_range",
-           "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MAX_WORKERS",
+           "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MODE_MIXED_F16",
+           "ZERO_MAX_WORKERS",
            "ZERO_OPT_ADAM", "ZERO_OPT_SGD", "zero_step_scalars", "zero_step_range_dev",
            "STEP_SCALARS_BYTES"]
 
@@ -104,6 +106,7 @@ _DTYPES = {
     ZERO_MODE_F64: ("float64", "float64", "float64"),
     ZERO_MODE_F32: ("float32", "float32", "float32"),
     ZERO_MODE_MIXED_BF16: ("bfloat16", "bfloat16", "float32"),
+    ZERO_MODE_MIXED_F16: ("float16", "float16", "float32"),
 }
 
 

@@ -17,6 +17,7 @@ ZERO_EHIP = -3
 ZERO_MODE_F64 = 0
 ZERO_MODE_F32 = 1
 ZERO_MODE_MIXED_BF16 = 2
+ZERO_MODE_MIXED_F16 = 3
 
 ZERO_OPT_ADAM = 0
 ZERO_OPT_SGD = 1

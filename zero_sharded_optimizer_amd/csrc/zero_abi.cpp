@@ -59,6 +59,7 @@ bool mode_widths(int32_t mode, Widths* w) {
     case ZERO_MODE_F64: *w = {8, 8, 8, 16}; return true;
     case ZERO_MODE_F32: *w = {4, 4, 4, 8}; return true;
     case ZERO_MODE_MIXED_BF16: *w = {2, 2, 4, 12}; return true;
+    case ZERO_MODE_MIXED_F16: *w = {2, 2, 4, 12}; return true;
     default: return false;
   }
 }
@@ -73,6 +74,11 @@ bool overlaps(const Range& x, const Range& y) {
 }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// bf16 or fp16 parameters and gradients with a separate fp32 master
+bool mixed_mode(int32_t mode) {
+  return mode == ZERO_MODE_MIXED_BF16 || mode == ZERO_MODE_MIXED_F16;
+}
 
 // Shared checks of zero_hparams. On success fills the shard range this call
 // covers ([a, b): the whole vector in full mode, worker `rank`'s shard in rank
@@ -129,7 +135,7 @@ zero_status check_states(const zero_hparams* hp, const zero_states* st, const Wi
   if (st->v == nullptr && !sgd) return fail(ZERO_EINVAL, "states.v is NULL");
   if (!aligned(st->m, 16) || (st->v != nullptr && !aligned(st->v, 16)))
     return fail(ZERO_EINVAL, "states.m and states.v must be 16-byte aligned");
-  const bool need_master = hp->mode == ZERO_MODE_MIXED_BF16 || hp->rank >= 0;
+  const bool need_master = mixed_mode(hp->mode) || hp->rank >= 0;
   if (need_master && st->master == nullptr)
     return fail(ZERO_EINVAL, "states.master is required in mixed mode and in rank mode");
   if (!need_master && st->master != nullptr)
@@ -175,8 +181,8 @@ zero_status zero_memory_bytes(int64_t n, int32_t n_workers, int32_t rank, int32_
     out->grads = w.grad * (stage >= 2 ? c : n);
     out->optimizer = w.optimizer * (stage >= 1 ? c : n);
   } else if (convention == 1) {
-    if (mode == ZERO_MODE_MIXED_BF16)
-      return fail(ZERO_EUNSUPPORTED, "convention 1 counts one value width; not for mixed mode");
+    if (mixed_mode(mode))
+      return fail(ZERO_EUNSUPPORTED, "convention 1 counts one value width; not for mixed modes");
     const int64_t B = w.param;
     switch (stage) {
       case 0: out->params = B * n; out->grads = B * n; out->optimizer = 2 * B * n; break;
@@ -296,7 +302,7 @@ zero_status build_step(const zero_hparams* hp, void* param, const void* const* g
   for (int k = 0; k < ngp; ++k) la->grads[k] = grads[k];
   la->m = st->m;
   la->v = st->v;
-  if (rank_mode || hp->mode == ZERO_MODE_MIXED_BF16) {
+  if (rank_mode || mixed_mode(hp->mode)) {
     la->w = st->master;
     la->out = static_cast<char*>(param) + a * wd.param;
   } else {

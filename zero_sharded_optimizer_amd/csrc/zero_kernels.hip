@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
 
 #include "zero_launch.h"
 
@@ -186,9 +187,24 @@ struct ModeMixed {
   static constexpr int VEC = 4;
 };
 
+// fp16 mixed precision: fp16 gradients and gathered parameters (bit patterns),
+// fp32 master, m and v; the same 8-byte gradient groups as bf16.
+struct ModeMixedF16 {
+  typedef float S;
+  typedef _Float16 G;
+  typedef uint16_t P;
+  static constexpr int VEC = 4;
+};
+
 // The step driven by a materialised fp32 mean gradient in mixed precision:
-// fp32 "gradient" groups, fp32 state, bf16 write-back.
+// fp32 "gradient" groups, fp32 state, bf16 (or fp16) write-back.
 struct ModeMixedMean {
+  typedef float S;
+  typedef float G;
+  typedef uint16_t P;
+  static constexpr int VEC = 4;
+};
+struct ModeMixedF16Mean {
   typedef float S;
   typedef float G;
   typedef uint16_t P;
@@ -205,6 +221,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
   u += 0x7FFFu + ((u >> 16) & 1u);
   return u >> 16;
+}
+
+// fp16 <-> fp32 by the hardware conversions: widening is exact; narrowing
+// rounds to nearest even, keeps fp16 subnormals and overflows to infinity. NaN
+// becomes the quiet NaN 0x7E00.
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+__device__ __forceinline__ uint32_t f32_to_f16(float x) {
+  if (x != x) return 0x7E00u;
+  return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
 // Raw gradient group (16 or 8 bytes) and its widening into S.
@@ -259,7 +286,29 @@ struct GradRaw<ModeMixed> {
 };
 
 template <>
+struct GradRaw<ModeMixedF16> {
+  u32x2 r;
+  __device__ __forceinline__ void load(const void* base, int64_t g) {
+    r = ld_stream(reinterpret_cast<const u32x2*>(base) + g);
+  }
+  __device__ __forceinline__ float elem(int e) const {
+    const uint32_t w = r[e >> 1];
+    return f16_to_f32((e & 1) ? (w >> 16) : (w & 0xFFFFu));
+  }
+  __device__ __forceinline__ void widen(float (&s)[4]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = elem(e);
+  }
+  __device__ __forceinline__ void add(float (&s)[4]) const {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s[e] = s[e] + elem(e);
+  }
+};
+
+template <>
 struct GradRaw<ModeMixedMean> : GradRaw<ModeF32> {};
+template <>
+struct GradRaw<ModeMixedF16Mean> : GradRaw<ModeF32> {};
 
 // State group (VEC elements of S) load / store.
 template <class M>
@@ -292,6 +341,10 @@ template <>
 struct StateIO<ModeMixed> : StateIO<ModeF32> {};
 template <>
 struct StateIO<ModeMixedMean> : StateIO<ModeF32> {};
+template <>
+struct StateIO<ModeMixedF16> : StateIO<ModeF32> {};
+template <>
+struct StateIO<ModeMixedF16Mean> : StateIO<ModeF32> {};
 
 // Gathered-parameter write-back of a group to a destination aligned to kAlign.
 template <class M>
@@ -325,13 +378,28 @@ struct OutIO<ModeMixed> {
 };
 
 template <>
+struct OutIO<ModeMixedF16> {
+  static constexpr int kAlign = 8;
+  __device__ __forceinline__ static void store_vec(uint16_t* p, int64_t g, const float (&x)[4]) {
+    u32x2 r;
+    r.x = f32_to_f16(x[0]) | (f32_to_f16(x[1]) << 16);
+    r.y = f32_to_f16(x[2]) | (f32_to_f16(x[3]) << 16);
+    st_stream(reinterpret_cast<u32x2*>(p) + g, r);
+  }
+  __device__ __forceinline__ static uint16_t conv(float x) { return (uint16_t)f32_to_f16(x); }
+};
+
+template <>
 struct OutIO<ModeMixedMean> : OutIO<ModeMixed> {};
+template <>
+struct OutIO<ModeMixedF16Mean> : OutIO<ModeMixedF16> {};
 
 __device__ __forceinline__ float sqrt_rn(float x) { return __builtin_sqrtf(x); }
 __device__ __forceinline__ double sqrt_rn(double x) { return __builtin_sqrt(x); }
 
 __device__ __forceinline__ double grad_elem(const double* p, int64_t i) { return p[i]; }
 __device__ __forceinline__ float grad_elem(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float grad_elem(const _Float16* p, int64_t i) { return (float)p[i]; }
 __device__ __forceinline__ float grad_elem(const uint16_t* p, int64_t i) {
   return bf16_to_f32(p[i]);
 }
@@ -715,7 +783,9 @@ __global__ void __launch_bounds__(kInitBlock)
     m[i] = S(0);
     if (v != nullptr) v[i] = S(0);
     if (master != nullptr) {
-      if constexpr (sizeof(typename M::P) == 2)
+      if constexpr (std::is_same_v<M, ModeMixedF16>)
+        master[i] = f16_to_f32(param[i]);
+      else if constexpr (sizeof(typename M::P) == 2)
         master[i] = bf16_to_f32(param[i]);
       else
         master[i] = param[i];
@@ -777,6 +847,8 @@ struct Shape<ModeMixed> {
   static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
   static constexpr bool PRE = ZERO_MIX_PRELOAD, WC = ZERO_MIX_WC;
 };
+template <>
+struct Shape<ModeMixedF16> : Shape<ModeMixed> {};
 // the step kernel's shape for NFIX fixed workers (0: any N)
 template <class M, int NFIX>
 struct StepShape : Shape<M> {};
@@ -838,6 +910,8 @@ struct Shape<ModeMixedMean> {
   static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
   static constexpr bool PRE = ZERO_MIX_PRELOAD, WC = ZERO_MIX_WC;
 };
+template <>
+struct Shape<ModeMixedF16Mean> : Shape<ModeMixedMean> {};
 
 template <class M>
 int64_t mean_blocks(int64_t len) {
@@ -898,6 +972,7 @@ const char* launch_step(const StepArgs& a, void* stream) {
     case 0: launch_mode<ModeF64>(a, st); break;
     case 1: launch_mode<ModeF32>(a, st); break;
     case 2: launch_mode<ModeMixed>(a, st); break;
+    case 3: launch_mode<ModeMixedF16>(a, st); break;
     default: return "unknown mode";
   }
   const hipError_t e = hipGetLastError();
@@ -911,6 +986,7 @@ const char* launch_step_mean(const StepArgs& a, void* stream) {
     case 0: launch_mode_n<ModeF64, 1, 1>(a, st); break;
     case 1: launch_mode_n<ModeF32, 1, 1>(a, st); break;
     case 2: launch_mode_n<ModeMixedMean, 1, 1>(a, st); break;
+    case 3: launch_mode_n<ModeMixedF16Mean, 1, 1>(a, st); break;
     default: return "unknown mode";
   }
   const hipError_t e = hipGetLastError();
@@ -921,6 +997,7 @@ int64_t mean_partials(int mode, int64_t len) {
   switch (mode) {
     case 0: return mean_blocks<ModeF64>(len);
     case 1: return mean_blocks<ModeF32>(len);
+    case 3: return mean_blocks<ModeMixedF16>(len);
     default: return mean_blocks<ModeMixed>(len);
   }
 }
@@ -932,6 +1009,7 @@ const char* launch_mean(const MeanArgs& a, void* stream) {
     case 0: launch_mean_mode<ModeF64>(a, st); break;
     case 1: launch_mean_mode<ModeF32>(a, st); break;
     case 2: launch_mean_mode<ModeMixed>(a, st); break;
+    case 3: launch_mean_mode<ModeMixedF16>(a, st); break;
     default: return "unknown mode";
   }
   const hipError_t e = hipGetLastError();
@@ -945,6 +1023,7 @@ const char* launch_init(const InitArgs& a, void* stream) {
     case 0: launch_init_mode<ModeF64>(a, st); break;
     case 1: launch_init_mode<ModeF32>(a, st); break;
     case 2: launch_init_mode<ModeMixed>(a, st); break;
+    case 3: launch_init_mode<ModeMixedF16>(a, st); break;
     default: return "unknown mode";
   }
   const hipError_t e = hipGetLastError();

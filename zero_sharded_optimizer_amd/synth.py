@@ -15,7 +15,7 @@ from typing import List, Optional, Tuple
 
 import numpy as np
 
-MODE_F64, MODE_F32, MODE_MIXED = 0, 1, 2
+MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16 = 0, 1, 2, 3
 
 
 @dataclass(frozen=True)
@@ -92,6 +92,9 @@ WORKLOADS = {
     "mixed-rank0-of-8B-n8": Workload(
         "mixed-rank0-of-8B-n8", MODE_MIXED, 8_000_000_000, 8, 3e-4, 0.9, 0.95, 1e-8, 0.1, 5,
         param_std=0.02, grad_std=1e-3, rank=0, decay="all", seed=20260004),
+    "mixed-fp16-1B-n8": Workload(
+        "mixed-fp16-1B-n8", MODE_MIXED_F16, 1_000_000_000, 8, 1e-4, 0.9, 0.95, 1e-8, 0.0, 10,
+        param_std=0.02, grad_std=1e-3, zero_frac=0.01, seed=20260006),
     "gpt2s-fp32-n64": Workload(
         "gpt2s-fp32-n64", MODE_F32, tensor_starts(_GPT2)[1], 64, 3e-4, 0.9, 0.95, 1e-8, 0.1,
         100, param_std=0.02, grad_std=1e-3, decay="2d", shapes=_GPT2, seed=20260005),
@@ -155,7 +158,8 @@ def _normal(n, std, device, gen, dtype):
 
 def param_dtype(wl):
     torch = _torch()
-    return {MODE_F64: torch.float64, MODE_F32: torch.float32, MODE_MIXED: torch.bfloat16}[wl.mode]
+    return {MODE_F64: torch.float64, MODE_F32: torch.float32, MODE_MIXED: torch.bfloat16,
+            MODE_MIXED_F16: torch.float16}[wl.mode]
 
 
 def state_dtype(wl):
