@@ -6,9 +6,10 @@
  *
  *   zero_c_consumer host   host-only checks of the ABI (no device call)
  *   zero_c_consumer gpu    init_states and three fused steps in fp64 (N = 3),
- *                          fp32 (N = 8) and mixed precision (N = 4), compared
- *                          with the oracle: fp64 bit-exact, fp32 within
- *                          1e-6 * max(1, |ref|), bf16 within 1 ulp.
+ *                          fp32 (N = 8), bf16 mixed precision (N = 4) and fp16
+ *                          mixed precision (N = 5), compared with the oracle:
+ *                          fp64 bit-exact, fp32 within 1e-6 * max(1, |ref|),
+ *                          bf16 and fp16 within 1 ulp.
  * Exit status 0 when every check holds.
  */
 #include <hip/hip_runtime_api.h>
@@ -58,6 +59,14 @@ static uint16_t random_bf16(int e_lo, int e_hi) {
   const uint16_t sign = (uint16_t)((r >> 63) << 15);
   const uint16_t exp = (uint16_t)(e_lo + (int)((r >> 8) % (uint64_t)(e_hi - e_lo + 1)));
   return (uint16_t)(sign | (uint16_t)(exp << 7) | (uint16_t)(r & 0x7F));
+}
+
+/* a random fp16 bit pattern with exponent field in [e_lo, e_hi] */
+static uint16_t random_fp16(int e_lo, int e_hi) {
+  const uint64_t r = next_u64();
+  const uint16_t sign = (uint16_t)((r >> 63) << 15);
+  const uint16_t exp = (uint16_t)(e_lo + (int)((r >> 12) % (uint64_t)(e_hi - e_lo + 1)));
+  return (uint16_t)(sign | (uint16_t)(exp << 10) | (uint16_t)(r & 0x3FF));
 }
 
 static int host_checks(void) {
@@ -118,7 +127,7 @@ static int64_t compare(const char* what, int kind, const void* got, const void* 
 
 static void run_mode(int mode, int64_t n, int N) {
   const size_t G = elem_size(mode), S = state_size(mode);
-  const int mixed = mode == ZERO_MODE_MIXED_BF16;
+  const int mixed = mode == ZERO_MODE_MIXED_BF16 || mode == ZERO_MODE_MIXED_F16;
   printf("[case] mode %d n %lld N %d\n", mode, (long long)n, N);
   fflush(stdout);
   /* host inputs */
@@ -128,7 +137,8 @@ static void run_mode(int mode, int64_t n, int N) {
   for (int64_t i = 0; i < n; ++i) {
     if (mode == ZERO_MODE_F64) ((double*)p_h)[i] = uniform() - 0.5;
     else if (mode == ZERO_MODE_F32) ((float*)p_h)[i] = (float)(0.04 * (uniform() - 0.5));
-    else ((uint16_t*)p_h)[i] = random_bf16(115, 124);
+    else if (mode == ZERO_MODE_MIXED_BF16) ((uint16_t*)p_h)[i] = random_bf16(115, 124);
+    else ((uint16_t*)p_h)[i] = random_fp16(5, 12); /* 2^-10 .. 2^-3 */
   }
   /* device buffers */
   void *p_d, *m_d, *v_d, *ms_d = NULL, *g_d[8];
@@ -167,7 +177,8 @@ static void run_mode(int mode, int64_t n, int N) {
       for (int64_t i = 0; i < n; ++i) {
         if (mode == ZERO_MODE_F64) ((double*)g_h[k])[i] = 2.0 * (uniform() - 0.5);
         else if (mode == ZERO_MODE_F32) ((float*)g_h[k])[i] = (float)(2e-3 * (uniform() - 0.5));
-        else ((uint16_t*)g_h[k])[i] = random_bf16(110, 121);
+        else if (mode == ZERO_MODE_MIXED_BF16) ((uint16_t*)g_h[k])[i] = random_bf16(110, 121);
+        else ((uint16_t*)g_h[k])[i] = random_fp16(1, 9); /* 2^-14 .. 2^-6 */
       }
       HIP(hipMemcpy(g_d[k], g_h[k], n * G, hipMemcpyHostToDevice));
     }
@@ -225,6 +236,7 @@ int main(int argc, char** argv) {
   run_mode(ZERO_MODE_F64, 100003, 3);
   run_mode(ZERO_MODE_F32, 65539, 8);
   run_mode(ZERO_MODE_MIXED_BF16, 40009, 4);
+  run_mode(ZERO_MODE_MIXED_F16, 30011, 5);
   printf("gpu run: %d failures\n", g_fail);
   return g_fail == 0 ? 0 : 1;
 }
