@@ -316,6 +316,16 @@ typedef struct {
 zero_status zero_memory_bytes(int64_t n, int32_t n_workers, int32_t rank, int32_t stage,
                               int32_t mode, int32_t convention, zero_mem* out);
 
+/* The smallest ZeRO stage that fits ("Data parallelism and ZeRO optimization",
+ * section "When to Use Each ZeRO Stage": the minimum stage whose memory need is
+ * below the memory available). For stage s in 0, 1, 2, 3 the need is
+ * zero_memory_bytes(n, N, 0, s, mode, 0).total (rank 0 holds the largest shard)
+ * plus activation_bytes; *stage is the first s whose need is < available_bytes,
+ * or -1 when none is. Host-only. Errors: ZERO_EINVAL for n < 1, N < 1, an
+ * unknown mode, a negative byte count or a NULL stage. */
+zero_status zero_min_stage(int64_t n, int32_t n_workers, int32_t mode, int64_t activation_bytes,
+                           int64_t available_bytes, int32_t* stage);
+
 /* Shard r of np.array_split(np.arange(n), N) as the half-open range
  * [*begin, *end) ("ZeRO-Sharded Adam Step", section "The shards"): the first
  * n mod N shards hold floor(n/N) + 1 indices, the rest floor(n/N). Host-only.

@@ -72,6 +72,8 @@ class Oracle:
         lib.orc_memory_bytes.argtypes = [_i64, _i64, _i64, _i32, _i64, _i64, _i64, _i32,
                                          C.POINTER(_i64)]
         lib.orc_memory_bytes.restype = _i32
+        lib.orc_min_stage.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64]
+        lib.orc_min_stage.restype = _i32
 
     @property
     def mutant(self):
@@ -267,6 +269,10 @@ class Oracle:
         return self.lib.orc_clip_factor(float(sumsq), float(max_norm))
 
     # -- memory ---------------------------------------------------------------
+    def min_stage(self, n, N, P, G, K, activation_bytes, available_bytes):
+        """The smallest ZeRO stage whose memory need fits, or -1."""
+        return self.lib.orc_min_stage(n, N, P, G, K, activation_bytes, available_bytes)
+
     def memory_bytes(self, n, N, r, stage, P, G, K, convention=0):
         out = (_i64 * 3)()
         rc = self.lib.orc_memory_bytes(n, N, r, stage, P, G, K, convention, out)

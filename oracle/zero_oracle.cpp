@@ -888,4 +888,17 @@ int orc_memory_bytes(int64_t n, int64_t N, int64_t r, int stage, int64_t P,
   return -1;
 }
 
+// The smallest stage whose memory need (convention 0, rank 0, plus the
+// activations) is below the memory available ("Data parallelism and ZeRO
+// optimization", section "When to Use Each ZeRO Stage"); -1 if none is.
+int orc_min_stage(int64_t n, int64_t N, int64_t P, int64_t G, int64_t K, int64_t act,
+                  int64_t avail) {
+  for (int stage = 0; stage <= 3; ++stage) {
+    int64_t out[3];
+    if (orc_memory_bytes(n, N, 0, stage, P, G, K, 0, out) != 0) return -2;
+    if (out[0] + out[1] + out[2] + act < avail) return stage;
+  }
+  return -1;
+}
+
 }  // extern "C"

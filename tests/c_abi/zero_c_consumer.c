@@ -76,6 +76,9 @@ static int host_checks(void) {
   zero_mem mem;
   CHECK(zero_memory_bytes(8000000000LL, 64, 0, 3, ZERO_MODE_MIXED_BF16, 0, &mem) == ZERO_OK);
   CHECK(mem.total == 16 * 125000000LL);
+  int32_t stage = 0;
+  CHECK(zero_min_stage(20000000000LL, 8, ZERO_MODE_MIXED_F16, 10000000000LL, 80000000000LL,
+                       &stage) == ZERO_OK && stage == 3);
   CHECK(zero_step(NULL, NULL, NULL, NULL, 1, NULL) == ZERO_EINVAL);
   CHECK(strlen(zero_last_error()) > 0);
   zero_hparams hp;

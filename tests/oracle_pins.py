@@ -499,6 +499,13 @@ def pin_memory_closed_forms(O):
             for s in range(4)]
     assert need == c["gb"], need
     assert [x < 80 for x in need] == c["fits_80gb"]
+    # the decision rule: the smallest stage that fits is ZeRO-3 here
+    assert O.min_stage(c["psi"], c["n_gpus"], P, G, K, int(c["activations_gb"] * 1e9),
+                       int(80e9)) == c["fits_80gb"].index(True)
+    assert O.min_stage(c["psi"], c["n_gpus"], P, G, K, int(c["activations_gb"] * 1e9),
+                       int(331e9)) == 0  # 330 GB < 331 GB: plain data parallelism fits
+    assert O.min_stage(c["psi"], c["n_gpus"], P, G, K, int(c["activations_gb"] * 1e9),
+                       int(50e9)) == -1  # 50 GB is not below 50 GB: nothing fits
     # 320M parameters in fp32: 5.12 GB
     c = cases[6]
     assert O.memory_bytes(c["psi"], 1, 0, 0, *WIDTHS["f32"])["total"] == int(c["gb"] * 1e9)

@@ -70,6 +70,11 @@ int main() {
       CHECK(m.total == m.params + m.grads + m.optimizer);
     }
   CHECK(zero_memory_bytes(10, 4, 0, 4, 0, 0, &m) == ZERO_EINVAL);
+  int32_t stage = 9;
+  CHECK(zero_min_stage(20000000000LL, 8, ZERO_MODE_MIXED_BF16, 10000000000LL, 80000000000LL,
+                       &stage) == ZERO_OK && stage == 3);
+  CHECK(zero_min_stage(10, 8, ZERO_MODE_F32, 0, 0, &stage) == ZERO_OK && stage == -1);
+  CHECK(zero_min_stage(10, 8, ZERO_MODE_F32, 0, 10, nullptr) == ZERO_EINVAL);
 
   // step validation with fake, aligned, non-overlapping addresses
   const uintptr_t A = (uintptr_t)1 << 32;

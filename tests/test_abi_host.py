@@ -386,3 +386,26 @@ def test_input_recipe_shard_matches_numpy_array_split():
             for r in range(N):
                 a, b = replace(base, n=n, n_workers=N, rank=r).shard
                 assert (a, b) == (starts[r], starts[r] + sizes[r])
+
+
+def test_min_stage_agrees_with_the_oracle_and_the_page(oracle):
+    """The smallest ZeRO stage that fits: the page's 20B example (8 GPUs, 10 GB of
+    activations, 80 GB each) needs ZeRO-3; random cases agree with the oracle."""
+    import json
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "memory_closed_forms.json")))
+    c = g["cases"][5]
+    act = int(c["activations_gb"] * 1e9)
+    assert z.zero_min_stage(c["psi"], c["n_gpus"], z.ZERO_MODE_MIXED_BF16, act, int(80e9)) == 3
+    assert z.zero_min_stage(c["psi"], c["n_gpus"], z.ZERO_MODE_MIXED_F16, act, int(120e9)) == 2
+    rng = np.random.default_rng(5)
+    for _ in range(2000):
+        n = int(rng.integers(1, 10 ** 12))
+        N = int(rng.integers(1, 129))
+        mode = int(rng.integers(0, 4))
+        act = int(rng.integers(0, 10 ** 11))
+        avail = int(rng.integers(0, 4 * 10 ** 12))
+        P, G, K = WIDTH[mode]
+        assert z.zero_min_stage(n, N, mode, act, avail) == oracle.min_stage(n, N, P, G, K, act, avail)
+    for bad in ((0, 8, 1, 0, 10), (10, 0, 1, 0, 10), (10, 8, 9, 0, 10), (10, 8, 1, -1, 10)):
+        with pytest.raises(z.ZeroError):
+            z.zero_min_stage(*bad)

@@ -29,6 +29,7 @@ workers sharing one GPU:
                                             read from device memory (for launches
                                             captured into a graph and replayed)
   zero_memory_bytes(...)                 -> per-rank memory by ZeRO stage
+  zero_min_stage(n, N, mode, act, avail) -> the smallest stage that fits
   zero_shard_bounds(n, N, r)             -> np.array_split shard [a, b)
 """
 import ctypes as C
@@ -50,7 +51,7 @@ __all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
            "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MODE_MIXED_F16",
            "ZERO_MAX_WORKERS",
            "ZERO_OPT_ADAM", "ZERO_OPT_SGD", "zero_step_scalars", "zero_step_range_dev",
-           "STEP_SCALARS_BYTES"]
+           "STEP_SCALARS_BYTES", "zero_min_stage", "ZERO_MODE_MIXED_F16"]
 
 
 class ZeroError(RuntimeError):
@@ -383,6 +384,19 @@ def zero_memory_bytes(n: int, n_workers: int, rank: int, stage: int, mode: int,
         _raise(st)
     return {"params": out.params, "grads": out.grads, "optimizer": out.optimizer,
             "total": out.total}
+
+
+def zero_min_stage(n: int, n_workers: int, mode: int, activation_bytes: int,
+                   available_bytes: int) -> int:
+    """The smallest ZeRO stage whose per-rank memory plus activation_bytes is
+    below available_bytes, or -1 if none is (see zero_adam.h)."""
+    lib = _abi.load()
+    out = C.c_int32()
+    st = lib.zero_min_stage(n, n_workers, mode, activation_bytes, available_bytes,
+                            C.byref(out))
+    if st != ZERO_OK:
+        _raise(st)
+    return out.value
 
 
 def zero_shard_bounds(n: int, n_workers: int, r: int):

@@ -197,6 +197,24 @@ zero_status zero_memory_bytes(int64_t n, int32_t n_workers, int32_t rank, int32_
   return ok();
 }
 
+zero_status zero_min_stage(int64_t n, int32_t n_workers, int32_t mode, int64_t activation_bytes,
+                           int64_t available_bytes, int32_t* stage) {
+  if (stage == nullptr) return fail(ZERO_EINVAL, "stage is NULL");
+  if (activation_bytes < 0 || available_bytes < 0)
+    return fail(ZERO_EINVAL, "byte counts must be >= 0");
+  *stage = -1;
+  for (int32_t s = 0; s <= 3; ++s) {
+    zero_mem m;
+    const zero_status st = zero_memory_bytes(n, n_workers, 0, s, mode, 0, &m);
+    if (st != ZERO_OK) return st;
+    if (m.total + activation_bytes < available_bytes) {
+      *stage = s;
+      break;
+    }
+  }
+  return ok();
+}
+
 zero_status zero_init_states(const zero_hparams* hp, const void* param, const zero_states* st,
                              void* stream) {
   Widths wd;
