@@ -386,6 +386,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--native-buckets", action="store_true",
+                    help="with --bucket-mib: enqueue all buckets in one zero_step_buckets call")
     ap.add_argument("--graph", action="store_true",
                     help="with --bucket-mib: capture the buckets once into a HIP graph "
                          "(zero_step_range_dev, step scalars in device memory) and replay it "
@@ -494,6 +496,8 @@ def main():
             k = z.STEP_SCALARS_BYTES
             scal.copy_(scal_all[(t - 1) * k:t * k])
             graph.replay()
+        elif buckets is not None and args.native_buckets:
+            z.zero_step_buckets(hp, param, grads, st, t, buckets, stream=stream)
         elif buckets is not None:
             for lo, hi in buckets:
                 z.zero_step_range(hp, param, grads, st, t, lo, hi, stream=stream)
@@ -557,7 +561,9 @@ def main():
                       {"clipped": True, "clip_fraction": args.clip, "max_norm": max_norm}),
                    **({} if buckets is None else
                       {"bucket_mib": args.bucket_mib, "buckets": len(buckets)}),
-                   **({"graph": True} if graph is not None else {})},
+                   **({"graph": True} if graph is not None else {}),
+                   **({"native_buckets": True} if buckets is not None and args.native_buckets
+                      else {})},
         "achieved_GBps": achieved,
         "kernel_ms_mean": avg_ms,
         "kernel_ms_median": sorted(kern_ms)[len(kern_ms) // 2],

@@ -195,6 +195,24 @@ zero_status zero_step_range(const zero_hparams* hp, void* param, const void* con
                             const zero_states* states, int64_t t, int64_t begin, int64_t end,
                             void* stream);
 
+/* The bucketed step in one call: for i = 0 .. nbuckets-1 in that order, bucket
+ * i covers [edges[2i], edges[2i+1]) of the call's index space (the begin a
+ * multiple of 8, as for zero_step_range) and, when ready_events is non-NULL and
+ * ready_events[i] (a hipEvent_t) is non-NULL, is launched on `stream` only after
+ * that event completes. This is the overlap of the step with backward ("Data
+ * Parallelism & ZeRO", section "Data parallelism, and why the obvious
+ * implementation is bad": gradients reduced in ~25 MB buckets while backward
+ * runs): the producer records one event per bucket as its gradients land, and
+ * the step of each bucket starts as soon as they have, with no host round trip
+ * per bucket. Buckets should be disjoint; the result for each element is then
+ * bit for bit that of zero_step. Every argument and every bucket is validated
+ * before anything is enqueued; an invalid bucket enqueues nothing. Errors as
+ * zero_step_range, plus ZERO_EINVAL for nbuckets < 0 or NULL edges;
+ * ZERO_EHIP if a wait or launch fails (buckets before it stay enqueued). */
+zero_status zero_step_buckets(const zero_hparams* hp, void* param, const void* const* grads,
+                              const zero_states* states, int64_t t, const int64_t* edges,
+                              int32_t nbuckets, void* const* ready_events, void* stream);
+
 /* ---- Step scalars in device memory, for captured launches -----------------
  * zero_step and zero_step_range bake the step-dependent scalars (1 - b1^t,
  * 1 - b2^t, and for SGD whether t == 1) into the launch. A launch captured

@@ -20,6 +20,7 @@ const char* launch_init(const InitArgs&, void*) { ++g_launches; return nullptr; 
 const char* launch_step_mean(const StepArgs&, void*) { ++g_launches; return nullptr; }
 const char* launch_mean(const MeanArgs&, void*) { ++g_launches; return nullptr; }
 int64_t mean_partials(int, int64_t len) { return len / 1024 + 1; }
+const char* stream_wait(void*, void*) { ++g_launches; return nullptr; }
 }  // namespace zlaunch
 
 static int g_fail = 0;
@@ -102,6 +103,19 @@ int main() {
   const zero_step_scalars* dsc = (const zero_step_scalars*)(A + ((uintptr_t)400 << 24));
   CHECK(zero_step_range_dev(&h, (void*)A, grads, &stm, dsc, 8, 800, nullptr) == ZERO_OK);
   CHECK(zero_step_range_dev(&h, (void*)A, grads, &stm, nullptr, 8, 800, nullptr) == ZERO_EINVAL);
+  // buckets in one call, with and without ready events; an invalid bucket enqueues nothing
+  {
+    const int64_t edges[6] = {400, 800, 0, 400, 800, 1001};  // rank 3 holds 1001 elements
+    void* evs[3] = {(void*)(A + 1), nullptr, (void*)(A + 2)};
+    const int before_b = g_launches;
+    CHECK(zero_step_buckets(&h, (void*)A, grads, &stm, 2, edges, 3, evs, nullptr) == ZERO_OK);
+    CHECK(g_launches == before_b + 5);  // 2 waits + 3 launches
+    const int64_t bad[4] = {0, 400, 404, 900};  // the second begin is not a multiple of 8
+    CHECK(zero_step_buckets(&h, (void*)A, grads, &stm, 2, bad, 2, nullptr, nullptr) == ZERO_EINVAL);
+    CHECK(g_launches == before_b + 5);
+    CHECK(zero_step_buckets(&h, (void*)A, grads, &stm, 2, nullptr, 1, nullptr, nullptr) == ZERO_EINVAL);
+    CHECK(zero_step_buckets(&h, (void*)A, grads, &stm, 2, edges, -1, nullptr, nullptr) == ZERO_EINVAL);
+  }
   // empty shard: nothing launched, pointers may be NULL
   const int before = g_launches;
   h = hp(3, 5, 4, ZERO_MODE_F64);

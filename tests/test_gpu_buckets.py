@@ -150,6 +150,60 @@ def test_overlap_with_a_producer_stream(oracle, mode):
     _check_vs_oracle(oracle, wl, p_ovl, s_ovl, p0, g_hist)
 
 
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16])
+def test_native_buckets_equal_one_shot(mode):
+    """zero_step_buckets: every bucket in one call, last bucket first."""
+    wl = synth.scaled(BASE[mode], 1_000_003, weight_decay=0.05, decay="all")
+    say(f"[case] native buckets mode={mode}")
+    hp, p_one, s_one, _ = setup(wl)
+    _, p_bkt, s_bkt, _ = setup(wl)
+    for t in (1, 2, 3):
+        grads = synth.make_grads(wl, t, "cuda")
+        z.zero_step(hp, p_one, grads, s_one, t)
+        z.zero_step_buckets(hp, p_bkt, grads, s_bkt, t, list(reversed(_buckets(wl.n, 65_536))))
+    torch.cuda.synchronize()
+    assert _same(p_one, p_bkt) and _same(s_one.m, s_bkt.m) and _same(s_one.v, s_bkt.v)
+    if s_one.master is not None:
+        assert _same(s_one.master, s_bkt.master)
+
+
+@pytest.mark.parametrize("mode", [MODE_F32, MODE_MIXED])
+def test_native_buckets_wait_for_their_events(oracle, mode):
+    """Backward, emulated: the producer stream is held back by a spin before each
+    bucket, writes that bucket's gradients and records an event; the host has
+    already enqueued the whole bucketed step on the optimizer stream with
+    zero_step_buckets, so each bucket's step must wait for its event on the
+    device. The result equals the one-shot step."""
+    wl = synth.scaled(BASE[mode], 1_000_003)
+    say(f"[case] native buckets waiting on events, mode={mode}")
+    hp, p_one, s_one, _ = setup(wl)
+    _, p_ovl, s_ovl, _ = setup(wl)
+    bkt = list(reversed(_buckets(wl.n, 131_072)))
+    producer, optimizer = torch.cuda.Stream(), torch.cuda.Stream()
+    p0 = host(p_one)
+    g_hist = []
+    for t in (1, 2):
+        src = synth.make_grads(wl, t, "cuda")
+        g_hist.append([host(g) for g in src])
+        z.zero_step(hp, p_one, src, s_one, t)
+        dst = [torch.zeros_like(g) for g in src]
+        torch.cuda.synchronize()
+        events = []
+        with torch.cuda.stream(producer):
+            for lo, hi in bkt:
+                torch.cuda._sleep(2_000_000)  # a bounded spin: the producer lags the host
+                for d, s_ in zip(dst, src):
+                    d[lo:hi].copy_(s_[lo:hi])
+                ev = torch.cuda.Event()
+                ev.record(producer)
+                events.append(ev)
+        z.zero_step_buckets(hp, p_ovl, dst, s_ovl, t, bkt, events, stream=optimizer)
+        torch.cuda.synchronize()
+        del dst
+    assert _same(p_one, p_ovl) and _same(s_one.m, s_ovl.m) and _same(s_one.v, s_ovl.v)
+    _check_vs_oracle(oracle, wl, p_ovl, s_ovl, p0, g_hist)
+
+
 def test_full_size_25MiB_buckets_fp32_320M_n8():
     """The fp32 320M-parameter 8-worker workload at full size, stepped in buckets
     of 25 MiB of one worker's gradient (6,553,600 parameters), equals the one-shot

@@ -4,7 +4,8 @@ Each case draws a mode (fp64, fp32, bf16 or fp16 mixed precision), an optimizer 
 without dampening and Nesterov), n from 1 to ~3e5, N up to 256 (N > n included),
 full or rank mode, no decay / decay everywhere / a random per-element mask, a
 call path (one zero_step; buckets of zero_step_range in a random order;
-buckets of zero_step_range_dev with the step scalars in device memory; the
+buckets of zero_step_range_dev with the step scalars in device memory; all
+buckets in one zero_step_buckets call; the
 materialised mean then zero_step_mean; or zero_step_clipped with a threshold
 never reached, whose factor is exactly 1) and 1-3 steps, and compares every
 element with the oracle's unclipped step at the parity bar of
@@ -63,7 +64,7 @@ def _draw(seed):
     c["rank"] = -1 if rng.random() < 0.6 else int(rng.integers(0, c["N"]))
     c["decay"] = str(rng.choice(["none", "all", "mask"]))
     c["wd"] = 0.0 if c["decay"] == "none" else float(rng.choice([0.01, 0.1]))
-    c["path"] = str(rng.choice(["step", "range", "range_dev", "split", "clip1"]))
+    c["path"] = str(rng.choice(["step", "range", "range_dev", "split", "clip1", "native"]))
     if c["path"] == "clip1" and c["rank"] >= 0:
         c["path"] = "split"  # a clipped step needs every shard: full mode only
     c["steps"] = int(rng.integers(1, 4))
@@ -129,6 +130,8 @@ def test_random_configuration_matches_the_oracle(oracle, seed):
             mean = torch.empty(L, dtype=sdt, device="cuda")
             z.zero_mean_grad(hp, grads, mean)
             z.zero_step_mean(hp, param, mean, st, t)
+        elif c["path"] == "native":  # every bucket in one zero_step_buckets call
+            z.zero_step_buckets(hp, param, grads, st, t, _buckets(rng, L))
         elif c["path"] == "clip1":  # clipped, threshold never reached: factor exactly 1
             ws = torch.empty(z.zero_step_clipped_workspace_bytes(hp), dtype=torch.uint8,
                              device="cuda")

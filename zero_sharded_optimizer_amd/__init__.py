@@ -16,6 +16,9 @@ workers sharing one GPU:
   zero_step_range(hp, param, grads, states, t, begin, end)
                                          -> the same step on [begin, end) only
                                             (one bucket of a bucketed step)
+  zero_step_buckets(hp, param, grads, states, t, buckets, events)
+                                         -> every bucket in one call, each after
+                                            its ready event (overlap with backward)
   zero_mean_grad(hp, grads, mean, sumsq)  -> the reduce-scatter mean, materialised,
                                             and its squared norm
   zero_step_mean(hp, param, mean, states, t, clip_sumsq, max_norm)
@@ -51,7 +54,8 @@ __all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
            "ZERO_MODE_F64", "ZERO_MODE_F32", "ZERO_MODE_MIXED_BF16", "ZERO_MODE_MIXED_F16",
            "ZERO_MAX_WORKERS",
            "ZERO_OPT_ADAM", "ZERO_OPT_SGD", "zero_step_scalars", "zero_step_range_dev",
-           "STEP_SCALARS_BYTES", "zero_min_stage", "ZERO_MODE_MIXED_F16"]
+           "STEP_SCALARS_BYTES", "zero_min_stage", "ZERO_MODE_MIXED_F16",
+           "zero_step_buckets"]
 
 
 class ZeroError(RuntimeError):
@@ -226,6 +230,39 @@ def zero_step_range(hp: HParams, param, grads: Sequence, states: States, t: int,
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
     st = lib.zero_step_range(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t), int(begin),
                              int(end), _stream_handle(stream, states.m))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+def _event_handle(ev):
+    if ev is None or isinstance(ev, int):
+        return ev
+    return ev.cuda_event  # torch.cuda.Event: its hipEvent_t (recorded before this call)
+
+
+def zero_step_buckets(hp: HParams, param, grads: Sequence, states: States, t: int,
+                      buckets: Sequence, events: Optional[Sequence] = None, stream=None) -> None:
+    """Enqueue the step on each (begin, end) bucket in order; bucket i waits for
+    events[i] (a recorded torch.cuda.Event, a raw hipEvent_t, or None) first."""
+    chk = _check_common(hp, param, states)
+    if chk is not None:
+        g_dt, glen = chk
+        if len(grads) != hp.n_workers:
+            raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
+        for k, g in enumerate(grads):
+            _check_tensor(g, g_dt, glen, f"grads[{k}]")
+    if events is not None and len(events) != len(buckets):
+        raise ValueError(f"events: {len(events)} for {len(buckets)} buckets")
+    lib = _abi.load()
+    c_hp, c_st = hp.to_c(), states.to_c()
+    arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
+    flat = [int(x) for lo_hi in buckets for x in lo_hi]
+    edges = (C.c_int64 * max(1, len(flat)))(*flat)
+    evs = None
+    if events is not None:
+        evs = (C.c_void_p * max(1, len(events)))(*[_event_handle(e) for e in events])
+    st = lib.zero_step_buckets(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t), edges,
+                               len(buckets), evs, _stream_handle(stream, states.m))
     if st != ZERO_OK:
         _raise(st)
 

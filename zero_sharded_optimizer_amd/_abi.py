@@ -64,7 +64,8 @@ class zero_mem(C.Structure):
 EXPORTED = ("zero_init_states", "zero_step", "zero_memory_bytes", "zero_shard_bounds",
             "zero_last_error", "zero_mean_grad_workspace_bytes", "zero_mean_grad",
             "zero_step_mean", "zero_step_clipped_workspace_bytes", "zero_step_clipped",
-            "zero_step_range", "zero_step_scalars_fill", "zero_step_range_dev", "zero_min_stage")
+            "zero_step_range", "zero_step_scalars_fill", "zero_step_range_dev", "zero_min_stage",
+            "zero_step_buckets")
 
 _lib = None
 
@@ -120,6 +121,10 @@ def load(path=None):
                                         C.POINTER(C.c_void_p), C.POINTER(zero_states), C.c_void_p,
                                         C.c_int64, C.c_int64, C.c_void_p]
     lib.zero_step_range_dev.restype = C.c_int
+    lib.zero_step_buckets.argtypes = [C.POINTER(zero_hparams), C.c_void_p, C.POINTER(C.c_void_p),
+                                      C.POINTER(zero_states), C.c_int64, C.POINTER(C.c_int64),
+                                      C.c_int32, C.POINTER(C.c_void_p), C.c_void_p]
+    lib.zero_step_buckets.restype = C.c_int
     lib.zero_min_stage.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int64, C.c_int64,
                                     C.POINTER(C.c_int32)]
     lib.zero_min_stage.restype = C.c_int

@@ -3,7 +3,8 @@ libzceil.so, the streaming-ceiling kernels that bench.py measures the memory
 system with.
 
 The host layer (zero_abi.cpp) is compiled with g++; the kernels
-(zero_kernels.hip) with hipcc for gfx950. Both with multiply-add contraction
+(zero_kernels.hip) and the stream helpers (zero_runtime.hip) with hipcc for
+gfx950. Both with multiply-add contraction
 off and IEEE division / square root, because the step's result is defined
 operation by operation. Packed fp32 instructions are disabled for the device
 code.
@@ -43,10 +44,13 @@ def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     abi_o = os.path.join(BUILD, "zero_abi.o")
     ker_o = os.path.join(BUILD, "zero_kernels.o")
+    rt_o = os.path.join(BUILD, "zero_runtime.o")
     steps = [
         ["g++", *HOST_FLAGS, "-c", os.path.join(CSRC, "zero_abi.cpp"), "-o", abi_o],
         [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "zero_kernels.hip"), "-o", ker_o],
-        [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", abi_o, ker_o, "-o", LIB + ".tmp"],
+        [HIPCC, *HIP_FLAGS, "-c", os.path.join(CSRC, "zero_runtime.hip"), "-o", rt_o],
+        [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", abi_o, ker_o, rt_o, "-o",
+         LIB + ".tmp"],
     ]
     for cmd in steps:
         if verbose:

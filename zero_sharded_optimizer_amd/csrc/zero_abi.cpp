@@ -444,6 +444,45 @@ zero_status zero_step_range(const zero_hparams* hp, void* param, const void* con
   return ok();
 }
 
+zero_status zero_step_buckets(const zero_hparams* hp, void* param, const void* const* grads,
+                              const zero_states* st, int64_t t, const int64_t* edges,
+                              int32_t nbuckets, void* const* ready_events, void* stream) {
+  if (edges == nullptr && nbuckets > 0) return fail(ZERO_EINVAL, "edges is NULL");
+  if (nbuckets < 0) return fail(ZERO_EINVAL, "nbuckets must be >= 0, got %d", nbuckets);
+  // validate the whole call and every bucket before enqueueing anything
+  zlaunch::StepArgs whole;
+  bool nothing = false;
+  zero_status s = build_range(hp, param, grads, st, t, 0, 0, &whole, &nothing);
+  if (s != ZERO_OK) return s;
+  int64_t a, b;
+  if (hp->rank >= 0) shard_range(hp->n, hp->n_workers, hp->rank, &a, &b);
+  else a = 0, b = hp->n;
+  const int64_t len = b - a;
+  for (int32_t i = 0; i < nbuckets; ++i) {
+    const int64_t lo = edges[2 * i], hi = edges[2 * i + 1];
+    if (lo < 0 || hi < lo || hi > len)
+      return fail(ZERO_EINVAL, "bucket %d: need 0 <= begin <= end <= %lld, got [%lld, %lld)", i,
+                  (long long)len, (long long)lo, (long long)hi);
+    if (lo % 8 != 0)
+      return fail(ZERO_EINVAL, "bucket %d: begin must be a multiple of 8, got %lld", i,
+                  (long long)lo);
+  }
+  for (int32_t i = 0; i < nbuckets; ++i) {
+    const int64_t lo = edges[2 * i], hi = edges[2 * i + 1];
+    if (ready_events != nullptr && ready_events[i] != nullptr) {
+      const char* err = zlaunch::stream_wait(stream, ready_events[i]);
+      if (err) return fail(ZERO_EHIP, "bucket %d: wait failed: %s", i, err);
+    }
+    zlaunch::StepArgs la;
+    s = build_range(hp, param, grads, st, t, lo, hi, &la, &nothing);
+    if (s != ZERO_OK) return s;  // not reached: validated above
+    if (nothing) continue;
+    const char* err = zlaunch::launch_step(la, stream);
+    if (err) return fail(ZERO_EHIP, "bucket %d: step launch failed: %s", i, err);
+  }
+  return ok();
+}
+
 zero_status zero_step_scalars_fill(const zero_hparams* hp, int64_t t, zero_step_scalars* out) {
   Widths wd;
   int64_t a = 0, b = 0;

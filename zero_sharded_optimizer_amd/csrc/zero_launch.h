@@ -76,5 +76,7 @@ const char* launch_step_mean(const StepArgs& a, void* stream);
 const char* launch_mean(const MeanArgs& a, void* stream);
 // Number of per-block partial sums launch_mean writes for a range of len.
 int64_t mean_partials(int mode, int64_t len);
+// Makes later work on `stream` wait for `event` (a hipEvent_t) to complete.
+const char* stream_wait(void* stream, void* event);
 
 }  // namespace zlaunch
