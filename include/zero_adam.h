@@ -204,11 +204,12 @@ zero_status zero_step_range(const zero_hparams* hp, void* param, const void* con
  * implementation is bad": gradients reduced in ~25 MB buckets while backward
  * runs): the producer records one event per bucket as its gradients land, and
  * the step of each bucket starts as soon as they have, with no host round trip
- * per bucket. Buckets should be disjoint; the result for each element is then
- * bit for bit that of zero_step. Every argument and every bucket is validated
- * before anything is enqueued; an invalid bucket enqueues nothing. Errors as
- * zero_step_range, plus ZERO_EINVAL for nbuckets < 0 or NULL edges;
- * ZERO_EHIP if a wait or launch fails (buckets before it stay enqueued). */
+ * per bucket. The buckets must be disjoint (they need not cover the range); each
+ * element of a bucket then ends bit for bit as after zero_step. Every argument
+ * and every bucket is validated before anything is enqueued; an invalid bucket
+ * enqueues nothing. Errors as zero_step_range, plus ZERO_EINVAL for
+ * nbuckets < 0, NULL edges or overlapping buckets; ZERO_EHIP if a wait or
+ * launch fails (buckets before it stay enqueued). */
 zero_status zero_step_buckets(const zero_hparams* hp, void* param, const void* const* grads,
                               const zero_states* states, int64_t t, const int64_t* edges,
                               int32_t nbuckets, void* const* ready_events, void* stream);

@@ -114,6 +114,9 @@ int main() {
     CHECK(zero_step_buckets(&h, (void*)A, grads, &stm, 2, bad, 2, nullptr, nullptr) == ZERO_EINVAL);
     CHECK(g_launches == before_b + 5);
     CHECK(zero_step_buckets(&h, (void*)A, grads, &stm, 2, nullptr, 1, nullptr, nullptr) == ZERO_EINVAL);
+    const int64_t overlap[4] = {0, 400, 392, 500};
+    CHECK(zero_step_buckets(&h, (void*)A, grads, &stm, 2, overlap, 2, nullptr, nullptr) == ZERO_EINVAL);
+    CHECK(g_launches == before_b + 5);
     CHECK(zero_step_buckets(&h, (void*)A, grads, &stm, 2, edges, -1, nullptr, nullptr) == ZERO_EINVAL);
   }
   // empty shard: nothing launched, pointers may be NULL

@@ -8,8 +8,11 @@
 #include <cstddef>
 #include <cstdint>
 #include <cstdio>
+#include <algorithm>
 #include <cstring>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "zero_launch.h"
 
@@ -466,6 +469,18 @@ zero_status zero_step_buckets(const zero_hparams* hp, void* param, const void* c
     if (lo % 8 != 0)
       return fail(ZERO_EINVAL, "bucket %d: begin must be a multiple of 8, got %lld", i,
                   (long long)lo);
+  }
+  {  // disjoint: an element stepped twice would take two updates in one step
+    std::vector<std::pair<int64_t, int64_t>> r;
+    r.reserve((size_t)nbuckets);
+    for (int32_t i = 0; i < nbuckets; ++i)
+      if (edges[2 * i + 1] > edges[2 * i]) r.emplace_back(edges[2 * i], edges[2 * i + 1]);
+    std::sort(r.begin(), r.end());
+    for (size_t i = 1; i < r.size(); ++i)
+      if (r[i].first < r[i - 1].second)
+        return fail(ZERO_EINVAL, "buckets overlap: [%lld, %lld) and [%lld, %lld)",
+                    (long long)r[i - 1].first, (long long)r[i - 1].second, (long long)r[i].first,
+                    (long long)r[i].second);
   }
   for (int32_t i = 0; i < nbuckets; ++i) {
     const int64_t lo = edges[2 * i], hi = edges[2 * i + 1];
