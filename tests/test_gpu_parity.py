@@ -79,14 +79,25 @@ def test_fp32_n8_worker_scales(oracle, n):
     run_full(oracle, synth.scaled(W["fp32-320M-n8"], n), steps=5)
 
 
-@pytest.mark.parametrize("n", [2_000_003, 4096])
+# sizes: 3,000,017 takes the modes' own launch shapes (at least two blocks per
+# CU); 4096 and the smaller cases take the small-launch shape
+@pytest.mark.parametrize("n", [3_000_017, 4096])
 def test_mixed_n8_bf16(oracle, n):
     run_full(oracle, synth.scaled(W["mixed-1B-n8"], n), steps=5)
 
 
-@pytest.mark.parametrize("n", [2_000_003, 4096])
+@pytest.mark.parametrize("n", [3_000_017, 4096])
 def test_mixed_n8_fp16(oracle, n):
     run_full(oracle, synth.scaled(W["mixed-fp16-1B-n8"], n), steps=5)
+
+
+@pytest.mark.parametrize("N", [5, 64])
+def test_fp32_any_n_in_its_own_shape(oracle, N):
+    """Worker counts other than 1, 2, 4 and 8 at a size that takes the any-N
+    kernel's own 128 x 8 shape, with a ragged last tile."""
+    wl = synth.scaled(W["fp32-320M-n8"], 3_000_017 if N == 5 else 2_500_011, n_workers=N,
+                      worker_scale=None)
+    run_full(oracle, wl, steps=3)
 
 
 @pytest.mark.parametrize("rank", [0, 3, 7])

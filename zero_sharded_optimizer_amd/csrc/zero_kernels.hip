@@ -858,37 +858,55 @@ struct StepShape<ModeF32, 0> {
   static constexpr bool PRE = ZERO_F32W_PRELOAD, WC = ZERO_F32W_WC;
 };
 
-template <class M, int NFIX, int CAP>
-void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
+// Launches the step in the shape (BLOCK, C, PRE, WC): one tile of BLOCK * C
+// groups per block, and at least one block for the leftover elements.
+template <class M, int NFIX, int CAP, int BLOCK, int C, bool PRE, bool WC>
+void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP>& gs,
+                   int out_vec) {
   typedef typename M::S S;
   typedef typename M::P P;
-  typedef StepShape<M, NFIX> SH;
-  constexpr int BLOCK = SH::BLOCK, C = SH::C;
-  constexpr bool PRE = SH::PRE, WC = SH::WC;
-  // one tile of BLOCK * C groups per block; at least one block for the
-  // leftover elements
   const int64_t ngroups = a.len / M::VEC;
   const int64_t per_block = (int64_t)BLOCK * C;
   int64_t blocks = (ngroups + per_block - 1) / per_block;
   if (blocks < 1) blocks = 1;
+  if (a.optimizer == 0)
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0, PRE, WC>),
+                       dim3((unsigned)blocks), dim3(BLOCK), 0, st, gs, a.n_workers,
+                       static_cast<S*>(a.w), static_cast<S*>(a.m), static_cast<S*>(a.v),
+                       static_cast<P*>(a.out), out_vec, a.len, round_consts<S>(a), a.mask,
+                       a.mask_bit_offset, a.decay_kind, a.clip_sumsq, a.max_norm,
+                       static_cast<const zlaunch::DynScalars*>(a.dyn));
+  else
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, PRE, WC>),
+                       dim3((unsigned)blocks), dim3(BLOCK), 0, st, gs, a.n_workers,
+                       static_cast<S*>(a.w), static_cast<S*>(a.m), static_cast<S*>(a.v),
+                       static_cast<P*>(a.out), out_vec, a.len, round_consts<S>(a), a.mask,
+                       a.mask_bit_offset, a.decay_kind, a.clip_sumsq, a.max_norm,
+                       static_cast<const zlaunch::DynScalars*>(a.dyn));
+}
+
+// Small launches (a bucket of a few MiB) take 256 x 1 tiles when the mode's
+// own shape would give fewer than two blocks per CU: the launch then spreads
+// over every CU instead of a quarter of them (1 MiB fp32 bucket, 8 workers:
+// 4.3 us against 5.8-6.3 us on MI355X). The arithmetic is the same.
+constexpr int kSmallBlock = 256;
+
+template <class M, int NFIX, int CAP>
+void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
+  typedef StepShape<M, NFIX> SH;
   GradSet<CAP> gs;
   for (int k = 0; k < CAP; ++k) gs.p[k] = k < a.n_workers ? a.grads[k] : nullptr;
   const int out_vec =
       a.out != nullptr && (reinterpret_cast<uintptr_t>(a.out) % OutIO<M>::kAlign == 0);
-  if (a.optimizer == 0)
-    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0, PRE, WC>), dim3((unsigned)blocks),
-                       dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
-                       static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
-                       out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
-                       a.decay_kind, a.clip_sumsq, a.max_norm,
-                       static_cast<const zlaunch::DynScalars*>(a.dyn));
-  else
-    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, PRE, WC>), dim3((unsigned)blocks),
-                       dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.w),
-                       static_cast<S*>(a.m), static_cast<S*>(a.v), static_cast<P*>(a.out),
-                       out_vec, a.len, round_consts<S>(a), a.mask, a.mask_bit_offset,
-                       a.decay_kind, a.clip_sumsq, a.max_norm,
-                       static_cast<const zlaunch::DynScalars*>(a.dyn));
+  if constexpr (SH::BLOCK * SH::C > kSmallBlock) {
+    const int64_t per_block = (int64_t)SH::BLOCK * SH::C;
+    const int64_t blocks = (a.len / M::VEC + per_block - 1) / per_block;
+    if (blocks < 2 * (int64_t)device_cus()) {
+      launch_shaped<M, NFIX, CAP, kSmallBlock, 1, false, false>(a, st, gs, out_vec);
+      return;
+    }
+  }
+  launch_shaped<M, NFIX, CAP, SH::BLOCK, SH::C, SH::PRE, SH::WC>(a, st, gs, out_vec);
 }
 
 template <class M>
