@@ -1,0 +1,190 @@
+"""A ZeroOptimizer over the C ABI, with the interface of "Data parallelism and
+ZeRO stages 1 to 3" (openlearn L11.3), section "4. The interface":
+ZeroOptimizer(..., stage, **kw) with step(), zero_grad(), gather() and
+memory_bytes().
+
+On one GPU the N logical workers share one HBM, so the optimizer keeps:
+  * one flat gathered parameter buffer in parameters() order; each model
+    parameter becomes a view of its slice (so the model reads the gathered
+    result directly, and no tensor can be unflattened out of order);
+  * one flat gradient buffer per logical worker, with per-parameter views
+    (worker_grads(k)) that worker k's backward pass (or a copy) fills;
+  * the optimizer state as flat device buffers (fp32 master in mixed precision,
+    m, v), each worker's shard being its [a_r, b_r) view.
+step() runs one fused zero_step over all of it. The stage only changes the
+memory model (memory_bytes), as on the pages: sharding moves storage between
+ranks and leaves the arithmetic unchanged.
+
+This module is argument marshalling only: every step of the computation runs
+in libzero.so's HIP kernels.
+"""
+from typing import Dict, List, Optional, Sequence
+
+import zero_sharded_optimizer_amd as z
+
+_MODE_DTYPE = {"fp64": (z.ZERO_MODE_F64, "float64", "float64"),
+               "fp32": (z.ZERO_MODE_F32, "float32", "float32"),
+               "bf16": (z.ZERO_MODE_MIXED_BF16, "bfloat16", "float32"),
+               "fp16": (z.ZERO_MODE_MIXED_F16, "float16", "float32")}
+
+
+class ZeroOptimizer:
+    """ZeRO-sharded Adam/AdamW (or momentum SGD) over N logical workers on one GPU.
+
+    params: the model's parameters (device tensors of the mode's parameter
+        dtype), in parameters() order.
+    n_workers: N, the logical data-parallel workers (ranks).
+    stage: 1, 2 or 3 (0, 4 and no parameters are rejected, as the pages do).
+    precision: "fp64", "fp32", "bf16" or "fp16" (the latter two with an fp32
+        master, m and v).
+    optimizer: "adamw" (lr, betas, eps, weight_decay) or "sgd" (lr, momentum,
+        dampening, nesterov, weight_decay). No hyperparameter has a hidden
+        default inside the library; the keyword defaults here are torch's.
+    decay: None (decay everything when weight_decay > 0) or one bool per
+        parameter tensor (e.g. 2-D tensors only).
+    """
+
+    def __init__(self, params: Sequence, n_workers: int, stage: int, precision: str = "fp32",
+                 optimizer: str = "adamw", lr: float = 1e-3, betas=(0.9, 0.999),
+                 eps: float = 1e-8, weight_decay: float = 0.0, momentum: float = 0.0,
+                 dampening: float = 0.0, nesterov: bool = False,
+                 decay: Optional[Sequence[bool]] = None):
+        params = list(params)
+        if stage not in (1, 2, 3):
+            raise ValueError(f"stage must be 1, 2 or 3, got {stage}")
+        if not params:
+            raise ValueError("no parameters")
+        if n_workers < 1 or n_workers > z.ZERO_MAX_WORKERS:
+            raise ValueError(f"n_workers must be in [1, {z.ZERO_MAX_WORKERS}], got {n_workers}")
+        if precision not in _MODE_DTYPE:
+            raise ValueError(f"precision must be one of {sorted(_MODE_DTYPE)}")
+        if optimizer not in ("adamw", "sgd"):
+            raise ValueError("optimizer must be 'adamw' or 'sgd'")
+        if decay is not None and len(decay) != len(params):
+            raise ValueError("decay: one flag per parameter tensor")
+        import torch
+        mode, pdt, sdt = _MODE_DTYPE[precision]
+        pdt, sdt = getattr(torch, pdt), getattr(torch, sdt)
+        for i, p in enumerate(params):
+            if not p.is_cuda or p.dtype != pdt:
+                raise ValueError(f"params[{i}]: expected a GPU tensor of {pdt}")
+        self.stage, self.n_workers, self.mode = stage, n_workers, mode
+        self.params = params
+        self.sizes = [p.numel() for p in params]
+        self.offsets = [sum(self.sizes[:i]) for i in range(len(params))]
+        n = sum(self.sizes)
+        self.n = n
+        dev = params[0].device
+        # the gathered buffer; each parameter becomes a view of its slice
+        self.flat = torch.empty(n, dtype=pdt, device=dev)
+        for p, off, size in zip(params, self.offsets, self.sizes):
+            self.flat[off:off + size].copy_(p.detach().reshape(-1))
+            p.data = self.flat[off:off + size].view_as(p)
+        self.grads = [torch.zeros(n, dtype=pdt, device=dev) for _ in range(n_workers)]
+        sgd = optimizer == "sgd"
+        mixed = mode in (z.ZERO_MODE_MIXED_BF16, z.ZERO_MODE_MIXED_F16)
+        self.states = z.States(torch.empty(n, dtype=sdt, device=dev) if mixed else None,
+                               torch.empty(n, dtype=sdt, device=dev),
+                               None if sgd else torch.empty(n, dtype=sdt, device=dev))
+        mask = None
+        if decay is not None and weight_decay:
+            flags = torch.zeros(n, dtype=torch.bool)
+            for f, off, size in zip(decay, self.offsets, self.sizes):
+                if f:
+                    flags[off:off + size] = True
+            mask = z.wd_mask_from_flags(flags, device=dev)
+        self.hp = z.HParams(n=n, n_workers=n_workers, mode=mode, lr=lr, beta1=betas[0],
+                            beta2=betas[1], eps=eps, weight_decay=weight_decay, wd_mask=mask,
+                            optimizer=z.ZERO_OPT_SGD if sgd else z.ZERO_OPT_ADAM,
+                            momentum=momentum, dampening=dampening, nesterov=nesterov)
+        z.zero_init_states(self.hp, self.flat, self.states)
+        self.t = 0
+
+    # -- the training step ------------------------------------------------------
+    def worker_grads(self, k: int) -> List:
+        """Per-parameter views of worker k's flat gradient buffer (shapes of the
+        parameters), to be filled by that worker's backward pass or a copy."""
+        g = self.grads[k]
+        return [g[off:off + size].view_as(p)
+                for p, off, size in zip(self.params, self.offsets, self.sizes)]
+
+    def zero_grad(self) -> None:
+        for g in self.grads:
+            g.zero_()
+
+    def gather(self) -> None:
+        """Stage 3's gather of the full parameters before forward. On one GPU every
+        worker reads the one gathered buffer, so there is nothing to move."""
+
+    def step(self, stream=None) -> None:
+        """One fused step (reduce-scatter mean, Adam/SGD on each shard,
+        all-gather) over the workers' gradient buffers, enqueued on `stream`."""
+        self.t += 1
+        z.zero_step(self.hp, self.flat, self.grads, self.states, self.t, stream=stream)
+
+    # -- memory and checkpoints -------------------------------------------------
+    def memory_bytes(self, rank: int = 0, convention: int = 0) -> Dict[str, int]:
+        """Rank `rank`'s bytes at this stage: params, grads, optimizer, by the
+        closed forms (convention 0) or the emulation's bookkeeping (convention 1,
+        fp64/fp32 only), as zero_memory_bytes defines them."""
+        d = z.zero_memory_bytes(self.n, self.n_workers, rank, self.stage, self.mode, convention)
+        return {k: d[k] for k in ("params", "grads", "optimizer")}
+
+    def state_dict(self) -> Dict:
+        """The step count and device copies of the gathered parameters and state."""
+        s = self.states
+        return {"t": self.t, "param": self.flat.clone(),
+                "master": None if s.master is None else s.master.clone(),
+                "m": s.m.clone(), "v": None if s.v is None else s.v.clone()}
+
+    def load_state_dict(self, sd: Dict) -> None:
+        """Restore a state_dict() of an optimizer of the same shape; checks every
+        entry before it copies any."""
+        s = self.states
+        pairs = [(self.flat, sd["param"], "param")]
+        pairs += [(getattr(s, k), sd[k], k) for k in ("master", "m", "v")]
+        for dst, src, name in pairs:
+            if (dst is None) != (src is None):
+                raise ValueError(f"state_dict: {name} does not match this optimizer")
+            if dst is not None and (src.dtype != dst.dtype or src.numel() != dst.numel()):
+                raise ValueError(f"state_dict: {name} has another dtype or size")
+        self.t = int(sd["t"])
+        for dst, src, _ in pairs:
+            if dst is not None:
+                dst.copy_(src)
+
+
+def init_states(n_params: int, n_workers: int, device="cuda", precision: str = "fp32",
+                param=None) -> z.States:
+    """init_states ("ZeRO-Sharded Adam Step", section "What to implement"): the
+    workers' (m, v) shards as flat buffers of zeros (and, in mixed precision,
+    the fp32 master copied from `param`)."""
+    import torch
+    mode, _, sdt = _MODE_DTYPE[precision]
+    sdt = getattr(torch, sdt)
+    mixed = mode in (z.ZERO_MODE_MIXED_BF16, z.ZERO_MODE_MIXED_F16)
+    if mixed and param is None:
+        raise ValueError("mixed precision: pass param to set the master copy")
+    st = z.States(torch.empty(n_params, dtype=sdt, device=device) if mixed else None,
+                  torch.empty(n_params, dtype=sdt, device=device),
+                  torch.empty(n_params, dtype=sdt, device=device))
+    hp = z.HParams(n=n_params, n_workers=n_workers, mode=mode, lr=0.0, beta1=0.9, beta2=0.999,
+                   eps=1e-8)
+    z.zero_init_states(hp, param, st)
+    return st
+
+
+def zero_step(param, grads: Sequence, states: z.States, t: int, lr: float = 1e-2,
+              betas=(0.9, 0.999), eps: float = 1e-8, weight_decay: float = 0.0,
+              precision: str = "fp32"):
+    """zero_step ("ZeRO-Sharded Adam Step", section "What to implement"), the
+    functional form: returns (new_param, new_states) and leaves its inputs as
+    they were. lr defaults to the page's 1e-2."""
+    new_param = param.clone()
+    new_states = z.States(None if states.master is None else states.master.clone(),
+                          states.m.clone(), states.v.clone())
+    mode = _MODE_DTYPE[precision][0]
+    hp = z.HParams(n=param.numel(), n_workers=len(grads), mode=mode, lr=lr, beta1=betas[0],
+                   beta2=betas[1], eps=eps, weight_decay=weight_decay)
+    z.zero_step(hp, new_param, list(grads), new_states, t)
+    return new_param, new_states
