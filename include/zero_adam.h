@@ -103,7 +103,7 @@ typedef enum {
  * every field is used as given ("Data parallelism and ZeRO stages 1 to 3",
  * section "5. Pitfalls", dropped hyperparameters). */
 typedef struct {
-  int64_t n;         /* parameters in the gathered vector; >= 1 */
+  int64_t n;         /* parameters in the gathered vector; 1 <= n <= 2^56 */
   int32_t n_workers; /* N, 1 <= N <= ZERO_MAX_WORKERS for zero_step; N > n is
                         allowed and gives trailing empty shards */
   int32_t rank;      /* -1: every worker's share in this call (full mode);
@@ -171,7 +171,7 @@ zero_status zero_init_states(const zero_hparams* hp, const void* param,
  * no buffer is touched and param, grads and states may be NULL (the scalar
  * arguments and t are still checked).
  * Errors: ZERO_EINVAL for a null or misaligned pointer, overlapping written
- * ranges, n < 1, N outside [1, ZERO_MAX_WORKERS], rank outside [-1, N), t < 1,
+ * ranges, n outside [1, 2^56], N outside [1, ZERO_MAX_WORKERS], rank outside [-1, N), t < 1,
  * a non-finite scalar, a beta outside [0, 1), eps <= 0, weight_decay < 0, an
  * unknown optimizer, SGD momentum < 0, dampening outside [0, 1], nesterov
  * without momentum or with dampening, a mode/master mismatch, or
@@ -278,8 +278,9 @@ zero_status zero_mean_grad(const zero_hparams* hp, const void* const* grads, voi
 
 /* The step driven by a materialised mean gradient (mean_grad: the call's len
  * elements of S, 16-byte aligned, read-only), otherwise as zero_step. If
- * clip_sumsq is non-NULL it points to the global squared norm (device double)
- * and the mean is scaled by the clipping factor for max_norm (finite, > 0).
+ * clip_sumsq is non-NULL it points to the global squared norm (device double,
+ * 8-byte aligned, not inside any buffer the step writes) and the mean is
+ * scaled by the clipping factor for max_norm (finite, > 0).
  * Unclipped, or with a factor of exactly 1, the result is bit-identical to
  * zero_step on the gradients that produced the mean. */
 zero_status zero_step_mean(const zero_hparams* hp, void* param, const void* mean_grad,
@@ -329,7 +330,7 @@ typedef struct {
  *              gradients kept in .grad plus the chunk's gradient)
  *     stage 2: B n,  B c,        3 B c
  *     stage 3: B c,  B c,        2 B c   (the chunk is the parameter storage)
- * Errors: ZERO_EINVAL for n < 1, N < 1, rank outside [0, N), stage outside
+ * Errors: ZERO_EINVAL for n < 1 or n > 2^56, N < 1, rank outside [0, N), stage outside
  * [0, 3], an unknown mode or convention, or a NULL out; ZERO_EUNSUPPORTED for
  * convention 1 in the mixed modes. */
 zero_status zero_memory_bytes(int64_t n, int32_t n_workers, int32_t rank, int32_t stage,
@@ -340,7 +341,7 @@ zero_status zero_memory_bytes(int64_t n, int32_t n_workers, int32_t rank, int32_
  * below the memory available). For stage s in 0, 1, 2, 3 the need is
  * zero_memory_bytes(n, N, 0, s, mode, 0).total (rank 0 holds the largest shard)
  * plus activation_bytes; *stage is the first s whose need is < available_bytes,
- * or -1 when none is. Host-only. Errors: ZERO_EINVAL for n < 1, N < 1, an
+ * or -1 when none is. Host-only. Errors: ZERO_EINVAL for n outside [1, 2^56], N < 1, an
  * unknown mode, a negative byte count or a NULL stage. */
 zero_status zero_min_stage(int64_t n, int32_t n_workers, int32_t mode, int64_t activation_bytes,
                            int64_t available_bytes, int32_t* stage);

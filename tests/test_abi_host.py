@@ -409,3 +409,36 @@ def test_min_stage_agrees_with_the_oracle_and_the_page(oracle):
     for bad in ((0, 8, 1, 0, 10), (10, 0, 1, 0, 10), (10, 8, 9, 0, 10), (10, 8, 1, -1, 10)):
         with pytest.raises(z.ZeroError):
             z.zero_min_stage(*bad)
+
+
+def test_n_above_two_to_the_56_is_rejected():
+    """Every byte count formed from n stays inside int64: n > 2^56 is rejected by
+    the step, the memory model and the stage choice."""
+    rc, msg = _call_step(_hp(n=(1 << 56) + 1))
+    assert rc == z.ZERO_EINVAL and "2^56" in msg
+    with pytest.raises(z.ZeroError):
+        z.zero_memory_bytes((1 << 56) + 1, 4, 0, 1, z.ZERO_MODE_F64)
+    with pytest.raises(z.ZeroError):
+        z.zero_min_stage((1 << 56) + 1, 4, z.ZERO_MODE_F64, 0, 1 << 62)
+    d = z.zero_memory_bytes(1 << 56, 1, 0, 0, z.ZERO_MODE_F64)
+    assert d["total"] == 32 << 56
+
+
+def test_min_stage_does_not_overflow_with_huge_activations():
+    """activation_bytes near INT64_MAX: no stage fits (no wrap-around)."""
+    big = (1 << 63) - 1
+    assert z.zero_min_stage(1000, 4, z.ZERO_MODE_F32, big, big) == -1
+    assert z.zero_min_stage(1000, 4, z.ZERO_MODE_F32, big - 100, big) == -1
+    assert z.zero_min_stage(1000, 4, z.ZERO_MODE_F32, 0, big) == 0
+
+
+def test_step_mean_rejects_a_clip_norm_inside_an_output():
+    """The clipped step reads the squared norm while it writes its outputs: a
+    norm inside m (or the parameter) is rejected before any launch."""
+    lib = _abi.load()
+    st = _abi.zero_states(master=None, m=A + (1 << 24), v=A + (2 << 24))
+    hp = _hp()
+    mean = A + (5 << 24)
+    for norm in (A + (1 << 24) + 64, A + 8, A + (2 << 24)):
+        rc = lib.zero_step_mean(C.byref(hp), A, mean, C.byref(st), 1, norm, 1.0, None)
+        assert rc == z.ZERO_EINVAL and "clip_sumsq overlaps" in lib.zero_last_error().decode()

@@ -25,6 +25,10 @@ namespace {
 
 thread_local std::string g_last_error;
 
+// Largest accepted n: 2^56 elements, so that every byte count and address
+// range formed from n (at most 32 bytes per element) stays inside int64_t.
+constexpr int64_t kMaxN = INT64_C(1) << 56;
+
 zero_status fail(zero_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 zero_status fail(zero_status st, const char* fmt, ...) {
   char buf[512];
@@ -93,6 +97,7 @@ zero_status check_hparams(const zero_hparams* hp, bool for_step, Widths* wd, int
   if (!mode_widths(hp->mode, wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
   if (hp->n < 1) return fail(ZERO_EINVAL, "n must be >= 1 (no parameters), got %lld",
                              (long long)hp->n);
+  if (hp->n > kMaxN) return fail(ZERO_EINVAL, "n must be <= 2^56, got %lld", (long long)hp->n);
   if (hp->n_workers < 1 || hp->n_workers > ZERO_MAX_WORKERS)
     return fail(ZERO_EINVAL, "n_workers must be in [1, %d], got %d", ZERO_MAX_WORKERS,
                 hp->n_workers);
@@ -171,6 +176,7 @@ zero_status zero_memory_bytes(int64_t n, int32_t n_workers, int32_t rank, int32_
                               int32_t mode, int32_t convention, zero_mem* out) {
   if (out == nullptr) return fail(ZERO_EINVAL, "out is NULL");
   if (n < 1) return fail(ZERO_EINVAL, "n must be >= 1 (no parameters)");
+  if (n > kMaxN) return fail(ZERO_EINVAL, "n must be <= 2^56");
   if (n_workers < 1) return fail(ZERO_EINVAL, "n_workers must be >= 1");
   if (rank < 0 || rank >= n_workers) return fail(ZERO_EINVAL, "rank must be in [0, %d)", n_workers);
   if (stage < 0 || stage > 3) return fail(ZERO_EINVAL, "stage must be in [0, 3], got %d", stage);
@@ -210,7 +216,8 @@ zero_status zero_min_stage(int64_t n, int32_t n_workers, int32_t mode, int64_t a
     zero_mem m;
     const zero_status st = zero_memory_bytes(n, n_workers, 0, s, mode, 0, &m);
     if (st != ZERO_OK) return st;
-    if (m.total + activation_bytes < available_bytes) {
+    // m.total + activation_bytes < available_bytes, without overflow
+    if (activation_bytes < available_bytes && m.total < available_bytes - activation_bytes) {
       *stage = s;
       break;
     }
@@ -360,6 +367,30 @@ zero_status build_step(const zero_hparams* hp, void* param, const void* const* g
 }
 
 int64_t align_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+// The ranges a built step launch writes: its master or in-place parameter,
+// m, v (NULL for SGD) and the separate gathered output (NULL when in place).
+void step_written(const zlaunch::StepArgs& la, const Widths& wd, Range out[4]) {
+  const uintptr_t w = (uintptr_t)la.w, m = (uintptr_t)la.m, v = (uintptr_t)la.v,
+                  o = (uintptr_t)la.out;
+  const uintptr_t sb = (uintptr_t)(la.len * wd.state);
+  out[0] = {w, w + sb, "w"};
+  out[1] = {m, m + sb, "m"};
+  out[2] = {v, v ? v + sb : 0, "v"};
+  out[3] = {o, o ? o + (uintptr_t)(la.len * wd.param) : 0, "param"};
+}
+
+// A device value of `bytes` bytes that the step kernel reads while it writes
+// its outputs must not overlap any of them.
+zero_status check_not_written(const zlaunch::StepArgs& la, const Widths& wd, const void* p,
+                              size_t bytes, const char* name) {
+  Range written[4];
+  step_written(la, wd, written);
+  const Range r{(uintptr_t)p, (uintptr_t)p + bytes, name};
+  for (const Range& x : written)
+    if (overlaps(r, x)) return fail(ZERO_EINVAL, "%s overlaps %s", name, x.name);
+  return ZERO_OK;
+}
 
 // Validation and launch arguments shared by zero_step_range and
 // zero_step_range_dev: the range [begin, end) of the call's index space as
@@ -524,18 +555,10 @@ zero_status zero_step_range_dev(const zero_hparams* hp, void* param, const void*
   // validated as step 1; the kernel takes the step-dependent values from dev_scalars
   zero_status s = build_range(hp, param, grads, st, 1, begin, end, &la, &nothing);
   if (s != ZERO_OK || nothing) return s == ZERO_OK ? ok() : s;
-  const Range rd{(uintptr_t)dev_scalars, (uintptr_t)dev_scalars + sizeof(zero_step_scalars),
-                 "dev_scalars"};
   Widths wd{};
   if (!mode_widths(hp->mode, &wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
-  const Range written[4] = {
-      {(uintptr_t)la.w, (uintptr_t)la.w + (uintptr_t)(la.len * wd.state), "w"},
-      {(uintptr_t)la.m, (uintptr_t)la.m + (uintptr_t)(la.len * wd.state), "m"},
-      {(uintptr_t)la.v, la.v ? (uintptr_t)la.v + (uintptr_t)(la.len * wd.state) : 0, "v"},
-      {(uintptr_t)la.out, la.out ? (uintptr_t)la.out + (uintptr_t)(la.len * wd.param) : 0,
-       "param"}};
-  for (const Range& r : written)
-    if (overlaps(rd, r)) return fail(ZERO_EINVAL, "dev_scalars overlaps %s", r.name);
+  s = check_not_written(la, wd, dev_scalars, sizeof(zero_step_scalars), "dev_scalars");
+  if (s != ZERO_OK) return s;
   la.dyn = dev_scalars;
   const char* err = zlaunch::launch_step(la, stream);
   if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
@@ -619,6 +642,9 @@ zero_status zero_step_mean(const zero_hparams* hp, void* param, const void* mean
   const void* one[1] = {mean_grad};
   zero_status s = build_step(hp, param, one, 1, wd.state, st, t, &la, &empty, &a, &b);
   if (s != ZERO_OK || empty) return s == ZERO_OK ? ok() : s;
+  if (clip_sumsq != nullptr &&
+      (s = check_not_written(la, wd, clip_sumsq, sizeof(double), "clip_sumsq")) != ZERO_OK)
+    return s;
   la.clip_sumsq = clip_sumsq;
   la.max_norm = max_norm;
   const char* err = zlaunch::launch_step_mean(la, stream);
