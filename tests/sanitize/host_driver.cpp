@@ -8,17 +8,52 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <vector>
 
 #include "zero_adam.h"
 #include "zero_launch.h"
 
 static int g_launches = 0;
 
+// What each launch reaching the stubs was given: kind 0 step, 1 step from a
+// mean, 2 mean (w = mean, m = partials), 3 finalize (w = partials, len = count).
+struct Rec {
+  int kind;
+  int64_t len;
+  uintptr_t w, m, v, out, g0, g1;
+  int64_t mask_off;
+};
+static std::vector<Rec> g_rec;
+
+static void record_step(int kind, const zlaunch::StepArgs& a) {
+  g_rec.push_back({kind, a.len, (uintptr_t)a.w, (uintptr_t)a.m, (uintptr_t)a.v, (uintptr_t)a.out,
+                   (uintptr_t)a.grads[0], a.n_workers > 1 ? (uintptr_t)a.grads[1] : 0,
+                   a.mask_bit_offset});
+}
+
 namespace zlaunch {
-const char* launch_step(const StepArgs&, void*) { ++g_launches; return nullptr; }
+const char* launch_step(const StepArgs& a, void*) {
+  ++g_launches;
+  record_step(0, a);
+  return nullptr;
+}
 const char* launch_init(const InitArgs&, void*) { ++g_launches; return nullptr; }
-const char* launch_step_mean(const StepArgs&, void*) { ++g_launches; return nullptr; }
-const char* launch_mean(const MeanArgs&, void*) { ++g_launches; return nullptr; }
+const char* launch_step_mean(const StepArgs& a, void*) {
+  ++g_launches;
+  record_step(1, a);
+  return nullptr;
+}
+const char* launch_mean(const MeanArgs& a, void*) {
+  ++g_launches;
+  g_rec.push_back({2, a.len, (uintptr_t)a.mean, (uintptr_t)a.partials, 0, 0,
+                   (uintptr_t)a.grads[0], 0, 0});
+  return nullptr;
+}
+const char* launch_sumsq_finalize(const double* partials, int64_t count, double* out, void*) {
+  ++g_launches;
+  g_rec.push_back({3, count, (uintptr_t)partials, 0, 0, (uintptr_t)out, 0, 0, 0});
+  return nullptr;
+}
 int64_t mean_partials(int, int64_t len) { return len / 1024 + 1; }
 const char* stream_wait(void*, void*) { ++g_launches; return nullptr; }
 }  // namespace zlaunch
@@ -153,6 +188,97 @@ int main() {
                        (void*)(A + ((uintptr_t)361 << 24)), mws, nullptr) == ZERO_OK);
   CHECK(zero_step_mean(&h, (void*)A, (void*)(A + ((uintptr_t)350 << 24)), &st, 1,
                        (const double*)(A + ((uintptr_t)360 << 24)), 1.0, nullptr) == ZERO_OK);
+  // Calls longer than zlaunch::kLaunchElems are enqueued as consecutive
+  // launches on offset views: lengths, pointers and mask offsets per piece.
+  {
+    const int64_t L = zlaunch::kLaunchElems;
+    const uintptr_t B = (uintptr_t)1 << 40, S = (uintptr_t)1 << 38;  // 256 GiB apart
+    const void* bg[2] = {(const void*)(B + 3 * S), (const void*)(B + 4 * S)};
+    zero_states bst = {(void*)(B + 5 * S), (void*)(B + 1 * S), (void*)(B + 2 * S)};
+    zero_hparams bh = hp(2 * L + 5, 2, -1, ZERO_MODE_MIXED_BF16);
+    bh.weight_decay = 0.1;
+    bh.wd_mask = (const uint32_t*)(B + 6 * S);
+    g_rec.clear();
+    CHECK(zero_step(&bh, (void*)B, bg, &bst, 1, nullptr) == ZERO_OK);
+    CHECK(g_rec.size() == 3);
+    for (size_t i = 0; i < g_rec.size() && i < 3; ++i) {
+      const int64_t off = (int64_t)i * L;
+      const Rec& r = g_rec[i];
+      CHECK(r.kind == 0 && r.len == (i < 2 ? L : 5) && r.mask_off == off);
+      CHECK(r.w == B + 5 * S + 4 * off && r.m == B + 1 * S + 4 * off && r.v == B + 2 * S + 4 * off);
+      CHECK(r.out == B + 2 * off && r.g0 == B + 3 * S + 2 * off && r.g1 == B + 4 * S + 2 * off);
+    }
+    // rank mode: the mask offset is the shard's start plus the piece's offset
+    zero_hparams rh = hp(8 * (L + 3) + 1, 8, 3, ZERO_MODE_MIXED_BF16);
+    int64_t ra, rb;
+    CHECK(zero_shard_bounds(rh.n, 8, 3, &ra, &rb) == ZERO_OK && rb - ra == L + 3);
+    rh.weight_decay = 0.1;
+    rh.wd_mask = (const uint32_t*)(B + 6 * S);
+    const void* rg[8];
+    for (int k = 0; k < 8; ++k) rg[k] = (const void*)(B + (8 + k) * S);
+    g_rec.clear();
+    CHECK(zero_step(&rh, (void*)B, rg, &bst, 1, nullptr) == ZERO_OK);
+    CHECK(g_rec.size() == 2);
+    if (g_rec.size() == 2) {
+      CHECK(g_rec[0].len == L && g_rec[0].mask_off == ra && g_rec[0].out == B + 2 * ra);
+      CHECK(g_rec[1].len == 3 && g_rec[1].mask_off == ra + L && g_rec[1].out == B + 2 * (ra + L));
+      CHECK(g_rec[1].w == B + 5 * S + 4 * L && g_rec[1].g0 == B + 8 * S + 2 * L);
+    }
+    // a range: the pieces start at `begin`
+    g_rec.clear();
+    CHECK(zero_step_range(&bh, (void*)B, bg, &bst, 1, 8, L + 24, nullptr) == ZERO_OK);
+    CHECK(g_rec.size() == 2);
+    if (g_rec.size() == 2) {
+      CHECK(g_rec[0].len == L && g_rec[0].w == B + 5 * S + 4 * 8 && g_rec[0].mask_off == 8);
+      CHECK(g_rec[1].len == 16 && g_rec[1].w == B + 5 * S + 4 * (8 + L) &&
+            g_rec[1].mask_off == 8 + L);
+    }
+    // the mean: pieces write their partials back to back, one finalize sums them all
+    zero_hparams mh = hp(L + 1, 1, -1, ZERO_MODE_F32);
+    size_t mws = 0;
+    CHECK(zero_mean_grad_workspace_bytes(&mh, &mws) == ZERO_OK);
+    const int64_t p0 = L / 1024 + 1, p1 = 1 / 1024 + 1;  // the stub's mean_partials
+    CHECK((int64_t)mws == 8 * (p0 + p1));
+    g_rec.clear();
+    CHECK(zero_mean_grad(&mh, bg, (void*)(B + 1 * S), (double*)(B + 2 * S), (void*)(B + 5 * S),
+                         mws, nullptr) == ZERO_OK);
+    CHECK(g_rec.size() == 3);
+    if (g_rec.size() == 3) {
+      CHECK(g_rec[0].kind == 2 && g_rec[0].len == L && g_rec[0].m == B + 5 * S);
+      CHECK(g_rec[1].kind == 2 && g_rec[1].len == 1 && g_rec[1].w == B + 1 * S + 4 * L &&
+            g_rec[1].g0 == B + 3 * S + 4 * L && g_rec[1].m == B + 5 * S + 8 * p0);
+      CHECK(g_rec[2].kind == 3 && g_rec[2].len == p0 + p1 && g_rec[2].w == B + 5 * S &&
+            g_rec[2].out == B + 2 * S);
+    }
+    CHECK(zero_mean_grad(&mh, bg, (void*)(B + 1 * S), (double*)(B + 2 * S), (void*)(B + 5 * S),
+                         mws - 8, nullptr) == ZERO_EINVAL);
+    // the clipped step: mean pieces, the finalize, then step pieces from the mean
+    zero_states cst = {nullptr, (void*)(B + 1 * S), (void*)(B + 2 * S)};
+    size_t cws = 0;
+    CHECK(zero_step_clipped_workspace_bytes(&mh, &cws) == ZERO_OK);
+    g_rec.clear();
+    CHECK(zero_step_clipped(&mh, (void*)(B + 7 * S), bg, &cst, 1, 1.0, nullptr,
+                            (void*)(B + 9 * S), cws, nullptr) == ZERO_OK);
+    CHECK(g_rec.size() == 5);
+    if (g_rec.size() == 5) {
+      CHECK(g_rec[0].kind == 2 && g_rec[1].kind == 2 && g_rec[2].kind == 3);
+      CHECK(g_rec[3].kind == 1 && g_rec[3].len == L && g_rec[3].g0 == B + 9 * S);
+      CHECK(g_rec[4].kind == 1 && g_rec[4].len == 1 && g_rec[4].g0 == B + 9 * S + 4 * L &&
+            g_rec[4].w == B + 7 * S + 4 * L);
+    }
+    // an empty rank shard still writes its (zero) norm: one mean launch, one finalize
+    zero_hparams eh = hp(3, 5, 4, ZERO_MODE_F32);
+    g_rec.clear();
+    CHECK(zero_mean_grad(&eh, nullptr, nullptr, (double*)(B + 2 * S), (void*)(B + 5 * S), 64,
+                         nullptr) == ZERO_OK);
+    CHECK(g_rec.size() == 2 && g_rec[0].len == 0 && g_rec[1].kind == 3 && g_rec[1].len == 1);
+    // one piece when the call fits one launch
+    zero_hparams oh = hp(L, 2, -1, ZERO_MODE_F32);
+    g_rec.clear();
+    CHECK(zero_step(&oh, (void*)B, bg, &cst, 1, nullptr) == ZERO_OK);
+    CHECK(g_rec.size() == 1 && g_rec[0].len == L);
+  }
+
   // NULL everywhere
   CHECK(zero_step(nullptr, nullptr, nullptr, nullptr, 1, nullptr) == ZERO_EINVAL);
   CHECK(zero_init_states(nullptr, nullptr, nullptr, nullptr) == ZERO_EINVAL);

@@ -212,6 +212,36 @@ def test_rank_mode_clipping_by_summed_shard_norms(oracle):
         compare(f"rank {r} m", host(st.m), ref[2][a:b], "f32")
 
 
+def test_mean_grad_past_one_launch(oracle):
+    """n = 2^32 + 1001 in bf16 mixed precision, N = 2: the mean is enqueued as two
+    launches (2^32 elements, then 1001) whose block partials one finalize sums.
+    Sampled means, the seam between the launches included, are bit-exact with
+    the oracle's (the mean is elementwise); the squared norm agrees with an fp64
+    sum of the same squares, in another order, within the order bound."""
+    n, N = (1 << 32) + 1001, 2
+    wl = synth.scaled(W["mixed-1B-n8"], n, n_workers=N, worker_scale=None)
+    say(f"[case] mean grad past one launch n={n} N={N}")
+    grads = synth.make_grads(wl, 1, "cuda")
+    hp = z.HParams(n=n, n_workers=N, mode=MODE_MIXED, lr=wl.lr, beta1=wl.beta1,
+                   beta2=wl.beta2, eps=wl.eps)
+    mean = torch.empty(n, dtype=torch.float32, device="cuda")
+    ws = _ws(z.zero_mean_grad_workspace_bytes(hp))
+    ss = _dev_double()
+    z.zero_mean_grad(hp, grads, mean, ss, ws)
+    idx = np.union1d(synth.sample_indices(wl, 1 << 18),
+                     np.arange((1 << 32) - 64, (1 << 32) + 64))
+    idx_d = torch.from_numpy(idx).to("cuda")
+    g_h = [host(g[idx_d]) for g in grads]
+    del grads
+    mean_h, _ = oracle.mean_grad(MODE_MIXED, idx.size, N, g_h)
+    compare("mean", host(mean[idx_d]), mean_h, "exact")
+    ref = 0.0
+    for i in range(0, n, 1 << 28):
+        ref += float(torch.sum(mean[i:i + (1 << 28)].double() ** 2).item())
+    assert sumsq_close(float(ss.item()), ref, n), (ss.item(), ref)
+    say(f"  squared norm {ss.item():.9g} against {ref:.9g}; {idx.size} sampled means bit-exact")
+
+
 def test_clipped_step_full_size_fp32_320M_n8(oracle):
     """The fp32 320M-parameter 8-worker workload at full size with clipping
     active: the global norm needs every element, so the oracle sees all of them

@@ -260,6 +260,14 @@ def test_more_than_2_31_elements_mixed(oracle):
     run_sampled(oracle, wl, steps=2, count=1 << 18)
 
 
+def test_more_than_2_32_elements_in_two_launches(oracle):
+    """Mixed precision with N = 2 over 2^32 + 1001 elements: the library enqueues
+    the step as two launches (2^32 elements, then 1001) on offset views. The last
+    4096 sampled elements straddle the seam between them."""
+    wl = synth.scaled(W["mixed-1B-n8"], (1 << 32) + 1001, n_workers=2)
+    run_sampled(oracle, wl, steps=2, count=1 << 18)
+
+
 def test_last_rank_share_of_8B(oracle):
     """Rank 7 of n = 8e9: its slot in the gathered bf16 buffer starts 14 GB in;
     everything outside the slot stays unchanged."""

@@ -392,6 +392,78 @@ zero_status check_not_written(const zlaunch::StepArgs& la, const Widths& wd, con
   return ZERO_OK;
 }
 
+// Element widths of hp's mode; only called after the mode has been validated.
+Widths range_widths(const zero_hparams* hp) {
+  Widths wd{};
+  mode_widths(hp->mode, &wd);
+  return wd;
+}
+
+// Moves a built launch `off` elements forward: the same step on offset views.
+// gelem: bytes per element of la->grads.
+void offset_step(zlaunch::StepArgs* la, int64_t off, const Widths& wd, int64_t gelem) {
+  for (int k = 0; k < la->n_workers; ++k)
+    la->grads[k] = static_cast<const char*>(la->grads[k]) + off * gelem;
+  la->w = static_cast<char*>(la->w) + off * wd.state;
+  la->m = static_cast<char*>(la->m) + off * wd.state;
+  if (la->v) la->v = static_cast<char*>(la->v) + off * wd.state;  // NULL for SGD
+  if (la->out) la->out = static_cast<char*>(la->out) + off * wd.param;
+  la->mask_bit_offset += off;
+}
+
+// Enqueues a built step as launches of at most zlaunch::kLaunchElems elements
+// each, in order, on consecutive offset views (the step is elementwise, so the
+// pieces compute exactly what one launch would).
+const char* launch_pieces(const zlaunch::StepArgs& la, const Widths& wd, int64_t gelem,
+                          bool from_mean, void* stream) {
+  auto one = [&](const zlaunch::StepArgs& x) {
+    return from_mean ? zlaunch::launch_step_mean(x, stream) : zlaunch::launch_step(x, stream);
+  };
+  if (la.len <= zlaunch::kLaunchElems) return one(la);
+  for (int64_t off = 0; off < la.len; off += zlaunch::kLaunchElems) {
+    zlaunch::StepArgs piece = la;
+    offset_step(&piece, off, wd, gelem);
+    piece.len = std::min(zlaunch::kLaunchElems, la.len - off);
+    if (const char* err = one(piece)) return err;
+  }
+  return nullptr;
+}
+
+// Block partials the mean writes for a range of len, summed over the launches
+// the range is split into (at least one launch, also for len == 0).
+int64_t partials_count(int mode, int64_t len) {
+  int64_t total = 0, off = 0;
+  do {
+    const int64_t piece = std::min(zlaunch::kLaunchElems, len - off);
+    total += zlaunch::mean_partials(mode, piece);
+    off += piece;
+  } while (off < len);
+  return total;
+}
+
+// Enqueues the mean of ma's range as launches of at most kLaunchElems
+// elements, their partials back to back from ma.partials, then, if sumsq_out,
+// the fixed-order sum of all partials_count(mode, len) of them.
+const char* launch_mean_pieces(const zlaunch::MeanArgs& ma, const Widths& wd, double* sumsq_out,
+                               void* stream) {
+  int64_t off = 0, np = 0;
+  do {
+    zlaunch::MeanArgs piece = ma;
+    piece.len = std::min(zlaunch::kLaunchElems, ma.len - off);
+    if (off > 0) {
+      for (int k = 0; k < ma.n_workers; ++k)
+        piece.grads[k] = static_cast<const char*>(ma.grads[k]) + off * wd.grad;
+      piece.mean = static_cast<char*>(ma.mean) + off * wd.state;
+    }
+    piece.partials = ma.partials ? ma.partials + np : nullptr;
+    np += zlaunch::mean_partials(ma.mode, piece.len);
+    if (const char* err = zlaunch::launch_mean(piece, stream)) return err;
+    off += piece.len;
+  } while (off < ma.len);
+  if (sumsq_out != nullptr) return zlaunch::launch_sumsq_finalize(ma.partials, np, sumsq_out, stream);
+  return nullptr;
+}
+
 // Validation and launch arguments shared by zero_step_range and
 // zero_step_range_dev: the range [begin, end) of the call's index space as
 // offset views of the full-length buffers.
@@ -415,13 +487,7 @@ zero_status build_range(const zero_hparams* hp, void* param, const void* const* 
   *nothing = empty || begin == end;
   if (*nothing) return ZERO_OK;
   // Elementwise: the sub-range is the same step on offset views.
-  for (int k = 0; k < la->n_workers; ++k)
-    la->grads[k] = static_cast<const char*>(la->grads[k]) + begin * wd.grad;
-  la->w = static_cast<char*>(la->w) + begin * wd.state;
-  la->m = static_cast<char*>(la->m) + begin * wd.state;
-  if (la->v) la->v = static_cast<char*>(la->v) + begin * wd.state;  // NULL for SGD
-  if (la->out) la->out = static_cast<char*>(la->out) + begin * wd.param;
-  la->mask_bit_offset += begin;
+  offset_step(la, begin, wd, wd.grad);
   la->len = end - begin;
   return ZERO_OK;
 }
@@ -435,7 +501,7 @@ ClipLayout clip_layout(int mode, int64_t len, int64_t state_bytes) {
   ClipLayout l;
   l.mean_off = 0;
   l.partials_off = align_up(len * state_bytes, 256);
-  l.sumsq_off = l.partials_off + align_up(zlaunch::mean_partials(mode, len) * 8, 256);
+  l.sumsq_off = l.partials_off + align_up(partials_count(mode, len) * 8, 256);
   l.total = l.sumsq_off + 8;
   return l;
 }
@@ -461,7 +527,7 @@ zero_status zero_step(const zero_hparams* hp, void* param, const void* const* gr
   const int N = hp->n_workers >= 1 && hp->n_workers <= ZERO_MAX_WORKERS ? hp->n_workers : 0;
   zero_status s = build_step(hp, param, grads, N, wd.grad, st, t, &la, &empty, &a, &b);
   if (s != ZERO_OK || empty) return s == ZERO_OK ? ok() : s;
-  const char* err = zlaunch::launch_step(la, stream);
+  const char* err = launch_pieces(la, wd, wd.grad, false, stream);
   if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
   return ok();
 }
@@ -473,7 +539,8 @@ zero_status zero_step_range(const zero_hparams* hp, void* param, const void* con
   bool nothing = false;
   zero_status s = build_range(hp, param, grads, st, t, begin, end, &la, &nothing);
   if (s != ZERO_OK || nothing) return s == ZERO_OK ? ok() : s;
-  const char* err = zlaunch::launch_step(la, stream);
+  const Widths wd = range_widths(hp);
+  const char* err = launch_pieces(la, wd, wd.grad, false, stream);
   if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
   return ok();
 }
@@ -523,7 +590,8 @@ zero_status zero_step_buckets(const zero_hparams* hp, void* param, const void* c
     s = build_range(hp, param, grads, st, t, lo, hi, &la, &nothing);
     if (s != ZERO_OK) return s;  // not reached: validated above
     if (nothing) continue;
-    const char* err = zlaunch::launch_step(la, stream);
+    const Widths wd = range_widths(hp);
+    const char* err = launch_pieces(la, wd, wd.grad, false, stream);
     if (err) return fail(ZERO_EHIP, "bucket %d: step launch failed: %s", i, err);
   }
   return ok();
@@ -560,7 +628,7 @@ zero_status zero_step_range_dev(const zero_hparams* hp, void* param, const void*
   s = check_not_written(la, wd, dev_scalars, sizeof(zero_step_scalars), "dev_scalars");
   if (s != ZERO_OK) return s;
   la.dyn = dev_scalars;
-  const char* err = zlaunch::launch_step(la, stream);
+  const char* err = launch_pieces(la, wd, wd.grad, false, stream);
   if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
   return ok();
 }
@@ -571,7 +639,7 @@ zero_status zero_mean_grad_workspace_bytes(const zero_hparams* hp, size_t* bytes
   if (bytes == nullptr) return fail(ZERO_EINVAL, "bytes is NULL");
   zero_status s = check_hparams(hp, false, &wd, &a, &b);
   if (s != ZERO_OK) return s;
-  *bytes = (size_t)(zlaunch::mean_partials(hp->mode, b - a) * 8);
+  *bytes = (size_t)(partials_count(hp->mode, b - a) * 8);
   return ok();
 }
 
@@ -584,7 +652,7 @@ zero_status zero_mean_grad(const zero_hparams* hp, const void* const* grads, voi
   if (s != ZERO_OK) return s;
   const int64_t len = b - a;
   const int N = hp->n_workers;
-  const int64_t need = zlaunch::mean_partials(hp->mode, len) * 8;
+  const int64_t need = partials_count(hp->mode, len) * 8;
   if (sumsq_out != nullptr) {
     if (!aligned(sumsq_out, 8)) return fail(ZERO_EINVAL, "sumsq_out must be 8-byte aligned");
     if (workspace == nullptr || !aligned(workspace, 16) || (int64_t)workspace_bytes < need)
@@ -596,8 +664,7 @@ zero_status zero_mean_grad(const zero_hparams* hp, const void* const* grads, voi
   ma.n_workers = N;
   ma.len = len;
   ma.n_workers_value = (double)N;
-  ma.partials = static_cast<double*>(workspace);
-  ma.sumsq_out = sumsq_out;
+  ma.partials = sumsq_out ? static_cast<double*>(workspace) : nullptr;
   if (len > 0) {
     if (grads == nullptr) return fail(ZERO_EINVAL, "grads is NULL");
     if (mean_out == nullptr || !aligned(mean_out, 16))
@@ -620,7 +687,7 @@ zero_status zero_mean_grad(const zero_hparams* hp, const void* const* grads, voi
     for (int k = 0; k < N; ++k) ma.grads[k] = grads[k];
   }
   if (len == 0 && sumsq_out == nullptr) return ok();  // an empty shard: nothing to do
-  const char* err = zlaunch::launch_mean(ma, stream);
+  const char* err = launch_mean_pieces(ma, wd, sumsq_out, stream);
   if (err) return fail(ZERO_EHIP, "mean launch failed: %s", err);
   return ok();
 }
@@ -647,7 +714,7 @@ zero_status zero_step_mean(const zero_hparams* hp, void* param, const void* mean
     return s;
   la.clip_sumsq = clip_sumsq;
   la.max_norm = max_norm;
-  const char* err = zlaunch::launch_step_mean(la, stream);
+  const char* err = launch_pieces(la, wd, wd.state, true, stream);
   if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
   return ok();
 }
@@ -718,8 +785,7 @@ zero_status zero_step_clipped(const zero_hparams* hp, void* param, const void* c
   ma.len = len;
   ma.n_workers_value = (double)N;
   ma.partials = reinterpret_cast<double*>(ws + L.partials_off);
-  ma.sumsq_out = sumsq;
-  const char* err = zlaunch::launch_mean(ma, stream);
+  const char* err = launch_mean_pieces(ma, wd, sumsq, stream);
   if (err) return fail(ZERO_EHIP, "mean launch failed: %s", err);
   la.n_workers = 1;
   la.grads[0] = ws + L.mean_off;
@@ -727,7 +793,7 @@ zero_status zero_step_clipped(const zero_hparams* hp, void* param, const void* c
   la.n_workers_value = 1.0;
   la.clip_sumsq = sumsq;
   la.max_norm = max_norm;
-  err = zlaunch::launch_step_mean(la, stream);
+  err = launch_pieces(la, wd, wd.state, true, stream);
   if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
   return ok();
 }

@@ -947,10 +947,7 @@ void launch_mean_n(const zlaunch::MeanArgs& a, hipStream_t st) {
   for (int k = 0; k < CAP; ++k) gs.p[k] = k < a.n_workers ? a.grads[k] : nullptr;
   hipLaunchKernelGGL((zero_mean_kernel<M, NFIX, CAP, BLOCK, C>), dim3((unsigned)blocks),
                      dim3(BLOCK), 0, st, gs, a.n_workers, static_cast<S*>(a.mean), a.len,
-                     (S)a.n_workers_value, a.sumsq_out ? a.partials : nullptr);
-  if (a.sumsq_out)
-    hipLaunchKernelGGL(zero_sumsq_finalize, dim3(1), dim3(kFinalBlock), 0, st, a.partials,
-                       blocks, a.sumsq_out);
+                     (S)a.n_workers_value, a.partials);
 }
 
 template <class M>
@@ -1030,6 +1027,16 @@ const char* launch_mean(const MeanArgs& a, void* stream) {
     case 3: launch_mean_mode<ModeMixedF16>(a, st); break;
     default: return "unknown mode";
   }
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? nullptr : hipGetErrorString(e);
+}
+
+const char* launch_sumsq_finalize(const double* partials, int64_t count, double* out,
+                                  void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(zero_sumsq_finalize, dim3(1), dim3(kFinalBlock), 0, st, partials, count,
+                     out);
   const hipError_t e = hipGetLastError();
   return e == hipSuccess ? nullptr : hipGetErrorString(e);
 }

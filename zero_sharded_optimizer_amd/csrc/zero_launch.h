@@ -9,18 +9,25 @@ namespace zlaunch {
 
 constexpr int kMaxWorkers = 256;
 
+// Largest element count one launch covers; the host layer enqueues a longer
+// call as consecutive launches on offset views. It is a multiple of every
+// kernel's tile (at most 4096 elements), so each piece but the last is whole
+// tiles, and in every launch shape blocks x threads stays below the 2^32
+// work-items one dispatch can describe.
+constexpr int64_t kLaunchElems = INT64_C(1) << 32;
+
 // Everything one fused step launch needs. All pointers are device addresses
 // that the ABI layer has validated (alignment, extents, no overlap of written
 // ranges).
 struct StepArgs {
-  int mode;        // 0 fp64, 1 fp32, 2 mixed bf16/fp32
+  int mode;        // 0 fp64, 1 fp32, 2 mixed bf16/fp32, 3 mixed fp16/fp32
   int n_workers;   // 1..kMaxWorkers
   const void* grads[kMaxWorkers];  // rank order; element j of worker k at grads[k][j]
   void* w;         // master values (S): the parameter itself when updated in place
   void* m;         // S
   void* v;         // S
   void* out;       // gathered parameter slot (P) written from w, or nullptr (in place)
-  int64_t len;     // elements this launch updates
+  int64_t len;     // elements this launch updates, at most kLaunchElems
   const uint32_t* mask;     // decay bitmask or nullptr
   int64_t mask_bit_offset;  // bit index of element 0
   int decay_kind;  // 0 no decay, 1 every element, 2 per the bitmask
@@ -47,16 +54,16 @@ struct DynScalars {
   int64_t t;            // the 1-based step number
 };
 
-// The materialised reduce-scatter mean of one call's range.
+// The materialised reduce-scatter mean of one launch's range.
 struct MeanArgs {
   int mode;
   int n_workers;
   const void* grads[kMaxWorkers];
   void* mean;            // len elements of S
-  int64_t len;
+  int64_t len;           // at most kLaunchElems
   double n_workers_value;
-  double* partials;      // mean_partials(mode, len) doubles, used when sumsq_out
-  double* sumsq_out;     // device double, or nullptr
+  double* partials;      // mean_partials(mode, len) per-block sums of the squared
+                         // mean, or nullptr when no norm is wanted
 };
 
 struct InitArgs {
@@ -76,6 +83,9 @@ const char* launch_step_mean(const StepArgs& a, void* stream);
 const char* launch_mean(const MeanArgs& a, void* stream);
 // Number of per-block partial sums launch_mean writes for a range of len.
 int64_t mean_partials(int mode, int64_t len);
+// *out = the sum of partials[0 .. count), in a fixed order.
+const char* launch_sumsq_finalize(const double* partials, int64_t count, double* out,
+                                  void* stream);
 // Makes later work on `stream` wait for `event` (a hipEvent_t) to complete.
 const char* stream_wait(void* stream, void* event);
 
