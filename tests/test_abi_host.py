@@ -442,3 +442,30 @@ def test_step_mean_rejects_a_clip_norm_inside_an_output():
     for norm in (A + (1 << 24) + 64, A + 8, A + (2 << 24)):
         rc = lib.zero_step_mean(C.byref(hp), A, mean, C.byref(st), 1, norm, 1.0, None)
         assert rc == z.ZERO_EINVAL and "clip_sumsq overlaps" in lib.zero_last_error().decode()
+
+
+def test_binding_rejects_tensors_on_several_devices():
+    """The binding checks that one call's tensors share a device, and that a
+    torch stream given for the call is on that device (fake tensors: only the
+    device attribute is read)."""
+    class Fake:
+        def __init__(self, dev):
+            self.device = dev
+
+        def data_ptr(self):
+            return A
+
+    class FakeStream:
+        def __init__(self, dev):
+            self.device = dev
+
+    z._same_device(None, Fake("cuda:0"), [Fake("cuda:0"), None, A],
+                   z.States(None, Fake("cuda:0"), None))
+    with pytest.raises(ValueError, match="one device"):
+        z._same_device(None, Fake("cuda:0"), [Fake("cuda:1")])
+    with pytest.raises(ValueError, match="one device"):
+        z._same_device(None, Fake("cuda:0"), z.States(Fake("cuda:1"), Fake("cuda:0"), None))
+    with pytest.raises(ValueError, match="stream is on"):
+        z._same_device(FakeStream("cuda:1"), Fake("cuda:0"))
+    z._same_device(FakeStream("cuda:0"), Fake("cuda:0"))
+    z._same_device(FakeStream("cuda:3"))  # no tensors: nothing to compare

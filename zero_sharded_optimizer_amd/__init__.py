@@ -141,6 +141,30 @@ def _check_tensor(x, dtype_name, numel, what):
         raise ValueError(f"{what}: {x.numel()} elements, the call touches {numel}")
 
 
+def _tensor_args(xs):
+    for x in xs:
+        if x is None or isinstance(x, int):
+            continue
+        if isinstance(x, (list, tuple)):
+            yield from _tensor_args(x)
+        elif isinstance(x, States):
+            yield from _tensor_args((x.master, x.m, x.v))
+        elif hasattr(x, "device") and hasattr(x, "data_ptr"):
+            yield x
+
+
+def _same_device(stream, *xs):
+    """The tensors of one call live on one GPU, and a torch stream passed for it
+    belongs to that GPU: the library launches on the stream with the pointers
+    as given, so a buffer on another device would be a bad address there."""
+    devs = {str(x.device) for x in _tensor_args(xs)}
+    if len(devs) > 1:
+        raise ValueError(f"all tensors of one call must be on one device, got {sorted(devs)}")
+    sdev = getattr(stream, "device", None)
+    if devs and sdev is not None and str(sdev) not in devs:
+        raise ValueError(f"stream is on {sdev}, the tensors on {devs.pop()}")
+
+
 def _stream_handle(stream, like):
     if stream is None:
         import torch
@@ -189,6 +213,7 @@ def _check_common(hp, param, states):
 def zero_init_states(hp: HParams, param, states: States, stream=None) -> None:
     """Enqueue init_states: m = v = 0, master = widen(param) (see zero_adam.h)."""
     _check_common(hp, param, states)
+    _same_device(stream, param, states, hp.wd_mask)
     lib = _abi.load()
     c_hp, c_st = hp.to_c(), states.to_c()
     st = lib.zero_init_states(C.byref(c_hp), _addr(param), C.byref(c_st),
@@ -206,6 +231,7 @@ def zero_step(hp: HParams, param, grads: Sequence, states: States, t: int, strea
             raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
         for k, g in enumerate(grads):
             _check_tensor(g, g_dt, glen, f"grads[{k}]")
+    _same_device(stream, param, grads, states, hp.wd_mask)
     lib = _abi.load()
     c_hp, c_st = hp.to_c(), states.to_c()
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
@@ -225,6 +251,7 @@ def zero_step_range(hp: HParams, param, grads: Sequence, states: States, t: int,
             raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
         for k, g in enumerate(grads):
             _check_tensor(g, g_dt, glen, f"grads[{k}]")
+    _same_device(stream, param, grads, states, hp.wd_mask)
     lib = _abi.load()
     c_hp, c_st = hp.to_c(), states.to_c()
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
@@ -253,6 +280,7 @@ def zero_step_buckets(hp: HParams, param, grads: Sequence, states: States, t: in
             _check_tensor(g, g_dt, glen, f"grads[{k}]")
     if events is not None and len(events) != len(buckets):
         raise ValueError(f"events: {len(events)} for {len(buckets)} buckets")
+    _same_device(stream, param, grads, states, hp.wd_mask)
     lib = _abi.load()
     c_hp, c_st = hp.to_c(), states.to_c()
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
@@ -297,6 +325,7 @@ def zero_step_range_dev(hp: HParams, param, grads: Sequence, states: States, sca
         for k, g in enumerate(grads):
             _check_tensor(g, g_dt, glen, f"grads[{k}]")
     _check_bytes(scalars, STEP_SCALARS_BYTES, "scalars")
+    _same_device(stream, param, grads, states, hp.wd_mask, scalars)
     lib = _abi.load()
     c_hp, c_st = hp.to_c(), states.to_c()
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
@@ -353,6 +382,7 @@ def zero_mean_grad(hp: HParams, grads: Sequence, mean_out, sumsq_out=None, works
         _check_double(sumsq_out, "sumsq_out")
         if sumsq_out is not None:
             _check_bytes(workspace, zero_mean_grad_workspace_bytes(hp), "workspace")
+    _same_device(stream, grads, mean_out, sumsq_out, workspace)
     lib = _abi.load()
     c_hp = hp.to_c()
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
@@ -371,6 +401,7 @@ def zero_step_mean(hp: HParams, param, mean_grad, states: States, t: int, clip_s
         _, glen = chk
         _check_tensor(mean_grad, _DTYPES[hp.mode][2], glen, "mean_grad")
         _check_double(clip_sumsq, "clip_sumsq")
+    _same_device(stream, param, mean_grad, states, hp.wd_mask, clip_sumsq)
     lib = _abi.load()
     c_hp, c_st = hp.to_c(), states.to_c()
     st = lib.zero_step_mean(C.byref(c_hp), _addr(param), _addr(mean_grad), C.byref(c_st), int(t),
@@ -402,6 +433,7 @@ def zero_step_clipped(hp: HParams, param, grads: Sequence, states: States, t: in
         _check_double(sumsq_out, "sumsq_out")
         if hp.rank < 0:
             _check_bytes(workspace, zero_step_clipped_workspace_bytes(hp), "workspace")
+    _same_device(stream, param, grads, states, hp.wd_mask, sumsq_out, workspace)
     lib = _abi.load()
     c_hp, c_st = hp.to_c(), states.to_c()
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
