@@ -236,3 +236,76 @@ def test_functional_zero_step(oracle, precision):
     compare("param", host(new_p), p_o, "f32" if precision == "fp32" else "bf16")
     compare("m", host(new_st.m), m_o, "f32")
     compare("v", host(new_st.v), v_o, "f32")
+
+
+def test_clipped_steps_match_torch_clip_grad_norm():
+    """step(max_norm) clips the averaged gradient by its global norm before
+    AdamW: one process's torch clip_grad_norm_ + AdamW in fp64 (1e-10), with
+    the clip active on every step, and grad_norm() equal to torch's norm."""
+    lr, wd, max_norm = 0.05, 0.1, 0.05
+    ref = _model(21)
+    model = copy.deepcopy(ref).cuda()
+    zo = ZeroOptimizer(model.parameters(), 4, 2, precision="fp64", lr=lr, weight_decay=wd)
+    opt = torch.optim.AdamW(ref.parameters(), lr=lr, weight_decay=wd)
+    for batch in _batches(23, 4, 4):
+        zo.zero_grad()
+        for k, (x, y) in enumerate(batch):
+            model.zero_grad()
+            _loss(model, x.cuda(), y.cuda()).backward()
+            for dst, p in zip(zo.worker_grads(k), model.parameters()):
+                dst.copy_(p.grad)
+        zo.step(max_norm=max_norm)
+        opt.zero_grad()
+        (sum(_loss(ref, x, y) for x, y in batch) / 4).backward()
+        norm = float(torch.nn.utils.clip_grad_norm_(ref.parameters(), max_norm))
+        opt.step()
+        assert norm > max_norm  # the clip is active
+        assert abs(zo.grad_norm() - norm) <= 1e-12 * norm
+    torch.cuda.synchronize()
+    for p, q in zip(model.parameters(), ref.parameters()):
+        assert torch.allclose(p.detach().cpu(), q.detach(), rtol=0, atol=1e-10)
+
+
+def test_clipped_step_equals_the_abi_call(oracle):
+    """bf16 mixed precision: ZeroOptimizer.step(max_norm) is the ABI's clipped
+    step, bit for bit, and an unreachable threshold gives the plain step."""
+    model = _model(4, torch.bfloat16).cuda()
+    zo = ZeroOptimizer(model.parameters(), 3, 1, precision="bf16", lr=1e-2)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for buf in zo.grads:
+        buf.copy_(torch.randn(buf.shape, generator=g, device="cuda").to(torch.bfloat16))
+    p0 = zo.flat.clone()
+    st0 = z.States(zo.states.master.clone(), zo.states.m.clone(), zo.states.v.clone())
+    zo.step(max_norm=0.1)
+    ws = torch.empty(z.zero_step_clipped_workspace_bytes(zo.hp), dtype=torch.uint8,
+                     device="cuda")
+    z.zero_step_clipped(zo.hp, p0, zo.grads, st0, 1, 0.1, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(zo.flat), host(p0))
+    assert np.array_equal(host(zo.states.master), host(st0.master))
+    plain = ZeroOptimizer([torch.zeros(1, dtype=torch.bfloat16, device="cuda")], 1, 1,
+                          precision="bf16", lr=1e-2)
+    plain.flat.copy_(zo.flat[:1])
+    plain.states.master.copy_(zo.states.master[:1])
+    saved = plain.state_dict()
+    plain.grads[0].copy_(zo.grads[0][:1])
+    plain.step(max_norm=1e30)
+    a = plain.state_dict()
+    plain.load_state_dict(saved)
+    plain.step()
+    b = plain.state_dict()
+    for k in ("param", "master", "m", "v"):
+        assert np.array_equal(host(a[k]), host(b[k])), k
+
+
+def test_averaged_grad_is_the_step_mean(oracle):
+    """averaged_grad() is the reduce-scatter mean of the workers' gradients,
+    bit-exact with the oracle's (what stage 1 keeps in .grad)."""
+    model = _model(6, torch.float32).cuda()
+    zo = ZeroOptimizer(model.parameters(), 5, 1, precision="fp32", lr=1e-3)
+    g = torch.Generator(device="cuda").manual_seed(9)
+    for buf in zo.grads:
+        buf.copy_(torch.randn(buf.shape, generator=g, device="cuda"))
+    mean = zo.averaged_grad()
+    ref, _ = oracle.mean_grad(MODE_F32, zo.n, 5, [host(b) for b in zo.grads])
+    compare("mean", host(mean), ref, "exact")

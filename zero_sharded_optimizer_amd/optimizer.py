@@ -11,9 +11,12 @@ On one GPU the N logical workers share one HBM, so the optimizer keeps:
     (worker_grads(k)) that worker k's backward pass (or a copy) fills;
   * the optimizer state as flat device buffers (fp32 master in mixed precision,
     m, v), each worker's shard being its [a_r, b_r) view.
-step() runs one fused zero_step over all of it. The stage only changes the
-memory model (memory_bytes), as on the pages: sharding moves storage between
-ranks and leaves the arithmetic unchanged.
+step() runs one fused zero_step over all of it; step(max_norm=...) first clips
+the averaged gradient by its global norm (the same page, section "Going
+further": a sum of the chunks' squared norms before the update). The stage only
+changes the memory model (memory_bytes), as on the pages: sharding moves
+storage between ranks and leaves the arithmetic unchanged. averaged_grad()
+gives what stage 1 keeps in .grad after a step: the averaged full gradient.
 
 This module is argument marshalling only: every step of the computation runs
 in libzero.so's HIP kernels.
@@ -99,6 +102,8 @@ class ZeroOptimizer:
                             momentum=momentum, dampening=dampening, nesterov=nesterov)
         z.zero_init_states(self.hp, self.flat, self.states)
         self.t = 0
+        self._clip_ws = None   # the clipped step's workspace, allocated on first use
+        self._sumsq = None     # device double: the last clipped step's squared norm
 
     # -- the training step ------------------------------------------------------
     def worker_grads(self, k: int) -> List:
@@ -116,11 +121,40 @@ class ZeroOptimizer:
         """Stage 3's gather of the full parameters before forward. On one GPU every
         worker reads the one gathered buffer, so there is nothing to move."""
 
-    def step(self, stream=None) -> None:
+    def step(self, max_norm: Optional[float] = None, stream=None) -> None:
         """One fused step (reduce-scatter mean, Adam/SGD on each shard,
-        all-gather) over the workers' gradient buffers, enqueued on `stream`."""
+        all-gather) over the workers' gradient buffers, enqueued on `stream`.
+        With max_norm, the averaged gradient is first scaled by
+        min(1, max_norm / (norm + 1e-6)), its global norm taken over every shard;
+        grad_norm() then returns that norm."""
         self.t += 1
-        z.zero_step(self.hp, self.flat, self.grads, self.states, self.t, stream=stream)
+        if max_norm is None:
+            z.zero_step(self.hp, self.flat, self.grads, self.states, self.t, stream=stream)
+            return
+        import torch
+        if self._clip_ws is None:
+            nbytes = z.zero_step_clipped_workspace_bytes(self.hp)
+            self._clip_ws = torch.empty(nbytes, dtype=torch.uint8, device=self.flat.device)
+            self._sumsq = torch.zeros(1, dtype=torch.float64, device=self.flat.device)
+        z.zero_step_clipped(self.hp, self.flat, self.grads, self.states, self.t, max_norm,
+                            self._clip_ws, sumsq_out=self._sumsq, stream=stream)
+
+    def grad_norm(self) -> float:
+        """The global norm of the averaged gradient of the last clipped step
+        (waits for that step to finish)."""
+        if self._sumsq is None:
+            raise RuntimeError("grad_norm: no clipped step has run")
+        return float(self._sumsq.item()) ** 0.5
+
+    def averaged_grad(self, stream=None):
+        """The averaged full gradient (1/N) sum_k g_k, as a new flat device tensor
+        of the state dtype: what stage 1 leaves in .grad until zero_grad(). The
+        same rank-order fold and division as the step, so it is bit-identical to
+        the gradient the step used."""
+        import torch
+        mean = torch.empty(self.n, dtype=self.states.m.dtype, device=self.flat.device)
+        z.zero_mean_grad(self.hp, self.grads, mean, stream=stream)
+        return mean
 
     # -- memory and checkpoints -------------------------------------------------
     def memory_bytes(self, rank: int = 0, convention: int = 0) -> Dict[str, int]:
