@@ -42,3 +42,11 @@ def test_parameters_must_be_device_tensors_of_the_mode():
 def test_mixed_init_states_needs_the_parameters():
     with pytest.raises(ValueError, match="pass param"):
         init_states(10, 2, device="cpu", precision="bf16")
+
+
+def test_zero_rejects_a_repeated_parameter():
+    """A tensor listed twice would get two slices of the gathered buffer and be
+    stepped twice per step."""
+    t = object()
+    with pytest.raises(ValueError, match="more than once"):
+        ZeroOptimizer([t, object(), t], 2, 1)

@@ -65,6 +65,8 @@ class ZeroOptimizer:
             raise ValueError("optimizer must be 'adamw' or 'sgd'")
         if decay is not None and len(decay) != len(params):
             raise ValueError("decay: one flag per parameter tensor")
+        if len({id(p) for p in params}) != len(params):
+            raise ValueError("a parameter appears more than once")
         import torch
         mode, pdt, sdt = _MODE_DTYPE[precision]
         pdt, sdt = getattr(torch, pdt), getattr(torch, sdt)
