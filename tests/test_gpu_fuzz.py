@@ -85,7 +85,7 @@ def _buckets(rng, L):
     return pairs
 
 
-@pytest.mark.parametrize("seed", range(120))
+@pytest.mark.parametrize("seed", range(400))
 def test_random_configuration_matches_the_oracle(oracle, seed):
     c, rng = _draw(seed)
     mode, n, N, rank = c["mode"], c["n"], c["N"], c["rank"]
