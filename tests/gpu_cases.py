@@ -20,6 +20,27 @@ def host(x):
     return x.cpu().numpy().copy()
 
 
+def device_bytes(wl):
+    """Device memory a sampled full-size run of wl holds at its peak: the N
+    gradients, the gathered parameters, master/m/v, and one fp32 draw buffer of
+    the generators."""
+    import torch
+    G = torch.empty(0, dtype=synth.param_dtype(wl)).element_size()
+    S = torch.empty(0, dtype=synth.state_dtype(wl)).element_size()
+    L = wl.length
+    return wl.n_workers * L * G + wl.n * G + 3 * L * S + 4 * L
+
+
+def need_free(nbytes):
+    """Skip (with the reason) when the device has less than nbytes free plus a
+    tenth: such a case would fail on memory, and under -x stop every later test."""
+    import pytest
+    import torch
+    free, _ = torch.cuda.mem_get_info()
+    if free < 1.1 * nbytes:
+        pytest.skip(f"needs {nbytes / 1e9:.0f} GB of free device memory, {free / 1e9:.0f} GB free")
+
+
 def kinds(wl):
     """(param kind, state kind) of the parity bar for a workload's mode."""
     if wl.mode == MODE_F64:
@@ -114,6 +135,7 @@ def run_sampled(O, wl, steps, count, compare_steps=None):
     import torch
     say(f"[case] sampled compare {wl.name}: mode={wl.mode} n={wl.n} N={wl.n_workers} "
         f"rank={wl.rank} steps={steps}")
+    need_free(device_bytes(wl))
     hp, param, st, flags = setup(wl)
     a, b = wl.shard
     idx = synth.sample_indices(wl, count)

@@ -28,7 +28,7 @@ import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
 from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from oracle.compare import compare  # noqa: E402
-from gpu_cases import host, kinds, say, setup  # noqa: E402
+from gpu_cases import host, kinds, need_free, say, setup  # noqa: E402
 
 W = synth.WORKLOADS
 BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"],
@@ -221,6 +221,7 @@ def test_mean_grad_past_one_launch(oracle):
     n, N = (1 << 32) + 1001, 2
     wl = synth.scaled(W["mixed-1B-n8"], n, n_workers=N, worker_scale=None)
     say(f"[case] mean grad past one launch n={n} N={N}")
+    need_free(N * n * 2 + n * 4 + 4 * n)  # gradients, the mean, one draw buffer
     grads = synth.make_grads(wl, 1, "cuda")
     hp = z.HParams(n=n, n_workers=N, mode=MODE_MIXED, lr=wl.lr, beta1=wl.beta1,
                    beta2=wl.beta2, eps=wl.eps)
