@@ -25,12 +25,12 @@
 //     Requirements", "Sharding Parameters", "Synchronizing Parameters".
 //
 // Readings where the pages are silent (each is also listed in the design notes):
-//   * The Adam formula is not printed ("adam_update is given"). Taken as textbook
-//     bias-corrected Adam with eps outside the square root, the only form that
-//     gives the pages' first step (move by lr against the mean gradient, eps
-//     touching the eighth digit).
-//   * Weight decay ("AdamW with decay", no formula): decoupled, multiplicative
-//     w <- w * (1 - lr*wd) applied to the pre-update w.
+//   * The Adam formula is not printed (the page treats adam_update as given).
+//     Taken as textbook bias-corrected Adam with eps outside the square root,
+//     the only form that gives the pages' first step (move by lr against the
+//     mean gradient, eps touching the eighth digit).
+//   * Weight decay (AdamW with decay is named, no formula): decoupled,
+//     multiplicative w <- w * (1 - lr*wd) applied to the pre-update w.
 //   * Mean: sum the N worker gradients left to right in rank order, then one
 //     division by N.
 //   * One fixed operation order per element, every operation a single IEEE
@@ -57,12 +57,12 @@
 //     coupled L2 decay, the buffer set to the first step's gradient, optional
 //     dampening and Nesterov; see sgd_update.
 //   * Global-norm clipping ("Data parallelism and ZeRO stages 1 to 3", section
-//     "Going further": the squared norms of the chunks, summed across ranks ahead of the update;
-//     no formula): each shard's squared norm of its mean gradient, summed in
-//     index order in double, then summed over shards in rank order; the factor
-//     min(1, max_norm / (sqrt(sum) + 1e-6)) in double, as torch's
-//     clip_grad_norm_ defines it, rounded once to S; the mean gradient is
-//     multiplied by it before the moments.
+//     "Going further", which names it as a sum over ranks of the chunks' squared
+//     norms before the step, with no formula): each shard's squared norm of its
+//     mean gradient, summed in index order in double, then summed over shards
+//     in rank order; the factor min(1, max_norm / (sqrt(sum) + 1e-6)) in
+//     double, as torch's clip_grad_norm_ defines it, rounded once to S; the
+//     mean gradient is multiplied by it before the moments.
 //
 // Build: g++ -O2 -std=c++17 -ffp-contract=off -fno-fast-math -shared -fPIC.
 // Single-threaded and deliberately unfused: every worker materialises its own
@@ -238,7 +238,7 @@ inline double oracle_sqrt(double x) { return std::sqrt(x); }
 // without printing it; the formula is the reading stated at the top of the
 // file. decay[i] != 0 selects decoupled weight decay for element i
 // ("Data parallelism and ZeRO stages 1 to 3", section "4. The interface" and
-// its test catalog: "AdamW with decay").
+// its test catalog, whose differential test runs AdamW with weight decay).
 // ---------------------------------------------------------------------------
 template <class S>
 void adam_update(S* w, const S* g, S* m, S* v, int64_t len,
@@ -533,9 +533,9 @@ void rank_step(int mode, int64_t n, int64_t N, int64_t r, const void* param_in,
 
 // ---------------------------------------------------------------------------
 // Squared norm of one shard's mean gradient, summed in index order in double.
-// "Data parallelism and ZeRO stages 1 to 3", section "Going further": sharded
-// global-norm clipping is the chunks' squared norms summed across ranks ahead of
-// the update.
+// "Data parallelism and ZeRO stages 1 to 3", section "Going further" names
+// sharded global-norm clipping: a sum over ranks of each chunk's squared norm,
+// taken before the update.
 // ---------------------------------------------------------------------------
 template <class S>
 double shard_sumsq(const std::vector<S>& g) {
@@ -792,7 +792,12 @@ int orc_sgd_step(int form, int mode, int64_t n, int64_t N, int64_t rank, const v
   if (n < 0 || N < 1 || t < 1 || form < 0 || form > 2) return -1;
   if (form == 2 && (rank < 0 || rank >= N)) return -1;
   const OptSel o = {1, momentum, dampening, nesterov};
-  const int64_t len = form == 2 ? [&] { int64_t a, b; split_bounds(n, N, rank, &a, &b); return b - a; }() : n;
+  int64_t len = n;
+  if (form == 2) {
+    int64_t a, b;
+    split_bounds(n, N, rank, &a, &b);
+    len = b - a;
+  }
   const size_t sb = mode == MODE_F64 ? 8 : 4;
   std::vector<unsigned char> vin((size_t)len * sb, 0), vout((size_t)len * sb, 0);  // unused by SGD
   if (mode == MODE_F64) {
@@ -844,7 +849,7 @@ int orc_sgd_step(int form, int mode, int64_t n, int64_t N, int64_t rank, const v
 //   stage 3: P c_r, G c_r, K c_r
 //
 // convention 1, the bookkeeping of "Data parallelism and ZeRO stages 1 to 3",
-// section "2. Principles" ("Your emulation's bookkeeping") and the byte table
+// section "2. Principles" (its paragraph on the emulation's bookkeeping) and the byte table
 // of section "3. Worked example by hand", with bw bytes per value (P is used):
 //   one process (stage 0): params bw n, grads bw n, optimizer 2 bw n
 //   stage 1: bw n, bw n + bw c_r (the chunk's gradient), 2 bw c_r + bw c_r (master)
