@@ -138,10 +138,11 @@ def pmc_summary(workload, fetch_dir, write_dir, cmd):
     return out
 
 
-def kt_summary(workload, kt_dir, cmd, variant=None):
+def kt_summary(workload, kt_dir, cmd, variant=None, bench_json=None):
     """Per-kernel durations from rocprofv3 --kernel-trace --stats, as
     profiles/kernel_trace_<workload>[_<variant>].md (variant: e.g. "clip" for a
-    --clip run)."""
+    --clip run). bench_json: the JSON line bench.py printed in the profiled
+    run, whose HIP-event kernel time is set beside rocprofv3's average."""
     import csv
     import glob
     f = glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
@@ -166,6 +167,17 @@ def kt_summary(workload, kt_dir, cmd, variant=None):
             name = name[:110]
             fh.write(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']):.0f} | {r['MinNs']} | "
                      f"{r['MaxNs']} | {float(r['Percentage']):.2f} |\n")
+        if bench_json:
+            with open(bench_json) as jf:
+                d = json.loads([ln for ln in jf.read().splitlines() if ln.startswith("{")][-1])
+            step = [r for r in rows if r["Name"].find(STEP_KERNEL + "<") >= 0]
+            calls = max(step, key=lambda r: int(r["Calls"]))
+            avg_ms = float(calls["AverageNs"]) / 1e6
+            fh.write(f"\nThe same run's bench.py line: step kernel {d['kernel_ms_mean']:.4f} ms "
+                     f"(HIP events on the launch stream, mean of {d['steps']} launches), "
+                     f"rocprofv3 average {avg_ms:.4f} ms over {calls['Calls']} launches "
+                     f"(ratio {avg_ms / d['kernel_ms_mean']:.3f}); roofline achieved "
+                     f"{d['roofline']['achieved']:.0f} GB/s, frac {d['roofline']['frac']:.4f}.\n")
     return path
 
 
@@ -405,6 +417,8 @@ def main():
     ap.add_argument("--kt-summary", metavar="KT_DIR",
                     help="summarise a rocprofv3 --kernel-trace --stats run into profiles/ and exit")
     ap.add_argument("--cmd", default="", help="the profiling command, recorded in the summary")
+    ap.add_argument("--bench-json", default=None,
+                    help="with --kt-summary: the profiled run's bench.py output")
     ap.add_argument("--variant", default=None,
                     help="with --kt-summary: a suffix for the summary's name (e.g. clip)")
     args = ap.parse_args()
@@ -412,7 +426,7 @@ def main():
         print(json.dumps(pmc_summary(args.workload, *args.pmc_summary, args.cmd)))
         return
     if args.kt_summary:
-        print(kt_summary(args.workload, args.kt_summary, args.cmd, args.variant))
+        print(kt_summary(args.workload, args.kt_summary, args.cmd, args.variant, args.bench_json))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (all logical workers live in one GPU's HBM); "
