@@ -317,6 +317,7 @@ def _zceil():
     path = os.path.join(ROOT, "zero_sharded_optimizer_amd", "libzceil.so")
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build() first")
+    import torch  # noqa: F401  (torch's HIP runtime first, as for libzero.so)
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER
     lib.zceil_streams.restype = ctypes.c_int

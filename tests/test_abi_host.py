@@ -469,3 +469,25 @@ def test_binding_rejects_tensors_on_several_devices():
         z._same_device(FakeStream("cuda:1"), Fake("cuda:0"))
     z._same_device(FakeStream("cuda:0"), Fake("cuda:0"))
     z._same_device(FakeStream("cuda:3"))  # no tensors: nothing to compare
+
+
+def test_one_hip_runtime_when_the_library_loads_first():
+    """A host-only call that loads libzero.so before the program has touched
+    torch still leaves one HIP runtime in the process: torch's (the binding
+    loads torch first). Checked in a fresh interpreter, without a GPU."""
+    import subprocess
+    import sys
+    code = ("import zero_sharded_optimizer_amd as z\n"
+            "z.zero_memory_bytes(10, 2, 0, 1, z.ZERO_MODE_F32)\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "paths = sorted({l.split()[-1] for l in maps if 'libamdhip64' in l})\n"
+            "print('\\n'.join(paths))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         timeout=300)
+    assert out.returncode == 0, out.stderr
+    paths = [p for p in out.stdout.splitlines() if p.strip()]
+    import torch
+    torch_dir = os.path.realpath(os.path.dirname(torch.__file__))
+    assert len(paths) == 1, paths
+    assert os.path.realpath(paths[0]).startswith(torch_dir), paths

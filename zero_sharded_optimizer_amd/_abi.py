@@ -70,6 +70,19 @@ EXPORTED = ("zero_init_states", "zero_step", "zero_memory_bytes", "zero_shard_bo
 _lib = None
 
 
+def _torch_runtime_first():
+    """Load torch (and with it the HIP runtime its wheel ships) before the
+    library. libzero.so links the runtime by its soname, libamdhip64.so.7; torch
+    links the file name libamdhip64.so from its own directory. Loaded in that
+    order, the library binds to torch's runtime, the one that owns the tensors
+    and streams it is given. Loaded the other way round, the process would hold
+    two HIP runtimes, and launches with torch's streams and memory would fail."""
+    try:
+        import torch  # noqa: F401
+    except ImportError:  # no torch: the library binds the system runtime alone
+        pass
+
+
 def load(path=None):
     """Load libzero.so (once). Raises if it has not been built: there is no
     fallback path."""
@@ -81,6 +94,7 @@ def load(path=None):
         raise RuntimeError(
             f"{p} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
             "or `python zero_sharded_optimizer_amd/build_lib.py`")
+    _torch_runtime_first()
     lib = C.CDLL(p)
     lib.zero_init_states.argtypes = [C.POINTER(zero_hparams), C.c_void_p,
                                      C.POINTER(zero_states), C.c_void_p]
