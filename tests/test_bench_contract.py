@@ -1,0 +1,62 @@
+"""bench.py's output contract: one JSON line with the metric, the roofline
+object (traffic from counters taken on the current kernel source) and the CPU
+baseline, and a clear refusal of more than one GPU."""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from zero_sharded_optimizer_amd import synth  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    res = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                         capture_output=True, text=True, timeout=300, cwd=ROOT)
+    assert res.returncode == 2
+    assert "one GPU" in res.stderr and res.stdout == ""
+
+
+@pytest.mark.parametrize("workload", sorted(synth.WORKLOADS))
+def test_traffic_summaries_match_the_current_kernel_source(workload):
+    """Each workload's counter summary was taken on the kernel source as it
+    stands (the hash of its code, comments and whitespace removed), and its
+    traffic is the algorithmic bytes: otherwise the bench line's traffic is null
+    and the profiles are stale."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    assert os.path.exists(path), path
+    d = json.load(open(path))
+    assert d["kernel_src_sha256_16"] == bench.kernel_hash(), "re-take the counters"
+    wl = synth.WORKLOADS[workload]
+    algo = bench.bytes_per_param(wl) * wl.length
+    assert d["algorithmic_bytes_per_launch"] == pytest.approx(algo)
+    assert 0.999 <= d["bytes_per_launch"] / algo <= 1.002
+
+
+@pytest.mark.gpu
+def test_bench_line_on_the_gpu():
+    print("[case] bench.py --steps 3 --warmup 1 --no-copy-ceiling", flush=True)
+    res = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3",
+                          "--warmup", "1", "--no-copy-ceiling"],
+                         capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-3000:]
+    lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, lines
+    d = json.loads(lines[0])
+    for key in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
+                "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
+                "roofline", "cpu_baseline"):
+        assert key in d, key
+    assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
+    assert d["config"]["workload"] == "fp32-320M-n8" and "model" not in d["config"]
+    assert d["value"] > 0 and d["unit"] == "params/s" and d["dtype"] == "f32"
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"])
+    assert r["traffic"] == pytest.approx(56 * 320_000_000, rel=2e-3)
+    c = d["cpu_baseline"]
+    assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0 and c["sample"]
