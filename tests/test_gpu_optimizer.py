@@ -21,7 +21,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd.optimizer import (ZeroOptimizer, init_states,  # noqa: E402
-                                                  zero_step)
+                                                  state_shards, zero_step)
 from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
 from oracle.compare import compare  # noqa: E402
 from gpu_cases import host, say  # noqa: E402
@@ -309,3 +309,27 @@ def test_averaged_grad_is_the_step_mean(oracle):
     mean = zo.averaged_grad()
     ref, _ = oracle.mean_grad(MODE_F32, zo.n, 5, [host(b) for b in zo.grads])
     compare("mean", host(mean), ref, "exact")
+
+
+def test_state_shards_are_the_array_split_views():
+    """The per-worker (m_shard, v_shard) pairs have numpy's array_split sizes and
+    are views of the flat state at the shard's offset (no copy), and a step
+    writes through them."""
+    n, N = 1001, 7
+    param = torch.randn(n, device="cuda")
+    st = init_states(n, N, precision="fp32", param=param)
+    pairs = state_shards(st, N)
+    sizes = [len(x) for x in np.array_split(np.arange(n), N)]
+    assert [m.numel() for m, _ in pairs] == sizes == [v.numel() for _, v in pairs]
+    es = st.m.element_size()
+    off = 0
+    for (m, v), size in zip(pairs, sizes):
+        assert m.data_ptr() == st.m.data_ptr() + off * es
+        assert v.data_ptr() == st.v.data_ptr() + off * es
+        off += size
+    grads = [torch.randn(n, device="cuda") for _ in range(N)]
+    hp = z.HParams(n=n, n_workers=N, mode=MODE_F32, lr=1e-2, beta1=0.9, beta2=0.999, eps=1e-8)
+    z.zero_step(hp, param, grads, st, 1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([m for m, _ in pairs]), st.m)
+    assert bool(st.m.ne(0).any())

@@ -115,6 +115,10 @@ class ZeroOptimizer:
         return [g[off:off + size].view_as(p)
                 for p, off, size in zip(self.params, self.offsets, self.sizes)]
 
+    def state_shards(self) -> List:
+        """Worker r's (m_shard, v_shard), as views (see state_shards)."""
+        return state_shards(self.states, self.n_workers)
+
     def zero_grad(self) -> None:
         for g in self.grads:
             g.zero_()
@@ -188,6 +192,19 @@ class ZeroOptimizer:
         for dst, src, _ in pairs:
             if dst is not None:
                 dst.copy_(src)
+
+
+def state_shards(states: z.States, n_workers: int) -> List:
+    """The N per-worker (m_shard, v_shard) pairs of "ZeRO-Sharded Adam Step",
+    section "What to implement": worker r's pair is the [a_r, b_r) view of the
+    flat m and v (np.array_split bounds), so each stays the size of its shard
+    and no memory is copied. v is None for momentum SGD."""
+    n = states.m.numel()
+    out = []
+    for r in range(n_workers):
+        a, b = z.zero_shard_bounds(n, n_workers, r)
+        out.append((states.m[a:b], None if states.v is None else states.v[a:b]))
+    return out
 
 
 def init_states(n_params: int, n_workers: int, device="cuda", precision: str = "fp32",
