@@ -17,7 +17,9 @@
  * On one GPU every logical worker lives in the same HBM, so the reduce-scatter
  * is a local sum over N gradient buffers (in rank order, left to right) and the
  * all-gather is the store into the one gathered parameter buffer. The whole
- * step is one kernel launch that streams each byte through HBM once.
+ * step is one kernel launch that streams each byte through HBM once (a call
+ * longer than 2^32 elements is enqueued as consecutive launches of at most
+ * 2^32 elements each, on offset views of the same buffers).
  *
  * Per element, in the state type S (double in fp64 mode, float otherwise),
  * each operation one IEEE round-to-nearest-even operation, never fused:
@@ -240,8 +242,9 @@ zero_status zero_step_scalars_fill(const zero_hparams* hp, int64_t t, zero_step_
  * zero_step_range (with t = 1); the device values are used as given, so the
  * buffer must hold a filled value whenever the launch runs. The result is bit
  * for bit that of zero_step_range with the same t. For graph capture
- * (hipStreamBeginCapture, or torch.cuda.graph): the launch enqueues one kernel
- * and makes no allocation, copy, set or synchronisation. */
+ * (hipStreamBeginCapture, or torch.cuda.graph): the call enqueues one kernel
+ * (one per 2^32 elements) and makes no allocation, copy, set or
+ * synchronisation. */
 zero_status zero_step_range_dev(const zero_hparams* hp, void* param, const void* const* grads,
                                 const zero_states* states, const zero_step_scalars* dev_scalars,
                                 int64_t begin, int64_t end, void* stream);

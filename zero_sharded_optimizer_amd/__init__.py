@@ -316,7 +316,8 @@ def zero_step_range_dev(hp: HParams, param, grads: Sequence, states: States, sca
     """Enqueue zero_step_range with the step scalars read on the device from
     `scalars` (a device tensor of >= STEP_SCALARS_BYTES bytes holding
     zero_step_scalars(hp, t) when the launch runs). Safe to capture into a
-    graph: one kernel, no allocation, copy or synchronisation."""
+    graph: one kernel (one per 2^32 elements), no allocation, copy or
+    synchronisation."""
     chk = _check_common(hp, param, states)
     if chk is not None:
         g_dt, glen = chk
