@@ -59,7 +59,10 @@ typedef enum {
   ZERO_OK = 0,
   ZERO_EINVAL = -1,       /* a bad argument; nothing was enqueued */
   ZERO_EUNSUPPORTED = -2, /* valid, but outside what this library implements */
-  ZERO_EHIP = -3          /* the HIP runtime reported an error at launch */
+  ZERO_EHIP = -3          /* the HIP runtime reported an error at launch; in a
+                             call of several launches (buckets, pieces of 2^32
+                             elements, the clipped step) the ones before it
+                             may already be enqueued */
 } zero_status;
 
 typedef enum {
