@@ -333,3 +333,34 @@ def test_state_shards_are_the_array_split_views():
     torch.cuda.synchronize()
     assert torch.equal(torch.cat([m for m, _ in pairs]), st.m)
     assert bool(st.m.ne(0).any())
+
+
+@pytest.mark.parametrize("precision", ["bf16", "fp16"])
+def test_mixed_precision_optimizer_matches_the_oracle(oracle, precision):
+    """ZeroOptimizer in bf16/fp16 mixed precision, decay on the 2-D tensors, 3
+    steps of random gradients: gathered parameters, fp32 master, m and v against
+    the oracle's sharded step at the parity bar."""
+    from oracle import MODE_MIXED_F16
+    pdt = torch.bfloat16 if precision == "bf16" else torch.float16
+    mode = MODE_MIXED if precision == "bf16" else MODE_MIXED_F16
+    model = _model(8, pdt).cuda()
+    params = list(model.parameters())
+    decay = [p.dim() >= 2 for p in params]
+    zo = ZeroOptimizer(params, 3, 2, precision=precision, lr=1e-2, betas=(0.9, 0.95),
+                       weight_decay=0.1, decay=decay)
+    flags = np.concatenate([np.full(p.numel(), d, dtype=np.uint8) for p, d in zip(params, decay)])
+    p_o = host(zo.flat)
+    mst_o, m_o, v_o = oracle.init_states(mode, p_o)
+    g = torch.Generator(device="cuda").manual_seed(31)
+    for t in (1, 2, 3):
+        for buf in zo.grads:
+            buf.copy_((torch.randn(buf.shape, generator=g, device="cuda") * 0.01).to(pdt))
+        g_h = [host(b) for b in zo.grads]
+        zo.step()
+        p_o, mst_o, m_o, v_o = oracle.zero_step(mode, p_o, g_h, mst_o, m_o, v_o, t, 1e-2, 0.9,
+                                                0.95, 1e-8, 0.1, flags)
+    torch.cuda.synchronize()
+    compare("param", host(zo.flat), p_o, precision)
+    compare("master", host(zo.states.master), mst_o, "f32")
+    compare("m", host(zo.states.m), m_o, "f32")
+    compare("v", host(zo.states.v), v_o, "f32")
