@@ -364,3 +364,46 @@ def test_mixed_precision_optimizer_matches_the_oracle(oracle, precision):
     compare("master", host(zo.states.master), mst_o, "f32")
     compare("m", host(zo.states.m), m_o, "f32")
     compare("v", host(zo.states.v), v_o, "f32")
+
+
+def test_bucketed_step_equals_the_one_shot_step():
+    """step_buckets over the default 25 MiB buckets and over 64-byte buckets, with
+    each bucket waiting on an event recorded on a producer stream after it
+    wrote that bucket's gradients, gives the step() result bit for bit."""
+    model = _model(12, torch.float32).cuda()
+    params = list(model.parameters())
+    a = ZeroOptimizer(params, 4, 2, precision="fp32", lr=1e-2, weight_decay=0.1)
+    b = ZeroOptimizer([torch.empty_like(p) for p in params], 4, 2, precision="fp32", lr=1e-2,
+                      weight_decay=0.1)
+    b.flat.copy_(a.flat)
+    g = torch.Generator(device="cuda").manual_seed(3)
+    src = [torch.randn(a.n, generator=g, device="cuda") for _ in range(4)]
+    for bufa, bufb, x in zip(a.grads, b.grads, src):
+        bufa.copy_(x)
+        bufb.copy_(x)
+    a.step()
+    assert len(b.buckets()) == 1
+    b.step_buckets(b.buckets())  # one bucket: the whole vector, no events
+    torch.cuda.synchronize()
+    assert torch.equal(a.flat, b.flat)
+    # small buckets, each released by an event after a producer stream writes it
+    for buf, x in zip(a.grads, src):
+        buf.copy_(-x)
+    a.step()
+    producer = torch.cuda.Stream()
+    bks = b.buckets(bucket_bytes=64)  # 16 elements each
+    assert len(bks) > 1 and bks[0][1] == b.n
+    events = []
+    producer.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(producer):
+        for lo, hi in bks:
+            for buf, x in zip(b.grads, src):
+                buf[lo:hi].copy_(-x[lo:hi])
+            ev = torch.cuda.Event()
+            ev.record(producer)
+            events.append(ev)
+    b.step_buckets(bks, events)
+    torch.cuda.synchronize()
+    assert torch.equal(a.flat, b.flat) and torch.equal(a.states.m, b.states.m)
+    with pytest.raises(ValueError, match="exactly once"):
+        b.step_buckets(bks[1:])

@@ -145,6 +145,36 @@ class ZeroOptimizer:
         z.zero_step_clipped(self.hp, self.flat, self.grads, self.states, self.t, max_norm,
                             self._clip_ws, sumsq_out=self._sumsq, stream=stream)
 
+    def buckets(self, bucket_bytes: int = 25 << 20) -> List:
+        """(begin, end) buckets of about bucket_bytes of one worker's gradient
+        (25 MiB by default, the DDP bucket size "Data Parallelism & ZeRO" names),
+        last bucket first: the order in which a backward pass finishes them. Each
+        begin is a multiple of 8 elements, as zero_step_buckets requires."""
+        esize = self.grads[0].element_size()
+        size = max(8, bucket_bytes // esize // 8 * 8)
+        edges = list(range(0, self.n, size)) + [self.n]
+        return list(reversed(list(zip(edges[:-1], edges[1:]))))
+
+    def step_buckets(self, buckets: Sequence, events: Optional[Sequence] = None,
+                     stream=None) -> None:
+        """The same step as step(), bucket by bucket in one call
+        (zero_step_buckets): bucket i first waits on the device for events[i] (a
+        recorded torch.cuda.Event, e.g. after the gradient producer wrote that
+        bucket, or None), so the step of early buckets overlaps the production
+        of later ones. The buckets must cover [0, n) once; the result is bit for
+        bit that of step()."""
+        covered = sorted((int(a), int(b)) for a, b in buckets)
+        pos = 0
+        for a, b in covered:
+            if a != pos or b < a:
+                raise ValueError("buckets must cover [0, n) exactly once")
+            pos = b
+        if pos != self.n:
+            raise ValueError("buckets must cover [0, n) exactly once")
+        self.t += 1
+        z.zero_step_buckets(self.hp, self.flat, self.grads, self.states, self.t, buckets,
+                            events, stream=stream)
+
     def grad_norm(self) -> float:
         """The global norm of the averaged gradient of the last clipped step
         (waits for that step to finish)."""
