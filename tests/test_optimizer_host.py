@@ -47,6 +47,16 @@ def test_mixed_init_states_needs_the_parameters():
 def test_zero_rejects_a_repeated_parameter():
     """A tensor listed twice would get two slices of the gathered buffer and be
     stepped twice per step."""
-    t = object()
+    torch = pytest.importorskip("torch")
+    t = torch.zeros(4)
     with pytest.raises(ValueError, match="more than once"):
-        ZeroOptimizer([t, object(), t], 2, 1)
+        ZeroOptimizer([t, torch.zeros(2), t], 2, 1)
+
+
+def test_zero_rejects_parameters_that_share_memory():
+    """Two views of one storage would each become a slice of their own, so the
+    tie between them would silently break."""
+    torch = pytest.importorskip("torch")
+    base = torch.zeros(16)
+    with pytest.raises(ValueError, match="share memory"):
+        ZeroOptimizer([base[:10], torch.zeros(3), base[8:]], 2, 1)

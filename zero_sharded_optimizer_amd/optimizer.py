@@ -67,12 +67,19 @@ class ZeroOptimizer:
             raise ValueError("decay: one flag per parameter tensor")
         if len({id(p) for p in params}) != len(params):
             raise ValueError("a parameter appears more than once")
+        spans = sorted((p.data_ptr(), p.data_ptr() + p.numel() * p.element_size(), i)
+                       for i, p in enumerate(params) if p.numel())
+        for (_, hi, i), (lo, _, j) in zip(spans, spans[1:]):
+            if lo < hi:  # each becomes its own slice of the gathered buffer: a tie would break
+                raise ValueError(f"params[{i}] and params[{j}] share memory")
         import torch
         mode, pdt, sdt = _MODE_DTYPE[precision]
         pdt, sdt = getattr(torch, pdt), getattr(torch, sdt)
         for i, p in enumerate(params):
             if not p.is_cuda or p.dtype != pdt:
                 raise ValueError(f"params[{i}]: expected a GPU tensor of {pdt}")
+            if p.device != params[0].device:
+                raise ValueError(f"params[{i}] is on {p.device}, params[0] on {params[0].device}")
         self.stage, self.n_workers, self.mode = stage, n_workers, mode
         self.params = params
         self.sizes = [p.numel() for p in params]
