@@ -491,3 +491,30 @@ def test_one_hip_runtime_when_the_library_loads_first():
     torch_dir = os.path.realpath(os.path.dirname(torch.__file__))
     assert len(paths) == 1, paths
     assert os.path.realpath(paths[0]).startswith(torch_dir), paths
+
+
+def test_every_call_raises_without_the_library():
+    """No CPU fallback: with libzero.so absent, a host-only call and a step both
+    raise, naming the missing file (fresh interpreter, library path redirected)."""
+    import subprocess
+    import sys
+    code = ("import zero_sharded_optimizer_amd as z\n"
+            "from zero_sharded_optimizer_amd import _abi\n"
+            "_abi.LIB_PATH = '/nonexistent/libzero.so'\n"
+            "for call in (lambda: z.zero_shard_bounds(10, 2, 0),\n"
+            "             lambda: z.zero_memory_bytes(10, 2, 0, 1, 1),\n"
+            "             lambda: z.zero_step(z.HParams(n=8, n_workers=1, mode=1, lr=1e-3,\n"
+            "                                           beta1=0.9, beta2=0.999, eps=1e-8),\n"
+            "                                 1 << 32, [2 << 32], z.States(None, 3 << 32, 4 << 32),\n"
+            "                                 1, stream=0)):\n"
+            "    try:\n"
+            "        call()\n"
+            "    except RuntimeError as e:\n"
+            "        assert 'libzero.so is missing' in str(e), e\n"
+            "    else:\n"
+            "        raise SystemExit('a call ran without the library')\n"
+            "print('all raised')\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT,
+                         timeout=300)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "all raised" in out.stdout
