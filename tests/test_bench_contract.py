@@ -60,3 +60,27 @@ def test_bench_line_on_the_gpu():
     assert r["traffic"] == pytest.approx(56 * 320_000_000, rel=2e-3)
     c = d["cpu_baseline"]
     assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0 and c["sample"]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("flags", [["--clip", "0.5"], ["--bucket-mib", "25"],
+                                   ["--bucket-mib", "25", "--native-buckets"],
+                                   ["--bucket-mib", "25", "--graph"]],
+                         ids=["clip", "buckets", "native-buckets", "graph"])
+def test_bench_variants_on_the_gpu(flags):
+    """The variant runs behind the committed kernel-trace summaries still print
+    one valid line (a few steps, no baselines or ceilings)."""
+    print(f"[case] bench.py {' '.join(flags)}", flush=True)
+    res = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "2",
+                          "--warmup", "1", "--no-cpu-baseline", "--no-copy-ceiling", *flags],
+                         capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-3000:]
+    lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, lines
+    d = json.loads(lines[0])
+    assert d["value"] > 0 and d["roofline"]["achieved"] > 0
+    assert d["roofline"]["traffic"] is None  # counters exist for the one-shot step only
+    if "--clip" in flags:
+        assert d["config"]["clipped"] is True
+    else:
+        assert d["config"]["bucket_mib"] == 25 and d["config"]["buckets"] > 1
