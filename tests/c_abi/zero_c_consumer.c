@@ -9,7 +9,10 @@
  *                          fp32 (N = 8), bf16 mixed precision (N = 4) and fp16
  *                          mixed precision (N = 5), compared with the oracle:
  *                          fp64 bit-exact, fp32 within 1e-6 * max(1, |ref|),
- *                          bf16 and fp16 within 1 ulp.
+ *                          bf16 and fp16 within 1 ulp; then a bucketed fp32
+ *                          step (zero_step_buckets) whose buckets wait on
+ *                          events that a producer stream records after copying
+ *                          each bucket's gradients in, against the oracle.
  * Exit status 0 when every check holds.
  */
 #include <hip/hip_runtime_api.h>
@@ -230,6 +233,99 @@ static void run_mode(int mode, int64_t n, int N) {
   free(dv);
 }
 
+/* Two bucketed steps: a producer stream copies each bucket's gradients from
+ * pinned host memory and records an event; zero_step_buckets on a second
+ * stream steps each bucket once its event has completed. */
+static void run_buckets(void) {
+  const int mode = ZERO_MODE_F32, N = 4;
+  const int64_t n = 65539, bsize = 8192;
+  const int nb = (int)((n + bsize - 1) / bsize);
+  printf("[case] buckets with events: fp32 n %lld N %d, %d buckets\n", (long long)n, N, nb);
+  fflush(stdout);
+  float *p_h, *g_h[4];
+  HIP(hipHostMalloc((void**)&p_h, n * 4, hipHostMallocDefault));
+  for (int k = 0; k < N; ++k) HIP(hipHostMalloc((void**)&g_h[k], n * 4, hipHostMallocDefault));
+  for (int64_t i = 0; i < n; ++i) p_h[i] = (float)(0.04 * (uniform() - 0.5));
+  void *p_d, *m_d, *v_d, *g_d[4];
+  HIP(hipMalloc(&p_d, n * 4));
+  HIP(hipMalloc(&m_d, n * 4));
+  HIP(hipMalloc(&v_d, n * 4));
+  for (int k = 0; k < N; ++k) HIP(hipMalloc(&g_d[k], n * 4));
+  HIP(hipMemcpy(p_d, p_h, n * 4, hipMemcpyHostToDevice));
+  float *op = malloc(n * 4), *om = malloc(n * 4), *ov = malloc(n * 4);
+  float *np_ = malloc(n * 4), *nm = malloc(n * 4), *nv = malloc(n * 4);
+  memcpy(op, p_h, n * 4);
+  orc_init_states(mode, n, op, NULL, om, ov);
+  zero_hparams hp;
+  memset(&hp, 0, sizeof hp);
+  hp.n = n;
+  hp.n_workers = N;
+  hp.rank = -1;
+  hp.mode = mode;
+  hp.lr = 1e-3;
+  hp.beta1 = 0.9;
+  hp.beta2 = 0.95;
+  hp.eps = 1e-8;
+  zero_states st = {NULL, m_d, v_d};
+  hipStream_t prod, step;
+  HIP(hipStreamCreate(&prod));
+  HIP(hipStreamCreate(&step));
+  CHECK(zero_init_states(&hp, p_d, &st, step) == ZERO_OK);
+  hipEvent_t ev[16];
+  int64_t edges[32];
+  for (int b = 0; b < nb; ++b) {
+    const int i = nb - 1 - b; /* last bucket first, as a backward pass finishes them */
+    edges[2 * b] = i * bsize;
+    edges[2 * b + 1] = (i + 1) * bsize < n ? (i + 1) * bsize : n;
+    HIP(hipEventCreateWithFlags(&ev[b], hipEventDisableTiming));
+  }
+  const void* gp[4];
+  for (int k = 0; k < N; ++k) gp[k] = g_d[k];
+  for (int64_t t = 1; t <= 2; ++t) {
+    for (int k = 0; k < N; ++k)
+      for (int64_t i = 0; i < n; ++i) g_h[k][i] = (float)(2e-3 * (uniform() - 0.5));
+    for (int b = 0; b < nb; ++b) {
+      const int64_t lo = edges[2 * b], hi = edges[2 * b + 1];
+      for (int k = 0; k < N; ++k)
+        HIP(hipMemcpyAsync((char*)g_d[k] + lo * 4, g_h[k] + lo, (hi - lo) * 4,
+                           hipMemcpyHostToDevice, prod));
+      HIP(hipEventRecord(ev[b], prod));
+    }
+    CHECK(zero_step_buckets(&hp, p_d, gp, &st, t, edges, nb, (void* const*)ev, step) ==
+          ZERO_OK);
+    HIP(hipStreamSynchronize(step)); /* every bucket waited for its copies */
+    CHECK(orc_zero_step(mode, n, N, op, (const void* const*)g_h, NULL, om, ov, np_, NULL, nm, nv,
+                        t, hp.lr, hp.beta1, hp.beta2, hp.eps, 0.0, NULL) == 0);
+    memcpy(op, np_, n * 4);
+    memcpy(om, nm, n * 4);
+    memcpy(ov, nv, n * 4);
+  }
+  float *dp = malloc(n * 4), *dm = malloc(n * 4);
+  HIP(hipMemcpy(dp, p_d, n * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(dm, m_d, n * 4, hipMemcpyDeviceToHost));
+  CHECK(compare("param", 1, dp, op, n) == 0);
+  CHECK(compare("m", 1, dm, om, n) == 0);
+  for (int b = 0; b < nb; ++b) HIP(hipEventDestroy(ev[b]));
+  HIP(hipStreamDestroy(prod));
+  HIP(hipStreamDestroy(step));
+  for (int k = 0; k < N; ++k) {
+    HIP(hipFree(g_d[k]));
+    HIP(hipHostFree(g_h[k]));
+  }
+  HIP(hipFree(p_d));
+  HIP(hipFree(m_d));
+  HIP(hipFree(v_d));
+  HIP(hipHostFree(p_h));
+  free(op);
+  free(om);
+  free(ov);
+  free(np_);
+  free(nm);
+  free(nv);
+  free(dp);
+  free(dm);
+}
+
 int main(int argc, char** argv) {
   if (argc != 2 || (strcmp(argv[1], "host") != 0 && strcmp(argv[1], "gpu") != 0)) {
     fprintf(stderr, "usage: %s host|gpu\n", argv[0]);
@@ -240,6 +336,7 @@ int main(int argc, char** argv) {
   run_mode(ZERO_MODE_F32, 65539, 8);
   run_mode(ZERO_MODE_MIXED_BF16, 40009, 4);
   run_mode(ZERO_MODE_MIXED_F16, 30011, 5);
+  run_buckets();
   printf("gpu run: %d failures\n", g_fail);
   return g_fail == 0 ? 0 : 1;
 }

@@ -1,8 +1,9 @@
 """The C ABI from plain C (tests/c_abi/zero_c_consumer.c): no Python, no torch.
 On the host it checks shard bounds, the memory model, rejection with a message
 and the step scalars; on the GPU it allocates with the HIP runtime, runs
-init_states and three fused steps in fp64, fp32 and mixed precision, and
-compares with the oracle library on the same inputs."""
+init_states and three fused steps in fp64, fp32 and mixed precision, then two
+bucketed steps released by events from a producer stream, and compares with
+the oracle library on the same inputs."""
 import os
 import subprocess
 
