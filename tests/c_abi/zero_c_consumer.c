@@ -12,7 +12,11 @@
  *                          bf16 and fp16 within 1 ulp; then a bucketed fp32
  *                          step (zero_step_buckets) whose buckets wait on
  *                          events that a producer stream records after copying
- *                          each bucket's gradients in, against the oracle.
+ *                          each bucket's gradients in, against the oracle;
+ *                          and a clipped fp32 step (zero_step_clipped): its
+ *                          squared norm within the summation-order bound of
+ *                          the oracle's, and the step equal to the oracle's
+ *                          step from the mean clipped by the device's norm.
  * Exit status 0 when every check holds.
  */
 #include <hip/hip_runtime_api.h>
@@ -30,6 +34,13 @@ int orc_zero_step(int mode, int64_t n, int64_t N, const void* param_in, const vo
                   const void* master_in, const void* m_in, const void* v_in, void* param_out,
                   void* master_out, void* m_out, void* v_out, int64_t t, double lr, double b1,
                   double b2, double eps, double wd, const uint8_t* decay);
+int orc_mean_grad(int mode, int64_t n, int64_t N, int64_t rank, const void* const* grads,
+                  void* mean_out, double* sumsq_out);
+int orc_step_mean(int mode, int64_t n, int64_t N, int64_t rank, const void* param_in,
+                  const void* mean, const void* master_in, const void* m_in, const void* v_in,
+                  void* param_out, void* master_out, void* m_out, void* v_out, int64_t t,
+                  double lr, double b1, double b2, double eps, double wd, const uint8_t* decay,
+                  const double* clip_sumsq, double max_norm);
 
 static int g_fail = 0;
 #define CHECK(c)                                                      \
@@ -326,6 +337,89 @@ static void run_buckets(void) {
   free(dm);
 }
 
+/* One clipped step with the clip active (max_norm = half the norm). The device
+ * sums the squares in a fixed tree, the oracle in index order: both sum the
+ * same exact squares in double, so they agree within 2 n 2^-53 relatively.
+ * Given the device's squared norm, the oracle's step is the same arithmetic. */
+static void run_clipped(void) {
+  const int mode = ZERO_MODE_F32, N = 8;
+  const int64_t n = 65539;
+  printf("[case] clipped step: fp32 n %lld N %d\n", (long long)n, N);
+  fflush(stdout);
+  float *p_h = malloc(n * 4), *g_h[8];
+  for (int64_t i = 0; i < n; ++i) p_h[i] = (float)(0.04 * (uniform() - 0.5));
+  void *p_d, *m_d, *v_d, *g_d[8], *ws_d;
+  double* ss_d;
+  for (int k = 0; k < N; ++k) {
+    g_h[k] = malloc(n * 4);
+    for (int64_t i = 0; i < n; ++i) g_h[k][i] = (float)(2e-3 * (uniform() - 0.5));
+    HIP(hipMalloc(&g_d[k], n * 4));
+    HIP(hipMemcpy(g_d[k], g_h[k], n * 4, hipMemcpyHostToDevice));
+  }
+  HIP(hipMalloc(&p_d, n * 4));
+  HIP(hipMalloc(&m_d, n * 4));
+  HIP(hipMalloc(&v_d, n * 4));
+  HIP(hipMalloc((void**)&ss_d, sizeof(double)));
+  HIP(hipMemcpy(p_d, p_h, n * 4, hipMemcpyHostToDevice));
+  zero_hparams hp;
+  memset(&hp, 0, sizeof hp);
+  hp.n = n;
+  hp.n_workers = N;
+  hp.rank = -1;
+  hp.mode = mode;
+  hp.lr = 1e-3;
+  hp.beta1 = 0.9;
+  hp.beta2 = 0.95;
+  hp.eps = 1e-8;
+  hp.weight_decay = 0.05;
+  size_t wsb = 0;
+  CHECK(zero_step_clipped_workspace_bytes(&hp, &wsb) == ZERO_OK && wsb > 0);
+  HIP(hipMalloc(&ws_d, wsb));
+  zero_states st = {NULL, m_d, v_d};
+  CHECK(zero_init_states(&hp, p_d, &st, NULL) == ZERO_OK);
+  float *mean_o = malloc(n * 4), *om = malloc(n * 4), *ov = malloc(n * 4);
+  float *np_ = malloc(n * 4), *nm = malloc(n * 4), *nv = malloc(n * 4);
+  double ss_o = 0.0;
+  CHECK(orc_mean_grad(mode, n, N, -1, (const void* const*)g_h, mean_o, &ss_o) == 0);
+  const double max_norm = 0.5 * sqrt(ss_o);
+  const void* gp[8];
+  for (int k = 0; k < N; ++k) gp[k] = g_d[k];
+  CHECK(zero_step_clipped(&hp, p_d, gp, &st, 1, max_norm, ss_d, ws_d, wsb, NULL) == ZERO_OK);
+  HIP(hipDeviceSynchronize());
+  double ss_dev = 0.0;
+  HIP(hipMemcpy(&ss_dev, ss_d, sizeof(double), hipMemcpyDeviceToHost));
+  CHECK(fabs(ss_dev - ss_o) <= 2.0 * (double)n * ldexp(1.0, -53) * ss_o);
+  orc_init_states(mode, n, p_h, NULL, om, ov);
+  CHECK(orc_step_mean(mode, n, N, -1, p_h, mean_o, NULL, om, ov, np_, NULL, nm, nv, 1, hp.lr,
+                      hp.beta1, hp.beta2, hp.eps, hp.weight_decay, NULL, &ss_dev, max_norm) == 0);
+  float *dp = malloc(n * 4), *dm = malloc(n * 4), *dv = malloc(n * 4);
+  HIP(hipMemcpy(dp, p_d, n * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(dm, m_d, n * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(dv, v_d, n * 4, hipMemcpyDeviceToHost));
+  CHECK(compare("param", 1, dp, np_, n) == 0);
+  CHECK(compare("m", 1, dm, nm, n) == 0);
+  CHECK(compare("v", 1, dv, nv, n) == 0);
+  for (int k = 0; k < N; ++k) {
+    HIP(hipFree(g_d[k]));
+    free(g_h[k]);
+  }
+  HIP(hipFree(p_d));
+  HIP(hipFree(m_d));
+  HIP(hipFree(v_d));
+  HIP(hipFree(ws_d));
+  HIP(hipFree(ss_d));
+  free(p_h);
+  free(mean_o);
+  free(om);
+  free(ov);
+  free(np_);
+  free(nm);
+  free(nv);
+  free(dp);
+  free(dm);
+  free(dv);
+}
+
 int main(int argc, char** argv) {
   if (argc != 2 || (strcmp(argv[1], "host") != 0 && strcmp(argv[1], "gpu") != 0)) {
     fprintf(stderr, "usage: %s host|gpu\n", argv[0]);
@@ -337,6 +431,7 @@ int main(int argc, char** argv) {
   run_mode(ZERO_MODE_MIXED_BF16, 40009, 4);
   run_mode(ZERO_MODE_MIXED_F16, 30011, 5);
   run_buckets();
+  run_clipped();
   printf("gpu run: %d failures\n", g_fail);
   return g_fail == 0 ? 0 : 1;
 }
