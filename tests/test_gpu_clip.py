@@ -108,8 +108,16 @@ def test_step_from_mean_is_bit_identical_to_the_fused_step(oracle, mode):
         assert torch.equal(x.view(bits), y.view(bits)) and torch.equal(x.view(bits), w.view(bits))
 
 
+def _bits_equal(a, b):
+    a, b = np.ascontiguousarray(a), np.ascontiguousarray(b)
+    return a.shape == b.shape and np.array_equal(a.view(np.uint8), b.view(np.uint8))
+
+
 def _run_clipped(oracle, wl, steps, max_norm_of, full_compare=True):
-    """Clipped steps on the device and in the oracle, each computing its own norm."""
+    """Clipped steps on the device and in the oracle, each computing its own norm;
+    and a second oracle trajectory given the device's squared norm each step,
+    which must match the device bit for bit (the norm's summation order is then
+    the only difference removed)."""
     say(f"[case] clipped steps {wl.name} mode={wl.mode} n={wl.n} N={wl.n_workers}")
     hp, param, st, flags = setup(wl)
     dec = None if flags is None else flags.astype(np.uint8)
@@ -118,6 +126,7 @@ def _run_clipped(oracle, wl, steps, max_norm_of, full_compare=True):
     p_h, m_h, v_h = host(param), host(st.m), host(st.v)
     mst_h = host(st.master) if st.master is not None else None
     pk, sk = kinds(wl)
+    ex = [p_h, mst_h, m_h, v_h]  # the trajectory driven by the device's squared norm
     clipped = 0
     for t in range(1, steps + 1):
         grads = synth.make_grads(wl, t, "cuda")
@@ -130,10 +139,17 @@ def _run_clipped(oracle, wl, steps, max_norm_of, full_compare=True):
                                                 wl.weight_decay, dec, clip_sumsq=ss_h,
                                                 max_norm=max_norm)
         torch.cuda.synchronize()
-        assert sumsq_close(float(ss.item()), ss_h, wl.n)
+        ss_dev = float(ss.item())
+        assert sumsq_close(ss_dev, ss_h, wl.n)
+        ex = list(oracle.step_mean(wl.mode, wl.n_workers, ex[0], mean_h, ex[1], ex[2], ex[3], t,
+                                   wl.lr, wl.beta1, wl.beta2, wl.eps, wl.weight_decay, dec,
+                                   clip_sumsq=ss_dev, max_norm=max_norm))
         clipped += oracle.clip_factor(ss_h, max_norm) < 1.0
-    eps_rel = 2 * wl.n * 2.0 ** -53
     got = [host(param), host(st.m), host(st.v)]
+    assert _bits_equal(got[0], ex[0]) and _bits_equal(got[1], ex[2]) and _bits_equal(got[2], ex[3])
+    if st.master is not None:
+        assert _bits_equal(host(st.master), ex[1])
+    eps_rel = 2 * wl.n * 2.0 ** -53
     refs = [p_h, m_h, v_h]
     if wl.mode == MODE_F64:
         for name, g, r in zip(("param", "m", "v"), got, refs):
