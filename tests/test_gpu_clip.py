@@ -271,6 +271,7 @@ def test_clipped_step_full_size_fp32_320M_n8(oracle):
     idx_d = torch.from_numpy(idx).to("cuda")
     p_h = host(param[idx_d])
     m_h, v_h = np.zeros(idx.size, np.float32), np.zeros(idx.size, np.float32)
+    ex = [p_h, m_h, v_h]  # driven by the device's squared norm: bit-exact
     ws = _ws(z.zero_step_clipped_workspace_bytes(hp))
     ss = _dev_double()
     for t in (1, 2):
@@ -284,9 +285,15 @@ def test_clipped_step_full_size_fp32_320M_n8(oracle):
         p_h, _, m_h, v_h = oracle.step_mean(wl.mode, wl.n_workers, p_h, mean_h[idx], None, m_h,
                                             v_h, t, wl.lr, wl.beta1, wl.beta2, wl.eps,
                                             clip_sumsq=ss_h, max_norm=max_norm)
-        del mean_h
         torch.cuda.synchronize()
         assert sumsq_close(float(ss.item()), ss_h, wl.n)
+        e = oracle.step_mean(wl.mode, wl.n_workers, ex[0], mean_h[idx], None, ex[1], ex[2], t,
+                             wl.lr, wl.beta1, wl.beta2, wl.eps, clip_sumsq=float(ss.item()),
+                             max_norm=max_norm)
+        ex = [e[0], e[2], e[3]]
+        del mean_h
+        assert _bits_equal(host(param[idx_d]), ex[0]) and _bits_equal(host(st.m[idx_d]), ex[1])
+        assert _bits_equal(host(st.v[idx_d]), ex[2])
         compare(f"t={t} param", host(param[idx_d]), p_h, "f32")
         compare(f"t={t} m", host(st.m[idx_d]), m_h, "f32")
         compare(f"t={t} v", host(st.v[idx_d]), v_h, "f32")
