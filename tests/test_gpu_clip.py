@@ -226,6 +226,14 @@ def test_rank_mode_clipping_by_summed_shard_norms(oracle):
         a, b = z.zero_shard_bounds(wl.n, N, r)
         compare(f"rank {r} master", host(st.master), ref[1][a:b], "f32")
         compare(f"rank {r} m", host(st.m), ref[2][a:b], "f32")
+    # given the ranks' summed squared norm, the oracle's step is the device's, bit for bit
+    ex = oracle.step_mean(wl.mode, N, p_h, mean_h, mst0, m0, v0, 1, wl.lr, wl.beta1, wl.beta2,
+                          wl.eps, wl.weight_decay, clip_sumsq=total, max_norm=max_norm)
+    assert _bits_equal(host(param), ex[0])
+    for r, st in enumerate(states):
+        a, b = z.zero_shard_bounds(wl.n, N, r)
+        assert _bits_equal(host(st.master), ex[1][a:b]) and _bits_equal(host(st.m), ex[2][a:b])
+        assert _bits_equal(host(st.v), ex[3][a:b])
 
 
 def test_mean_grad_past_one_launch(oracle):
