@@ -70,7 +70,7 @@ constexpr int kWideBatch = 8;
 //                      up to 1 %; 1024 threads lose 5 %);
 //   mixed, N = 8:      512 x 2, PRELOAD, WC: 4 % over 256 x 1 (PRELOAD alone at
 //                      256 x 1 loses 6 %);
-//   fp32, N = 64:      128 x 8, WC, no PRELOAD: 3 % over 512 x 2 (368 registers,
+//   fp32, N = 64:      128 x 8, WC, no PRELOAD: 3 % over 512 x 2 (314 registers,
 //                      one wave per SIMD, 64 loads of 1 KiB in flight per wave);
 //   fp64 (1 M params): 256 x 1; launch-bound, every shape within noise.
 #ifndef ZERO_F64_BLOCK
