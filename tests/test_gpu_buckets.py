@@ -17,7 +17,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
 from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
-from oracle.compare import compare  # noqa: E402
+from gpu_cases import compare_bits  # noqa: E402
 from gpu_cases import host, kinds, say, setup  # noqa: E402
 
 W = synth.WORKLOADS
@@ -49,9 +49,9 @@ def _check_vs_oracle(oracle, wl, param, st, p0, g_hist):
         p, mst, m, v = oracle.zero_step(wl.mode, p, g_h, mst, m, v, t, wl.lr, wl.beta1, wl.beta2,
                                         wl.eps, wl.weight_decay, dec)
     pk, sk = kinds(wl)
-    compare("param", host(param), p, pk)
-    compare("m", host(st.m), m, sk)
-    compare("v", host(st.v), v, sk)
+    compare_bits("param", host(param), p, pk)
+    compare_bits("m", host(st.m), m, sk)
+    compare_bits("v", host(st.v), v, sk)
 
 
 @pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED, MODE_MIXED_F16])

@@ -21,7 +21,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from oracle import MIXED_MODES, MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
-from oracle.compare import compare  # noqa: E402
+from gpu_cases import compare_bits  # noqa: E402
 from gpu_cases import host, say  # noqa: E402
 
 _PDT = {MODE_F64: np.float64, MODE_F32: np.float32}
@@ -157,10 +157,10 @@ def test_random_configuration_matches_the_oracle(oracle, seed):
     torch.cuda.synchronize()
     pk = {MODE_F64: "exact", MODE_F32: "f32", MODE_MIXED: "bf16", MODE_MIXED_F16: "fp16"}[mode]
     sk = "exact" if mode == MODE_F64 else "f32"
-    compare("param", host(param), o_p, pk)
+    compare_bits("param", host(param), o_p, pk)
     if not c["sgd"] or mom:
-        compare("m", host(st.m), o_m, sk)
+        compare_bits("m", host(st.m), o_m, sk)
     if not c["sgd"]:
-        compare("v", host(st.v), o_v, sk)
+        compare_bits("v", host(st.v), o_v, sk)
     if need_master:
-        compare("master", host(st.master), o_mst, sk)
+        compare_bits("master", host(st.master), o_mst, sk)

@@ -23,7 +23,7 @@ import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd.optimizer import (ZeroOptimizer, init_states,  # noqa: E402
                                                   state_shards, zero_step)
 from oracle import MODE_F32, MODE_F64, MODE_MIXED  # noqa: E402
-from oracle.compare import compare  # noqa: E402
+from gpu_cases import compare_bits  # noqa: E402
 from gpu_cases import host, say  # noqa: E402
 
 
@@ -89,9 +89,9 @@ def test_zero_matches_single_process(oracle, stage, N):
         p_o, _, m_o, v_o = oracle.zero_step(MODE_F64, p_before, grads, None, m_o, v_o, t, lr,
                                             betas[0], betas[1], eps, wd, flags)
         got = host(zo.flat)
-        compare("param", got, p_o, "exact")
-        compare("m", host(zo.states.m), m_o, "exact")
-        compare("v", host(zo.states.v), v_o, "exact")
+        compare_bits("param", got, p_o, "exact")
+        compare_bits("m", host(zo.states.m), m_o, "exact")
+        compare_bits("v", host(zo.states.v), v_o, "exact")
         for p, q in zip(model.parameters(), ref.parameters()):
             assert p.shape == q.shape
             assert torch.allclose(p.detach().cpu(), q.detach(), rtol=0, atol=1e-10), t
@@ -233,9 +233,9 @@ def test_functional_zero_step(oracle, precision):
     p_o = p0
     for t in (1, 2):
         p_o, master, m_o, v_o = oracle.zero_step(mode, p_o, g0, master, m_o, v_o, t, lr)
-    compare("param", host(new_p), p_o, "f32" if precision == "fp32" else "bf16")
-    compare("m", host(new_st.m), m_o, "f32")
-    compare("v", host(new_st.v), v_o, "f32")
+    compare_bits("param", host(new_p), p_o, "f32" if precision == "fp32" else "bf16")
+    compare_bits("m", host(new_st.m), m_o, "f32")
+    compare_bits("v", host(new_st.v), v_o, "f32")
 
 
 def test_clipped_steps_match_torch_clip_grad_norm():
@@ -308,7 +308,7 @@ def test_averaged_grad_is_the_step_mean(oracle):
         buf.copy_(torch.randn(buf.shape, generator=g, device="cuda"))
     mean = zo.averaged_grad()
     ref, _ = oracle.mean_grad(MODE_F32, zo.n, 5, [host(b) for b in zo.grads])
-    compare("mean", host(mean), ref, "exact")
+    compare_bits("mean", host(mean), ref, "exact")
 
 
 def test_state_shards_are_the_array_split_views():
@@ -360,10 +360,10 @@ def test_mixed_precision_optimizer_matches_the_oracle(oracle, precision):
         p_o, mst_o, m_o, v_o = oracle.zero_step(mode, p_o, g_h, mst_o, m_o, v_o, t, 1e-2, 0.9,
                                                 0.95, 1e-8, 0.1, flags)
     torch.cuda.synchronize()
-    compare("param", host(zo.flat), p_o, precision)
-    compare("master", host(zo.states.master), mst_o, "f32")
-    compare("m", host(zo.states.m), m_o, "f32")
-    compare("v", host(zo.states.v), v_o, "f32")
+    compare_bits("param", host(zo.flat), p_o, precision)
+    compare_bits("master", host(zo.states.master), mst_o, "f32")
+    compare_bits("m", host(zo.states.m), m_o, "f32")
+    compare_bits("v", host(zo.states.v), v_o, "f32")
 
 
 def test_bucketed_step_equals_the_one_shot_step():

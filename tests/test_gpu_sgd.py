@@ -12,7 +12,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
 from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
-from oracle.compare import compare  # noqa: E402
+from gpu_cases import compare_bits  # noqa: E402
 from gpu_cases import host, kinds, say  # noqa: E402
 
 W = synth.WORKLOADS
@@ -63,11 +63,11 @@ def run_sgd(oracle, wl, variant, steps):
                                           nest, dec, form=form, N=wl.n_workers, rank=wl.rank)
     torch.cuda.synchronize()
     pk, sk = kinds(wl)
-    out = [compare("param", host(param), p_h, pk)]
+    out = [compare_bits("param", host(param), p_h, pk)]
     if mom:
-        out.append(compare("momentum buffer", host(st.m), b_h, sk))
+        out.append(compare_bits("momentum buffer", host(st.m), b_h, sk))
     if st.master is not None:
-        out.append(compare("master", host(st.master), mst_h, sk))
+        out.append(compare_bits("master", host(st.master), mst_h, sk))
     say("[done] " + "; ".join(f"{s['name']} bitexact {s['bitexact']}/{s['n']}" for s in out))
 
 
@@ -130,8 +130,8 @@ def test_sgd_full_size_fp32_320M_n8(oracle):
         p_h, _, b_h = oracle.sgd_step(wl.mode, p_h, g_h, None, b_h, t, wl.lr, wd, mom, damp, nest,
                                       form="full")
     torch.cuda.synchronize()
-    compare("param", host(param[idx_d]), p_h, "f32")
-    compare("momentum buffer", host(st.m[idx_d]), b_h, "f32")
+    compare_bits("param", host(param[idx_d]), p_h, "f32")
+    compare_bits("momentum buffer", host(st.m[idx_d]), b_h, "f32")
 
 
 @pytest.mark.parametrize("mode", [MODE_F32, MODE_MIXED])

@@ -14,7 +14,7 @@ if not torch.cuda.is_available():  # pragma: no cover
 
 import zero_sharded_optimizer_amd as z  # noqa: E402
 from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
-from oracle.compare import compare  # noqa: E402
+from gpu_cases import compare_bits  # noqa: E402
 from gpu_cases import host, say  # noqa: E402
 
 
@@ -75,14 +75,14 @@ def test_special_values_match_the_oracle(oracle, mode):
     kind = "exact" if mode == MODE_F64 else "f32"
     got_p = host(p_d)
     if mixed:
-        compare("param", got_p, p_h, "bf16" if mode == MODE_MIXED else "fp16")
+        compare_bits("param", got_p, p_h, "bf16" if mode == MODE_MIXED else "fp16")
         nan_out = got_p[np.isnan(mst)]
         assert nan_out.size > 0 and np.all(nan_out == (0x7FC0 if mode == MODE_MIXED else 0x7E00))
-        compare("master", host(st.master), mst, kind)
+        compare_bits("master", host(st.master), mst, kind)
     else:
-        compare("param", got_p, p_h, kind)
-    compare("m", host(st.m), m, kind)
-    compare("v", host(st.v), v, kind)
+        compare_bits("param", got_p, p_h, kind)
+    compare_bits("m", host(st.m), m, kind)
+    compare_bits("v", host(st.v), v, kind)
     # the special values did reach the state
     assert np.isnan(m).any() and np.isinf(m).any()
 
@@ -134,8 +134,8 @@ def test_fp16_gathered_copy_overflows_and_underflows(oracle, case):
                                           1e-8)
     torch.cuda.synchronize()
     got = host(p_d)
-    compare("param", got, p_h, "fp16")
-    compare("master", host(st.master), mst, "f32")
+    compare_bits("param", got, p_h, "fp16")
+    compare_bits("master", host(st.master), mst, "f32")
     assert np.all(np.isfinite(mst))
     if case == "overflow":
         assert np.all((p_h & 0x7FFF) == 0x7C00)  # every gathered value is an infinity
