@@ -575,12 +575,16 @@ void mean_grad(int mode, int64_t n, int64_t N, int64_t r, const void* const* gra
 
 // The clipping factor from the global squared norm, as torch's
 // clip_grad_norm_ (the production equivalent the openlearn page names)
-// defines it: min(1, max_norm / (norm + 1e-6)), in double.
+// defines it: min(1, max_norm / (norm + 1e-6)), in double, where the clamp at
+// 1 lets a NaN through (a NaN norm makes every clipped gradient NaN).
 double clip_factor(double sumsq, double max_norm) {
 #if ORACLE_MUTANT == 15
   return max_norm / (std::sqrt(sumsq) + 1e-6);  // planted: no clamp at 1
 #else
   const double c = max_norm / (std::sqrt(sumsq) + 1e-6);
+#if ORACLE_MUTANT != 20  // planted (20): a NaN factor clamped to 1
+  if (std::isnan(c)) return c;
+#endif
   return c < 1.0 ? c : 1.0;
 #endif
 }

@@ -610,6 +610,41 @@ def pin_clipping_vs_torch(O):
         assert 0 < clipped < T
 
 
+def pin_clipping_nonfinite_vs_torch(O):
+    """A non-finite global norm, as torch.nn.utils.clip_grad_norm_ handles it
+    (fp64, one worker): a NaN entry makes the norm NaN, and its clamp at 1 lets
+    the NaN factor through, so every gradient entry becomes NaN; an infinite
+    entry gives a zero factor, so the finite entries become 0 and the infinite
+    one NaN. The oracle's clipped mean must match torch's clipped gradient
+    entry for entry (NaN where torch has NaN), and so must one Adam step."""
+    import torch
+    n = 7
+    w0 = np.linspace(-1.0, 1.0, n)
+    for bad in (float("nan"), float("inf")):
+        g = np.linspace(0.1, 0.7, n)
+        g[3] = bad
+        p = torch.nn.Parameter(torch.tensor(w0))
+        p.grad = torch.tensor(g)
+        torch.nn.utils.clip_grad_norm_([p], 1.0, foreach=False)
+        tg = p.grad.numpy()
+        mean, ss = O.mean_grad(MODE_F64, n, 1, [g])
+        coef = O.clip_factor(ss, 1.0)
+        ours = mean * coef
+        assert np.array_equal(np.isnan(ours), np.isnan(tg)), (bad, ours, tg)
+        fin = ~np.isnan(tg)
+        assert np.array_equal(ours[fin], tg[fin]), (bad, ours, tg)
+        opt = torch.optim.Adam([p], lr=1e-2, betas=(0.9, 0.95), eps=1e-8, foreach=False)
+        opt.step()
+        _, m, v = O.init_states(MODE_F64, w0)
+        w, _, _, _ = O.step_mean(MODE_F64, 1, w0, mean, None, m, v, 1, 1e-2, 0.9, 0.95, 1e-8,
+                                 clip_sumsq=ss, max_norm=1.0)
+        tw = p.detach().numpy()
+        assert np.array_equal(np.isnan(w), np.isnan(tw)), (bad, w, tw)
+        assert np.allclose(w[~np.isnan(tw)], tw[~np.isnan(tw)], rtol=1e-12, atol=0.0)
+    if np.isnan(O.clip_factor(float("nan"), 1.0)) is not np.True_:
+        raise AssertionError("a NaN norm must give a NaN factor")
+
+
 def pin_clipping_closed_form(O):
     """With clipping active at t = 1, m1 = (1-b1) * c * gbar with
     c = max_norm / (|gbar| + 1e-6), so |m1| / (1-b1) = max_norm |gbar| / (|gbar| + 1e-6)."""
@@ -727,6 +762,7 @@ ALL_PINS = [
     pin_step_from_mean_equals_step,
     pin_clipping_vs_torch,
     pin_clipping_closed_form,
+    pin_clipping_nonfinite_vs_torch,
     pin_sgd_vs_torch,
     pin_sgd_constant_gradient,
     pin_sgd_sharded_equals_shard_free_and_rank_share,

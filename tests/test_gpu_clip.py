@@ -28,7 +28,7 @@ import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
 from oracle import MODE_F32, MODE_F64, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from oracle.compare import compare  # noqa: E402
-from gpu_cases import host, kinds, need_free, say, setup  # noqa: E402
+from gpu_cases import compare_bits, host, kinds, need_free, say, setup  # noqa: E402
 
 W = synth.WORKLOADS
 BASE = {MODE_F64: W["fp64-1M-n4"], MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"],
@@ -307,3 +307,37 @@ def test_clipped_step_full_size_fp32_320M_n8(oracle):
         compare(f"t={t} v", host(st.v[idx_d]), v_h, "f32")
         say(f"  t={t}: norm {math.sqrt(ss_h):.6g}, device squared norm within "
             f"{abs(ss.item() - ss_h) / ss_h:.2e} relative; {idx.size} samples within the bar")
+
+
+@pytest.mark.parametrize("mode", [MODE_F64, MODE_F32, MODE_MIXED])
+def test_nan_gradient_under_clipping_makes_every_element_nan(oracle, mode):
+    """One NaN gradient entry makes the global squared norm NaN. The clipping
+    factor is then NaN (torch's clip_grad_norm_ clamps at 1 with NaN passing
+    through), so every element's update is NaN, not only the poisoned one's:
+    on the device as in the oracle."""
+    wl = synth.scaled(BASE[mode], 10_007, n_workers=4, worker_scale=None, zero_frac=0.0)
+    say(f"[case] NaN gradient under clipping, mode={mode}")
+    hp, param, st, _ = setup(wl)
+    grads = synth.make_grads(wl, 1, "cuda")
+    grads[2][4321] = float("nan")
+    g_h = [host(g) for g in grads]
+    p_h = host(param)
+    mst, m0, v0 = oracle.init_states(wl.mode, p_h)
+    ws = _ws(z.zero_step_clipped_workspace_bytes(hp))
+    ss = _dev_double()
+    z.zero_step_clipped(hp, param, grads, st, 1, 1.0, ws, sumsq_out=ss)
+    mean_h, ss_h = oracle.mean_grad(wl.mode, wl.n, wl.n_workers, g_h)
+    ref = oracle.step_mean(wl.mode, wl.n_workers, p_h, mean_h, mst, m0, v0, 1, wl.lr, wl.beta1,
+                           wl.beta2, wl.eps, clip_sumsq=ss_h, max_norm=1.0)
+    torch.cuda.synchronize()
+    assert math.isnan(ss.item()) and math.isnan(ss_h)
+    pk, sk = kinds(wl)
+    compare_bits("param", host(param), ref[0], pk)
+    compare_bits("m", host(st.m), ref[2], sk)
+    compare_bits("v", host(st.v), ref[3], sk)
+    assert np.isnan(host(st.m)).all() and np.isnan(host(st.v)).all()
+    if st.master is not None:
+        compare_bits("master", host(st.master), ref[1], sk)
+        assert np.all(host(param) == 0x7FC0)
+    else:
+        assert np.isnan(host(param)).all()

@@ -7,7 +7,7 @@ full gradients, dropped hyperparameters) plus plausible slips in the Adam formul
 itself (exchanged betas, a dropped bias correction, eps inside the square root,
 coupled instead of decoupled decay, a wrong sign, an off-by-one step count, an
 inverted decay mask, truncating instead of rounding to bf16 or fp16, an unclamped or
-wrongly normed clipping factor). The mistakes are
+wrongly normed clipping factor, a NaN norm clamped away). The mistakes are
 planted in the oracle on the CPU only.
 """
 import pytest
@@ -35,6 +35,7 @@ MUTANTS = {
     17: "SGD momentum buffer starting at zero",
     18: "SGD with decoupled instead of coupled decay",
     19: "fp16 truncation",
+    20: "NaN clipping factor clamped to 1",
 }
 
 

@@ -406,12 +406,14 @@ __device__ __forceinline__ float grad_elem(const uint16_t* p, int64_t i) {
 }
 
 // The global-norm clipping factor min(1, max_norm / (sqrt(sumsq) + 1e-6)), in
-// double (the definition torch's clip_grad_norm_ uses), rounded once to S.
+// double (the definition torch's clip_grad_norm_ uses), rounded once to S. A NaN
+// norm gives a NaN factor, as torch's clamp does, so every clipped element
+// becomes NaN rather than taking an unclipped step.
 template <class S>
 __device__ __forceinline__ S clip_coef(const double* __restrict__ sumsq, double max_norm) {
   const double nrm = __builtin_sqrt(*sumsq);
   const double cf = max_norm / (nrm + 1e-6);
-  return (S)(cf < 1.0 ? cf : 1.0);
+  return (S)((cf < 1.0 || cf != cf) ? cf : 1.0);
 }
 
 // Steps 2-3 for one element: the moments, bias correction, optional decoupled
