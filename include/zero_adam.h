@@ -265,6 +265,23 @@ zero_status zero_step_range_dev(const zero_hparams* hp, void* param, const void*
  * order), so it is the same on every run; it may differ from another summation
  * order in the last bits. */
 
+/* zero_step that also stores the averaged gradient ("Data parallelism and ZeRO
+ * stages 1 to 3", section "2. Principles": in stage 1 each rank keeps the full
+ * averaged gradient in .grad, "Your emulation's bookkeeping"). In the same pass
+ * over the gradients, mean_out[j] receives gb = (g_0 + ... + g_{N-1}) / N of
+ * each element j of the call (full mode: n elements; rank mode: the c_r
+ * elements of worker `rank`'s shard), in S, bit for bit the value the update
+ * uses and the one zero_mean_grad computes. It costs sizeof(S) more bytes per
+ * parameter than zero_step, against N*sizeof(G) + sizeof(S) for a separate
+ * zero_mean_grad pass. Every other output is bit-identical to zero_step's.
+ * mean_out: device, 16-byte aligned, must not overlap any buffer the step reads
+ * or writes. Errors as zero_step, plus ZERO_EINVAL for a NULL, misaligned or
+ * overlapping mean_out (unless the rank's shard is empty: then nothing is
+ * touched). */
+zero_status zero_step_with_mean(const zero_hparams* hp, void* param, const void* const* grads,
+                                const zero_states* states, int64_t t, void* mean_out,
+                                void* stream);
+
 /* Device workspace bytes zero_mean_grad needs when sumsq_out is non-NULL. */
 zero_status zero_mean_grad_workspace_bytes(const zero_hparams* hp, size_t* bytes);
 

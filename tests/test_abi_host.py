@@ -518,3 +518,30 @@ def test_every_call_raises_without_the_library():
                          timeout=300)
     assert out.returncode == 0, out.stdout + out.stderr
     assert "all raised" in out.stdout
+
+
+def test_step_with_mean_rejects_before_any_launch():
+    """zero_step_with_mean validates everything zero_step does, plus its mean
+    buffer: NULL, misaligned, or overlapping an output, a gradient or the mask."""
+    lib = _abi.load()
+    st = _abi.zero_states(master=None, m=A + (1 << 24), v=A + (2 << 24))
+    arr = (C.c_void_p * 4)(*[A + ((3 + k) << 24) for k in range(4)])
+    hp = _hp()
+    for mean in (None, A + (9 << 24) + 4, A + 16, A + (1 << 24) + 64, A + (2 << 24),
+                 A + (4 << 24) + 16):
+        assert lib.zero_step_with_mean(C.byref(hp), A, arr, C.byref(st), 1, mean,
+                                       None) == z.ZERO_EINVAL, mean
+        assert lib.zero_last_error()
+    hpm = _hp(weight_decay=0.1, wd_mask=A + (9 << 24))
+    assert lib.zero_step_with_mean(C.byref(hpm), A, arr, C.byref(st), 1, A + (9 << 24),
+                                   None) == z.ZERO_EINVAL
+    # the checks of zero_step come first: t = 0 is rejected with a valid mean buffer
+    assert lib.zero_step_with_mean(C.byref(hp), A, arr, C.byref(st), 0, A + (9 << 24),
+                                   None) == z.ZERO_EINVAL
+    assert "t must be" in lib.zero_last_error().decode()
+    # an empty rank shard is valid with no mean buffer and launches nothing
+    hpe = _hp(n=3, n_workers=5, rank=4)
+    ste = _abi.zero_states(master=A + (9 << 24), m=A + (1 << 24), v=A + (2 << 24))
+    arr5 = (C.c_void_p * 5)(*[A + ((3 + k) << 24) for k in range(5)])
+    assert lib.zero_step_with_mean(C.byref(hpe), A, arr5, C.byref(ste), 1, None,
+                                   None) == z.ZERO_OK

@@ -13,6 +13,9 @@ workers sharing one GPU:
   zero_init_states(hp, param, states)   -> m = v = 0, master from param
   zero_step(hp, param, grads, states, t) -> one reduce-scatter-mean / Adam /
                                             all-gather step, in place
+  zero_step_with_mean(hp, param, grads, states, t, mean)
+                                         -> the same step, also storing the averaged
+                                            gradient (stage 1's .grad) in one pass
   zero_step_range(hp, param, grads, states, t, begin, end)
                                          -> the same step on [begin, end) only
                                             (one bucket of a bucketed step)
@@ -55,7 +58,7 @@ __all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
            "ZERO_MAX_WORKERS",
            "ZERO_OPT_ADAM", "ZERO_OPT_SGD", "zero_step_scalars", "zero_step_range_dev",
            "STEP_SCALARS_BYTES", "zero_min_stage", "ZERO_MODE_MIXED_F16",
-           "zero_step_buckets"]
+           "zero_step_buckets", "zero_step_with_mean"]
 
 
 class ZeroError(RuntimeError):
@@ -237,6 +240,28 @@ def zero_step(hp: HParams, param, grads: Sequence, states: States, t: int, strea
     arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
     st = lib.zero_step(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t),
                        _stream_handle(stream, states.m))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+def zero_step_with_mean(hp: HParams, param, grads: Sequence, states: States, t: int, mean_out,
+                        stream=None) -> None:
+    """Enqueue one fused step that also stores the averaged gradient of each
+    element of the call in mean_out (state dtype; see zero_adam.h)."""
+    chk = _check_common(hp, param, states)
+    if chk is not None:
+        g_dt, glen = chk
+        if len(grads) != hp.n_workers:
+            raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
+        for k, g in enumerate(grads):
+            _check_tensor(g, g_dt, glen, f"grads[{k}]")
+        _check_tensor(mean_out, _DTYPES[hp.mode][2], glen, "mean_out")
+    _same_device(stream, param, grads, states, hp.wd_mask, mean_out)
+    lib = _abi.load()
+    c_hp, c_st = hp.to_c(), states.to_c()
+    arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
+    st = lib.zero_step_with_mean(C.byref(c_hp), _addr(param), arr, C.byref(c_st), int(t),
+                                 _addr(mean_out), _stream_handle(stream, states.m))
     if st != ZERO_OK:
         _raise(st)
 

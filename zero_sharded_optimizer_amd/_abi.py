@@ -65,7 +65,7 @@ EXPORTED = ("zero_init_states", "zero_step", "zero_memory_bytes", "zero_shard_bo
             "zero_last_error", "zero_mean_grad_workspace_bytes", "zero_mean_grad",
             "zero_step_mean", "zero_step_clipped_workspace_bytes", "zero_step_clipped",
             "zero_step_range", "zero_step_scalars_fill", "zero_step_range_dev", "zero_min_stage",
-            "zero_step_buckets")
+            "zero_step_buckets", "zero_step_with_mean")
 
 _lib = None
 
@@ -102,6 +102,10 @@ def load(path=None):
     lib.zero_step.argtypes = [C.POINTER(zero_hparams), C.c_void_p, C.POINTER(C.c_void_p),
                               C.POINTER(zero_states), C.c_int64, C.c_void_p]
     lib.zero_step.restype = C.c_int
+    lib.zero_step_with_mean.argtypes = [C.POINTER(zero_hparams), C.c_void_p,
+                                        C.POINTER(C.c_void_p), C.POINTER(zero_states), C.c_int64,
+                                        C.c_void_p, C.c_void_p]
+    lib.zero_step_with_mean.restype = C.c_int
     lib.zero_memory_bytes.argtypes = [C.c_int64, C.c_int32, C.c_int32, C.c_int32, C.c_int32,
                                       C.c_int32, C.POINTER(zero_mem)]
     lib.zero_memory_bytes.restype = C.c_int

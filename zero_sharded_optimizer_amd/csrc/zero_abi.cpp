@@ -408,6 +408,7 @@ void offset_step(zlaunch::StepArgs* la, int64_t off, const Widths& wd, int64_t g
   la->m = static_cast<char*>(la->m) + off * wd.state;
   if (la->v) la->v = static_cast<char*>(la->v) + off * wd.state;  // NULL for SGD
   if (la->out) la->out = static_cast<char*>(la->out) + off * wd.param;
+  if (la->mean_out) la->mean_out = static_cast<char*>(la->mean_out) + off * wd.state;
   la->mask_bit_offset += off;
 }
 
@@ -527,6 +528,39 @@ zero_status zero_step(const zero_hparams* hp, void* param, const void* const* gr
   const int N = hp->n_workers >= 1 && hp->n_workers <= ZERO_MAX_WORKERS ? hp->n_workers : 0;
   zero_status s = build_step(hp, param, grads, N, wd.grad, st, t, &la, &empty, &a, &b);
   if (s != ZERO_OK || empty) return s == ZERO_OK ? ok() : s;
+  const char* err = launch_pieces(la, wd, wd.grad, false, stream);
+  if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
+  return ok();
+}
+
+zero_status zero_step_with_mean(const zero_hparams* hp, void* param, const void* const* grads,
+                                const zero_states* st, int64_t t, void* mean_out, void* stream) {
+  zlaunch::StepArgs la;
+  bool empty = false;
+  int64_t a, b;
+  if (hp == nullptr) return fail(ZERO_EINVAL, "hparams is NULL");
+  Widths wd;
+  if (!mode_widths(hp->mode, &wd)) return fail(ZERO_EINVAL, "unknown mode %d", hp->mode);
+  const int N = hp->n_workers >= 1 && hp->n_workers <= ZERO_MAX_WORKERS ? hp->n_workers : 0;
+  zero_status s = build_step(hp, param, grads, N, wd.grad, st, t, &la, &empty, &a, &b);
+  if (s != ZERO_OK || empty) return s == ZERO_OK ? ok() : s;
+  if (mean_out == nullptr || !aligned(mean_out, 16))
+    return fail(ZERO_EINVAL, "mean_out must be non-NULL and 16-byte aligned");
+  const size_t mbytes = (size_t)(la.len * wd.state);
+  // the mean is one more written range: it must not overlap the other outputs,
+  // the gradients or the decay mask
+  if ((s = check_not_written(la, wd, mean_out, mbytes, "mean_out")) != ZERO_OK) return s;
+  const Range rm{(uintptr_t)mean_out, (uintptr_t)mean_out + (uintptr_t)mbytes, "mean_out"};
+  for (int k = 0; k < N; ++k) {
+    const Range g{(uintptr_t)grads[k], (uintptr_t)grads[k] + (uintptr_t)(la.len * wd.grad), "grad"};
+    if (overlaps(rm, g)) return fail(ZERO_EINVAL, "mean_out overlaps grads[%d]", k);
+  }
+  if (la.mask != nullptr) {
+    const Range mk{(uintptr_t)hp->wd_mask,
+                   (uintptr_t)hp->wd_mask + (uintptr_t)(((hp->n + 31) / 32) * 4), "wd_mask"};
+    if (overlaps(rm, mk)) return fail(ZERO_EINVAL, "mean_out overlaps wd_mask");
+  }
+  la.mean_out = mean_out;
   const char* err = launch_pieces(la, wd, wd.grad, false, stream);
   if (err) return fail(ZERO_EHIP, "step launch failed: %s", err);
   return ok();

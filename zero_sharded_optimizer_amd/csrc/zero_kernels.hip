@@ -510,12 +510,13 @@ __device__ __forceinline__ void load_states(typename M::S* __restrict__ w,
 // thread's groups may lie past the end (only in the last block of the grid);
 // otherwise no load is predicated, so the loads form one straight run with no
 // branches between them.
-template <class M, int NFIX, int CAP, int GS, int C, int OPT, bool PRE, bool GUARD>
+template <class M, int NFIX, int CAP, int GS, int C, int OPT, bool PRE, bool MEAN, bool GUARD>
 __device__ __forceinline__ void step_groups(
     const GradSet<CAP>& gs, int N, typename M::S* __restrict__ w, typename M::S* __restrict__ m,
-    typename M::S* __restrict__ v, typename M::P* __restrict__ out, int out_vec, int64_t g0,
-    int64_t ngroups, const Consts<typename M::S>& c, const uint32_t* __restrict__ mask,
-    int64_t mask_off, int decay_kind, bool clip, typename M::S coef) {
+    typename M::S* __restrict__ v, typename M::P* __restrict__ out, int out_vec,
+    typename M::S* __restrict__ mean_out, int64_t g0, int64_t ngroups,
+    const Consts<typename M::S>& c, const uint32_t* __restrict__ mask, int64_t mask_off,
+    int decay_kind, bool clip, typename M::S coef) {
   typedef typename M::S S;
   constexpr int VEC = M::VEC;
   bool live[C];
@@ -574,6 +575,12 @@ __device__ __forceinline__ void step_groups(
       if (use_m) StateIO<M>::load(m, g, mv[u]);
       if (OPT == 0) StateIO<M>::load(v, g, vv[u]);
     }
+    if constexpr (MEAN) {  // the averaged gradient, as the update below forms it
+      S gb[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) gb[e] = s[u][e] / c.nw;
+      StateIO<M>::store(mean_out, g, gb);
+    }
     uint32_t dbits = 0;
     if (decay_kind == 1) dbits = (1u << VEC) - 1u;
     else if (decay_kind == 2) dbits = decay_bits<VEC>(mask, mask_off + g * VEC);
@@ -600,11 +607,12 @@ __device__ __forceinline__ void step_groups(
 
 // The fused step. NFIX > 0: exactly NFIX workers; NFIX == 0: any N <= CAP,
 // loaded in batches of 8 workers. Each thread handles C groups of one tile.
-template <class M, int NFIX, int CAP, int BLOCK, int C, int OPT, bool PRE, bool WC>
+template <class M, int NFIX, int CAP, int BLOCK, int C, int OPT, bool PRE, bool WC, bool MEAN>
 __global__ void __launch_bounds__(BLOCK)
     zero_step_kernel(GradSet<CAP> gs, int nw, typename M::S* __restrict__ w,
                      typename M::S* __restrict__ m, typename M::S* __restrict__ v,
-                     typename M::P* __restrict__ out, int out_vec, int64_t len,
+                     typename M::P* __restrict__ out, int out_vec,
+                     typename M::S* __restrict__ mean_out, int64_t len,
                      Consts<typename M::S> c, const uint32_t* __restrict__ mask,
                      int64_t mask_off, int decay_kind, const double* __restrict__ clip_sumsq,
                      double max_norm, const zlaunch::DynScalars* __restrict__ dyn) {
@@ -624,13 +632,13 @@ __global__ void __launch_bounds__(BLOCK)
   const S coef = clip ? clip_coef<S>(clip_sumsq, max_norm) : S(1);
   const int N = NFIX > 0 ? NFIX : nw;
   if (g0 + (int64_t)(C - 1) * GS < ngroups)
-    step_groups<M, NFIX, CAP, GS, C, OPT, PRE, false>(gs, N, w, m, v, out, out_vec, g0,
-                                                         ngroups, c, mask, mask_off, decay_kind,
-                                                         clip, coef);
+    step_groups<M, NFIX, CAP, GS, C, OPT, PRE, MEAN, false>(gs, N, w, m, v, out, out_vec,
+                                                               mean_out, g0, ngroups, c, mask,
+                                                               mask_off, decay_kind, clip, coef);
   else if (g0 < ngroups)
-    step_groups<M, NFIX, CAP, GS, C, OPT, PRE, true>(gs, N, w, m, v, out, out_vec, g0,
-                                                        ngroups, c, mask, mask_off, decay_kind,
-                                                        clip, coef);
+    step_groups<M, NFIX, CAP, GS, C, OPT, PRE, MEAN, true>(gs, N, w, m, v, out, out_vec,
+                                                              mean_out, g0, ngroups, c, mask,
+                                                              mask_off, decay_kind, clip, coef);
 
   // leftover elements (fewer than VEC), one per thread of block 0
   const int64_t i = ngroups * VEC + threadIdx.x;
@@ -638,6 +646,7 @@ __global__ void __launch_bounds__(BLOCK)
     typedef typename M::G G;
     S sum = grad_elem(reinterpret_cast<const G*>(gs.p[0]), i);
     for (int k = 1; k < N; ++k) sum = sum + grad_elem(reinterpret_cast<const G*>(gs.p[k]), i);
+    if constexpr (MEAN) mean_out[i] = sum / c.nw;
     bool dec = decay_kind == 1;
     if (decay_kind == 2) {
       const int64_t bit = mask_off + i;
@@ -865,7 +874,7 @@ struct StepShape<ModeF32, 0> {
 
 // Launches the step in the shape (BLOCK, C, PRE, WC): one tile of BLOCK * C
 // groups per block, and at least one block for the leftover elements.
-template <class M, int NFIX, int CAP, int BLOCK, int C, bool PRE, bool WC>
+template <class M, int NFIX, int CAP, int BLOCK, int C, bool PRE, bool WC, bool MEAN>
 void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP>& gs,
                    int out_vec) {
   typedef typename M::S S;
@@ -875,19 +884,19 @@ void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP
   int64_t blocks = (ngroups + per_block - 1) / per_block;
   if (blocks < 1) blocks = 1;
   if (a.optimizer == 0)
-    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0, PRE, WC>),
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0, PRE, WC, MEAN>),
                        dim3((unsigned)blocks), dim3(BLOCK), 0, st, gs, a.n_workers,
                        static_cast<S*>(a.w), static_cast<S*>(a.m), static_cast<S*>(a.v),
-                       static_cast<P*>(a.out), out_vec, a.len, round_consts<S>(a), a.mask,
-                       a.mask_bit_offset, a.decay_kind, a.clip_sumsq, a.max_norm,
-                       static_cast<const zlaunch::DynScalars*>(a.dyn));
+                       static_cast<P*>(a.out), out_vec, static_cast<S*>(a.mean_out), a.len,
+                       round_consts<S>(a), a.mask, a.mask_bit_offset, a.decay_kind,
+                       a.clip_sumsq, a.max_norm, static_cast<const zlaunch::DynScalars*>(a.dyn));
   else
-    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, PRE, WC>),
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, PRE, WC, MEAN>),
                        dim3((unsigned)blocks), dim3(BLOCK), 0, st, gs, a.n_workers,
                        static_cast<S*>(a.w), static_cast<S*>(a.m), static_cast<S*>(a.v),
-                       static_cast<P*>(a.out), out_vec, a.len, round_consts<S>(a), a.mask,
-                       a.mask_bit_offset, a.decay_kind, a.clip_sumsq, a.max_norm,
-                       static_cast<const zlaunch::DynScalars*>(a.dyn));
+                       static_cast<P*>(a.out), out_vec, static_cast<S*>(a.mean_out), a.len,
+                       round_consts<S>(a), a.mask, a.mask_bit_offset, a.decay_kind,
+                       a.clip_sumsq, a.max_norm, static_cast<const zlaunch::DynScalars*>(a.dyn));
 }
 
 // Small launches (a bucket of a few MiB) take 256 x 1 tiles when the mode's
@@ -896,8 +905,8 @@ void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP
 // 4.3 us against 5.8-6.3 us on MI355X). The arithmetic is the same.
 constexpr int kSmallBlock = 256;
 
-template <class M, int NFIX, int CAP>
-void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
+template <class M, int NFIX, int CAP, bool MEAN>
+void launch_mode_nm(const zlaunch::StepArgs& a, hipStream_t st) {
   typedef StepShape<M, NFIX> SH;
   GradSet<CAP> gs;
   for (int k = 0; k < CAP; ++k) gs.p[k] = k < a.n_workers ? a.grads[k] : nullptr;
@@ -907,11 +916,19 @@ void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
     const int64_t per_block = (int64_t)SH::BLOCK * SH::C;
     const int64_t blocks = (a.len / M::VEC + per_block - 1) / per_block;
     if (blocks < 2 * (int64_t)device_cus()) {
-      launch_shaped<M, NFIX, CAP, kSmallBlock, 1, false, false>(a, st, gs, out_vec);
+      launch_shaped<M, NFIX, CAP, kSmallBlock, 1, false, false, MEAN>(a, st, gs, out_vec);
       return;
     }
   }
-  launch_shaped<M, NFIX, CAP, SH::BLOCK, SH::C, SH::PRE, SH::WC>(a, st, gs, out_vec);
+  launch_shaped<M, NFIX, CAP, SH::BLOCK, SH::C, SH::PRE, SH::WC, MEAN>(a, st, gs, out_vec);
+}
+
+// The step, with the averaged gradient also stored when a.mean_out is set (the
+// step from a materialised mean never stores it again).
+template <class M, int NFIX, int CAP>
+void launch_mode_n(const zlaunch::StepArgs& a, hipStream_t st) {
+  if (a.mean_out != nullptr) launch_mode_nm<M, NFIX, CAP, true>(a, st);
+  else launch_mode_nm<M, NFIX, CAP, false>(a, st);
 }
 
 template <class M>
@@ -1002,11 +1019,12 @@ const char* launch_step(const StepArgs& a, void* stream) {
 const char* launch_step_mean(const StepArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
+  if (a.mean_out != nullptr) return "the step from a materialised mean stores no mean";
   switch (a.mode) {
-    case 0: launch_mode_n<ModeF64, 1, 1>(a, st); break;
-    case 1: launch_mode_n<ModeF32, 1, 1>(a, st); break;
-    case 2: launch_mode_n<ModeMixedMean, 1, 1>(a, st); break;
-    case 3: launch_mode_n<ModeMixedF16Mean, 1, 1>(a, st); break;
+    case 0: launch_mode_nm<ModeF64, 1, 1, false>(a, st); break;
+    case 1: launch_mode_nm<ModeF32, 1, 1, false>(a, st); break;
+    case 2: launch_mode_nm<ModeMixedMean, 1, 1, false>(a, st); break;
+    case 3: launch_mode_nm<ModeMixedF16Mean, 1, 1, false>(a, st); break;
     default: return "unknown mode";
   }
   const hipError_t e = hipGetLastError();

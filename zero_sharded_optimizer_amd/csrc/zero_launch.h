@@ -27,6 +27,7 @@ struct StepArgs {
   void* m;         // S
   void* v;         // S
   void* out;       // gathered parameter slot (P) written from w, or nullptr (in place)
+  void* mean_out;  // the averaged gradient (S) of each element, or nullptr (not stored)
   int64_t len;     // elements this launch updates, at most kLaunchElems
   const uint32_t* mask;     // decay bitmask or nullptr
   int64_t mask_bit_offset;  // bit index of element 0
@@ -88,5 +89,6 @@ const char* launch_sumsq_finalize(const double* partials, int64_t count, double*
                                   void* stream);
 // Makes later work on `stream` wait for `event` (a hipEvent_t) to complete.
 const char* stream_wait(void* stream, void* event);
+
 
 }  // namespace zlaunch

@@ -15,8 +15,10 @@ step() runs one fused zero_step over all of it; step(max_norm=...) first clips
 the averaged gradient by its global norm (the same page, section "Going
 further": a sum of the chunks' squared norms before the update). The stage only
 changes the memory model (memory_bytes), as on the pages: sharding moves
-storage between ranks and leaves the arithmetic unchanged. averaged_grad()
-gives what stage 1 keeps in .grad after a step: the averaged full gradient.
+storage between ranks and leaves the arithmetic unchanged, except that stage 1
+keeps the averaged full gradient (what the pages leave in .grad): the step
+stores it in the same pass (zero_step_with_mean), and averaged_grad() returns
+it.
 
 This module is argument marshalling only: every step of the computation runs
 in libzero.so's HIP kernels.
@@ -45,13 +47,19 @@ class ZeroOptimizer:
         default inside the library; the keyword defaults here are torch's.
     decay: None (decay everything when weight_decay > 0) or one bool per
         parameter tensor (e.g. 2-D tensors only).
+    keep_averaged_grad: store the averaged gradient during each step (n more
+        values of the state dtype in memory, sizeof(state) more bytes per
+        parameter per step). None: on in stage 1, whose ranks keep the full
+        averaged gradient in .grad, off in stages 2 and 3, which keep only
+        their chunk of it.
     """
 
     def __init__(self, params: Sequence, n_workers: int, stage: int, precision: str = "fp32",
                  optimizer: str = "adamw", lr: float = 1e-3, betas=(0.9, 0.999),
                  eps: float = 1e-8, weight_decay: float = 0.0, momentum: float = 0.0,
                  dampening: float = 0.0, nesterov: bool = False,
-                 decay: Optional[Sequence[bool]] = None):
+                 decay: Optional[Sequence[bool]] = None,
+                 keep_averaged_grad: Optional[bool] = None):
         params = list(params)
         if stage not in (1, 2, 3):
             raise ValueError(f"stage must be 1, 2 or 3, got {stage}")
@@ -113,6 +121,10 @@ class ZeroOptimizer:
         self.t = 0
         self._clip_ws = None   # the clipped step's workspace, allocated on first use
         self._sumsq = None     # device double: the last clipped step's squared norm
+        keep = stage == 1 if keep_averaged_grad is None else bool(keep_averaged_grad)
+        # the averaged gradient of the last step (stage 1's .grad), or None
+        self._mean = torch.empty(n, dtype=sdt, device=dev) if keep else None
+        self._mean_valid = False
 
     # -- the training step ------------------------------------------------------
     def worker_grads(self, k: int) -> List:
@@ -129,6 +141,7 @@ class ZeroOptimizer:
     def zero_grad(self) -> None:
         for g in self.grads:
             g.zero_()
+        self._mean_valid = False
 
     def gather(self) -> None:
         """Stage 3's gather of the full parameters before forward. On one GPU every
@@ -139,18 +152,42 @@ class ZeroOptimizer:
         all-gather) over the workers' gradient buffers, enqueued on `stream`.
         With max_norm, the averaged gradient is first scaled by
         min(1, max_norm / (norm + 1e-6)), its global norm taken over every shard;
-        grad_norm() then returns that norm."""
-        self.t += 1
+        grad_norm() then returns that norm. With keep_averaged_grad, the
+        averaged gradient (before clipping) is stored as well. The step count
+        advances only when the call is accepted."""
+        t = self.t + 1
+        keep = self._mean is not None
+        self._mean_valid = False
         if max_norm is None:
-            z.zero_step(self.hp, self.flat, self.grads, self.states, self.t, stream=stream)
-            return
-        import torch
-        if self._clip_ws is None:
-            nbytes = z.zero_step_clipped_workspace_bytes(self.hp)
-            self._clip_ws = torch.empty(nbytes, dtype=torch.uint8, device=self.flat.device)
-            self._sumsq = torch.zeros(1, dtype=torch.float64, device=self.flat.device)
-        z.zero_step_clipped(self.hp, self.flat, self.grads, self.states, self.t, max_norm,
-                            self._clip_ws, sumsq_out=self._sumsq, stream=stream)
+            if keep:
+                z.zero_step_with_mean(self.hp, self.flat, self.grads, self.states, t, self._mean,
+                                      stream=stream)
+            else:
+                z.zero_step(self.hp, self.flat, self.grads, self.states, t, stream=stream)
+        else:
+            import torch
+            if self._sumsq is None:
+                self._sumsq = torch.zeros(1, dtype=torch.float64, device=self.flat.device)
+            if keep:
+                # the clipped step's own two launches, with the mean kept in place
+                # of the workspace: the mean and its squared norm, then the step
+                if self._clip_ws is None:
+                    nbytes = max(1, z.zero_mean_grad_workspace_bytes(self.hp))
+                    self._clip_ws = torch.empty(nbytes, dtype=torch.uint8,
+                                                device=self.flat.device)
+                z.zero_mean_grad(self.hp, self.grads, self._mean, self._sumsq, self._clip_ws,
+                                 stream=stream)
+                z.zero_step_mean(self.hp, self.flat, self._mean, self.states, t, self._sumsq,
+                                 max_norm, stream=stream)
+            else:
+                if self._clip_ws is None:
+                    nbytes = z.zero_step_clipped_workspace_bytes(self.hp)
+                    self._clip_ws = torch.empty(nbytes, dtype=torch.uint8,
+                                                device=self.flat.device)
+                z.zero_step_clipped(self.hp, self.flat, self.grads, self.states, t, max_norm,
+                                    self._clip_ws, sumsq_out=self._sumsq, stream=stream)
+        self.t = t
+        self._mean_valid = keep
 
     def buckets(self, bucket_bytes: int = 25 << 20) -> List:
         """(begin, end) buckets of about bucket_bytes of one worker's gradient
@@ -178,9 +215,11 @@ class ZeroOptimizer:
             pos = b
         if pos != self.n:
             raise ValueError("buckets must cover [0, n) exactly once")
-        self.t += 1
-        z.zero_step_buckets(self.hp, self.flat, self.grads, self.states, self.t, buckets,
+        t = self.t + 1
+        self._mean_valid = False
+        z.zero_step_buckets(self.hp, self.flat, self.grads, self.states, t, buckets,
                             events, stream=stream)
+        self.t = t
 
     def grad_norm(self) -> float:
         """The global norm of the averaged gradient of the last clipped step
@@ -190,10 +229,15 @@ class ZeroOptimizer:
         return float(self._sumsq.item()) ** 0.5
 
     def averaged_grad(self, stream=None):
-        """The averaged full gradient (1/N) sum_k g_k, as a new flat device tensor
-        of the state dtype: what stage 1 leaves in .grad until zero_grad(). The
-        same rank-order fold and division as the step, so it is bit-identical to
-        the gradient the step used."""
+        """The averaged full gradient (1/N) sum_k g_k as a flat device tensor of
+        the state dtype: what stage 1 leaves in .grad until zero_grad(). After a
+        step() with keep_averaged_grad, it is the buffer that step stored in the
+        same pass (valid until the next step or zero_grad()); otherwise a new
+        tensor from a separate pass over the workers' gradients
+        (zero_mean_grad). Both use the step's rank-order fold and division, so
+        either is bit-identical to the gradient the step used."""
+        if self._mean_valid:
+            return self._mean
         import torch
         mean = torch.empty(self.n, dtype=self.states.m.dtype, device=self.flat.device)
         z.zero_mean_grad(self.hp, self.grads, mean, stream=stream)
