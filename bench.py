@@ -25,7 +25,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = ("params updated/sec + achieved HBM GB/s (% of peak), fused ZeRO Adam step, 1 GPU")
-DEFAULT_WORKLOAD = "fp32-320M-n8"
+# one rank's real-shaped share of an 8B-model step: a 10^9-element shard, 8 bf16
+# gradient chunks, fp32 master/m/v, AdamW 0.1, bf16 write-back into the slot
+DEFAULT_WORKLOAD = "mixed-rank0-of-8B-n8"
+CPU_SAMPLE = 1 << 26  # elements of the workload the CPU oracle steps
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD's published figure
 KERNEL_SRC = os.path.join(ROOT, "zero_sharded_optimizer_amd", "csrc", "zero_kernels.hip")
 
@@ -68,16 +71,20 @@ def kernel_hash():
 
 
 def load_traffic(workload, algo_bytes):
-    """HBM bytes per launch measured by rocprofv3 counters, if a summary for
-    this workload was taken from the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    """HBM bytes per launch measured by rocprofv3 counters (two --pmc runs,
+    summarised in profiles/traffic_<workload>.json), if that summary was taken
+    from the current kernel source; else None. Returns (bytes, source): the
+    counters are not collected in the timed run itself."""
+    rel = os.path.join("profiles", f"traffic_{workload}.json")
+    path = os.path.join(ROOT, rel)
     if not os.path.exists(path):
-        return None
+        return None, None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_src_sha256_16") != kernel_hash():
-        return None
-    return d.get("bytes_per_launch")
+    if d.get("kernel_src_sha256_16") != kernel_hash() or not d.get("command"):
+        return None, None
+    return d.get("bytes_per_launch"), (f"{rel}: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE runs "
+                                       f"on kernel source {d['kernel_src_sha256_16']}")
 
 
 STEP_KERNEL = "zero_step_kernel"
@@ -101,7 +108,8 @@ def pmc_summary(workload, fetch_dir, write_dir, cmd):
     the plain 4 GiB device copy run in the same process (known bytes / counter).
     Writes profiles/traffic_<workload>.json and .md."""
     import statistics
-    wl = None
+    if not cmd.strip():
+        raise SystemExit("--pmc-summary needs --cmd: the exact rocprofv3 commands of both runs")
     from zero_sharded_optimizer_amd import synth
     wl = synth.WORKLOADS[workload]
     res = {}
@@ -145,6 +153,8 @@ def kt_summary(workload, kt_dir, cmd, variant=None, bench_json=None):
     run, whose HIP-event kernel time is set beside rocprofv3's average."""
     import csv
     import glob
+    if not cmd.strip():
+        raise SystemExit("--kt-summary needs --cmd: the exact rocprofv3 command of the run")
     f = glob.glob(os.path.join(kt_dir, "**", "*kernel_stats.csv"), recursive=True)[0]
     rows = list(csv.DictReader(open(f)))
     label = workload if not variant else f"{workload}_{variant}"
@@ -181,9 +191,12 @@ def kt_summary(workload, kt_dir, cmd, variant=None, bench_json=None):
     return path
 
 
-def cpu_baseline(wl, target_s=12.0, sample_n=1 << 22):
+def cpu_baseline(wl, target_s=12.0, sample_n=CPU_SAMPLE):
     """The CPU oracle (single-threaded, as it stands) on the first sample_n
-    elements of the same workload, stepped until about target_s seconds."""
+    elements of the same workload, stepped until about target_s seconds. A
+    rank-mode workload is sampled as a full-mode call over the same N, dtypes
+    and hyperparameters: per element the arithmetic is the same, and the
+    oracle's rank share would take the whole gathered vector."""
     import numpy as np
     import torch
     from oracle import Oracle
@@ -217,8 +230,10 @@ def cpu_baseline(wl, target_s=12.0, sample_n=1 << 22):
         if el >= target_s:
             break
     return {"value": n * steps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n} elements of the workload, {wl.n_workers} workers, {steps} "
-                      f"steps, single-threaded C++ oracle, {el:.1f} s"}
+            "sample": f"first {n} elements (2^{n.bit_length() - 1}) of the workload"
+                      f"{' as a full-mode call' if wl.rank >= 0 else ''}, {wl.n_workers} "
+                      f"workers, same dtypes and hyperparameters, {steps} steps, "
+                      f"single-threaded C++ oracle, {el:.1f} s"}
 
 
 def cpu_threads():
@@ -231,7 +246,7 @@ def cpu_threads():
     return max(1, min(16, n, int(os.environ.get("OMP_NUM_THREADS", n))))
 
 
-def cpu_baseline_threads(wl, target_s=8.0, sample_n=1 << 22):
+def cpu_baseline_threads(wl, target_s=8.0, sample_n=CPU_SAMPLE):
     """The same oracle, unchanged, on the same sample split into one slice per
     host thread (the step is elementwise, so the slices are independent; the
     oracle's C code runs without Python's lock). Elements stepped per second
@@ -407,6 +422,9 @@ def main():
                          "each step")
     ap.add_argument("--no-copy-ceiling", action="store_true",
                     help="skip the copy and streaming-ceiling measurements")
+    ap.add_argument("--no-stream-ceilings", action="store_true",
+                    help="keep the 4 GiB copy (it calibrates the --pmc counters) but skip the "
+                         "streaming-ceiling kernels")
     ap.add_argument("--clip", type=float, default=None, metavar="FRACTION",
                     help="time the clipped step (zero_step_clipped) with max_norm set to "
                          "FRACTION times the first step's global gradient norm")
@@ -543,13 +561,14 @@ def main():
     bpp = bytes_per_param(wl) if max_norm is None else bytes_per_param_clipped(wl)
     algo_bytes = bpp * L
     achieved = algo_bytes / (avg_ms * 1e-3) / 1e9
-    traffic = load_traffic(wl.name, algo_bytes) if max_norm is None and buckets is None else None
+    traffic, traffic_src = (load_traffic(wl.name, algo_bytes) if max_norm is None and
+                            buckets is None else (None, None))
     dtype = {0: "f64", 1: "f32", 2: "bf16+f32", 3: "f16+f32"}[wl.mode]
 
     del grads, param, st
     torch.cuda.empty_cache()
     copy_gbps = None if args.no_copy_ceiling else copy_ceiling()
-    ceil = None if args.no_copy_ceiling else stream_ceilings(wl)
+    ceil = None if args.no_copy_ceiling or args.no_stream_ceilings else stream_ceilings(wl)
     if ceil is not None and ceil["step_streams_GBps"]:
         ceil["step_frac_of_step_streams"] = achieved / ceil["step_streams_GBps"]
     cpu = None if args.no_cpu_baseline else cpu_baseline(wl)
@@ -586,7 +605,8 @@ def main():
         "copy_ceiling_GBps": copy_gbps,
         "stream_ceilings": ceil,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic},
+                     "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic,
+                     "traffic_source": traffic_src},
         "cpu_baseline": cpu,
         "cpu_baseline_threads": cpu_mt,
     }

@@ -37,6 +37,29 @@ def test_traffic_summaries_match_the_current_kernel_source(workload):
     assert 0.999 <= d["bytes_per_launch"] / algo <= 1.002
 
 
+def test_every_profile_summary_records_its_command():
+    """Every committed profile summary gives the full command that made it (the
+    rocprofv3 invocation, with the program after --), so each figure can be
+    re-taken; an empty command block fails."""
+    import re
+    d = os.path.join(ROOT, "profiles")
+    files = sorted(os.listdir(d))
+    assert files
+    for fn in files:
+        txt = open(os.path.join(d, fn)).read()
+        if fn.endswith(".json"):
+            cmd = json.loads(txt).get("command", "")
+        else:
+            blocks = re.findall(r"```\n(.*?)```", txt, flags=re.S)
+            assert blocks, f"{fn}: no command block"
+            cmd = blocks[0]
+        assert cmd.strip(), f"{fn}: empty command"
+        assert "rocprofv3" in cmd, f"{fn}: the command is not a rocprofv3 run"
+        for line in cmd.splitlines():
+            if line.lstrip().startswith("rocprofv3") or " rocprofv3 " in line:
+                assert " -- python" in line or " -- ./" in line, f"{fn}: {line}"
+
+
 @pytest.mark.gpu
 def test_bench_line_on_the_gpu():
     print("[case] bench.py --steps 3 --warmup 1 --no-copy-ceiling", flush=True)
@@ -52,14 +75,22 @@ def test_bench_line_on_the_gpu():
                 "roofline", "cpu_baseline"):
         assert key in d, key
     assert d["n_gpus"] == 1 and d["steps"] == 3 and d["warmup"] == 1
-    assert d["config"]["workload"] == "fp32-320M-n8" and "model" not in d["config"]
-    assert d["value"] > 0 and d["unit"] == "params/s" and d["dtype"] == "f32"
+    assert d["config"]["workload"] == "mixed-rank0-of-8B-n8" and "model" not in d["config"]
+    assert d["config"]["params_updated_per_step"] == 1_000_000_000
+    assert d["value"] > 0 and d["unit"] == "params/s" and d["dtype"] == "bf16+f32"
     r = d["roofline"]
     assert r["bound"] == "hbm" and r["peak"] == 8000.0 and r["unit"] == "GB/s"
     assert r["frac"] == pytest.approx(r["achieved"] / r["peak"])
-    assert r["traffic"] == pytest.approx(56 * 320_000_000, rel=2e-3)
+    wl = synth.WORKLOADS["mixed-rank0-of-8B-n8"]
+    if bench.load_traffic(wl.name, 42 * wl.length)[0] is None:
+        # no counter summary of the current kernel source: traffic is null
+        assert r["traffic"] is None and r["traffic_source"] is None
+    else:
+        assert r["traffic"] == pytest.approx(42 * 1_000_000_000, rel=2e-3)
+        assert r["traffic_source"].startswith("profiles/traffic_mixed-rank0-of-8B-n8.json")
     c = d["cpu_baseline"]
-    assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0 and c["sample"]
+    assert c["kind"] == "oracle" and c["cores"] == 1 and c["value"] > 0
+    assert c["sample"].startswith(f"first {1 << 26} elements (2^26)")
 
 
 @pytest.mark.gpu
@@ -70,9 +101,10 @@ def test_bench_line_on_the_gpu():
 def test_bench_variants_on_the_gpu(flags):
     """The variant runs behind the committed kernel-trace summaries still print
     one valid line (a few steps, no baselines or ceilings)."""
-    print(f"[case] bench.py {' '.join(flags)}", flush=True)
+    print(f"[case] bench.py --workload fp32-320M-n8 {' '.join(flags)}", flush=True)
     res = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "2",
-                          "--warmup", "1", "--no-cpu-baseline", "--no-copy-ceiling", *flags],
+                          "--warmup", "1", "--no-cpu-baseline", "--no-copy-ceiling",
+                          "--workload", "fp32-320M-n8", *flags],
                          capture_output=True, text=True, timeout=600, cwd=ROOT)
     assert res.returncode == 0, res.stderr[-3000:]
     lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
