@@ -299,6 +299,26 @@ zero_status zero_mean_grad(const zero_hparams* hp, const void* const* grads, voi
                            double* sumsq_out, void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * zero_mean_grad with no workspace argument. The squared norm's per-block
+ * partial sums go to a library-owned static device array of 16 MiB (2^21
+ * doubles) that each GPU the library runs on holds until the process ends; its
+ * device address is looked up on the first call on each device. The call
+ * allocates nothing and calls no allocating routine. Results are bit for bit
+ * those of zero_mean_grad. Every call on one GPU shares that GPU's array:
+ * calls with sumsq_out non-NULL that overlap in time on one GPU (on different
+ * streams, or captured into graphs replayed concurrently) race on it and must
+ * be ordered by the caller. The array needs no clearing: each call writes
+ * every partial it reads. Limit: the call's range may need at most 2^21
+ * partial sums, which is 2^33 elements in fp32 and the mixed modes and
+ * 2^30 + 1 in fp64; a larger range with sumsq_out non-NULL returns ZERO_EINVAL (use
+ * zero_mean_grad with a workspace). With sumsq_out NULL the scratch is not
+ * used and any size is accepted. Other errors as zero_mean_grad; ZERO_EHIP
+ * also if the scratch's address cannot be looked up. */
+zero_status zero_mean_grad_noalloc(const zero_hparams* hp, const void* const* grads,
+                                   void* mean_out, double* sumsq_out, void* stream);
+
 /* The step driven by a materialised mean gradient (mean_grad: the call's len
  * elements of S, 16-byte aligned, read-only), otherwise as zero_step. If
  * clip_sumsq is non-NULL it points to the global squared norm (device double,

@@ -56,6 +56,14 @@ const char* launch_sumsq_finalize(const double* partials, int64_t count, double*
 }
 int64_t mean_partials(int, int64_t len) { return len / 1024 + 1; }
 const char* stream_wait(void*, void*) { ++g_launches; return nullptr; }
+// a stand-in address for the library's static device scratch
+constexpr uintptr_t kFakeScratch = (uintptr_t)0x7A << 40;
+static int g_scratch_lookups = 0;
+const char* scratch_address(void*, double** out) {
+  ++g_scratch_lookups;
+  *out = reinterpret_cast<double*>(kFakeScratch);
+  return nullptr;
+}
 }  // namespace zlaunch
 
 static int g_fail = 0;
@@ -272,6 +280,31 @@ int main() {
     CHECK(zero_mean_grad(&eh, nullptr, nullptr, (double*)(B + 2 * S), (void*)(B + 5 * S), 64,
                          nullptr) == ZERO_OK);
     CHECK(g_rec.size() == 2 && g_rec[0].len == 0 && g_rec[1].kind == 3 && g_rec[1].len == 1);
+    // the no-alloc mean: the partials go to the library's scratch, looked up only
+    // after validation; the same pieces and finalize as with a workspace
+    g_rec.clear();
+    zlaunch::g_scratch_lookups = 0;
+    zero_hparams nh = hp(1 << 20, 2, -1, ZERO_MODE_F32);  // the stub counts 1025 partials
+    CHECK(zero_mean_grad_noalloc(&nh, bg, (void*)(B + 1 * S), (double*)(B + 2 * S), nullptr) ==
+          ZERO_OK);
+    CHECK(zlaunch::g_scratch_lookups == 1 && g_rec.size() == 2);
+    if (g_rec.size() == 2) {
+      CHECK(g_rec[0].kind == 2 && g_rec[0].m == zlaunch::kFakeScratch && g_rec[0].len == 1 << 20);
+      CHECK(g_rec[1].kind == 3 && g_rec[1].w == zlaunch::kFakeScratch && g_rec[1].len == 1025 &&
+            g_rec[1].out == B + 2 * S);
+    }
+    // rejected calls look nothing up and launch nothing
+    g_rec.clear();
+    zlaunch::g_scratch_lookups = 0;
+    CHECK(zero_mean_grad_noalloc(&nh, bg, (void*)(B + 1 * S + 4), (double*)(B + 2 * S),
+                                 nullptr) == ZERO_EINVAL);
+    zero_hparams huge = hp(zlaunch::kScratchDoubles * 1024 * 2, 1, -1, ZERO_MODE_F32);
+    CHECK(zero_mean_grad_noalloc(&huge, bg, (void*)(B + 1 * S), (double*)(B + 2 * S),
+                                 nullptr) == ZERO_EINVAL);
+    CHECK(zlaunch::g_scratch_lookups == 0 && g_rec.empty());
+    // without a squared norm no scratch is needed, whatever the size
+    CHECK(zero_mean_grad_noalloc(&huge, bg, (void*)(B + 1 * S), nullptr, nullptr) == ZERO_OK);
+    CHECK(zlaunch::g_scratch_lookups == 0);
     // one piece when the call fits one launch
     zero_hparams oh = hp(L, 2, -1, ZERO_MODE_F32);
     g_rec.clear();

@@ -545,3 +545,23 @@ def test_step_with_mean_rejects_before_any_launch():
     arr5 = (C.c_void_p * 5)(*[A + ((3 + k) << 24) for k in range(5)])
     assert lib.zero_step_with_mean(C.byref(hpe), A, arr5, C.byref(ste), 1, None,
                                    None) == z.ZERO_OK
+
+
+def test_noalloc_mean_grad_rejects_ranges_beyond_its_scratch():
+    """zero_mean_grad_noalloc's scratch holds 2^21 partial sums: 2^33 elements
+    in fp32 (2^30 + 1 in fp64, whose one leftover element block 0 takes). One
+    element more is rejected on the host, with a
+    message naming the limit, before any device call; without a squared norm
+    the scratch is not used and the limit does not apply (rejected here for
+    another reason, a misaligned mean, so nothing runs)."""
+    lib = _abi.load()
+    for mode, limit in ((z.ZERO_MODE_F32, 1 << 33), (z.ZERO_MODE_F64, (1 << 30) + 1),
+                        (z.ZERO_MODE_MIXED_BF16, 1 << 33)):
+        hp = _hp(n=limit + 1, n_workers=1, mode=mode)
+        arr = (C.c_void_p * 1)(1 << 45)
+        rc = lib.zero_mean_grad_noalloc(C.byref(hp), arr, 1 << 46, 1 << 47, None)
+        assert rc == z.ZERO_EINVAL
+        msg = lib.zero_last_error().decode()
+        assert "scratch" in msg and str(1 << 21) in msg, msg
+        rc = lib.zero_mean_grad_noalloc(C.byref(hp), arr, (1 << 46) + 4, None, None)
+        assert rc == z.ZERO_EINVAL and "mean_out" in lib.zero_last_error().decode()

@@ -24,6 +24,8 @@ workers sharing one GPU:
                                             its ready event (overlap with backward)
   zero_mean_grad(hp, grads, mean, sumsq)  -> the reduce-scatter mean, materialised,
                                             and its squared norm
+  zero_mean_grad_noalloc(hp, grads, mean, sumsq)
+                                         -> the same with no workspace (library scratch)
   zero_step_mean(hp, param, mean, states, t, clip_sumsq, max_norm)
                                          -> the step from a materialised mean,
                                             optionally clipped by the global norm
@@ -58,7 +60,7 @@ __all__ = ["HParams", "States", "ZeroError", "zero_init_states", "zero_step",
            "ZERO_MAX_WORKERS",
            "ZERO_OPT_ADAM", "ZERO_OPT_SGD", "zero_step_scalars", "zero_step_range_dev",
            "STEP_SCALARS_BYTES", "zero_min_stage", "ZERO_MODE_MIXED_F16",
-           "zero_step_buckets", "zero_step_with_mean"]
+           "zero_step_buckets", "zero_step_with_mean", "zero_mean_grad_noalloc"]
 
 
 class ZeroError(RuntimeError):
@@ -415,6 +417,31 @@ def zero_mean_grad(hp: HParams, grads: Sequence, mean_out, sumsq_out=None, works
     st = lib.zero_mean_grad(C.byref(c_hp), arr, _addr(mean_out), _addr(sumsq_out),
                             _addr(workspace), _nbytes(workspace),
                             _stream_handle(stream, mean_out if mean_out is not None else grads[0]))
+    if st != ZERO_OK:
+        _raise(st)
+
+
+def zero_mean_grad_noalloc(hp: HParams, grads: Sequence, mean_out, sumsq_out=None,
+                           stream=None) -> None:
+    """Enqueue zero_mean_grad with the squared norm's partial sums in the
+    library's static device scratch: no workspace, no allocation (see
+    zero_adam.h for the size limit and the sharing rule)."""
+    if hp.mode in _DTYPES and hp.n >= 1 and 1 <= hp.n_workers and -1 <= hp.rank < hp.n_workers:
+        _, g_dt, s_dt = _DTYPES[hp.mode]
+        a, b = _shard_len(hp)
+        if len(grads) != hp.n_workers:
+            raise ValueError(f"grads: {len(grads)} buffers for {hp.n_workers} workers")
+        for k, g in enumerate(grads):
+            _check_tensor(g, g_dt, b - a, f"grads[{k}]")
+        _check_tensor(mean_out, s_dt, b - a, "mean_out")
+        _check_double(sumsq_out, "sumsq_out")
+    _same_device(stream, grads, mean_out, sumsq_out)
+    lib = _abi.load()
+    c_hp = hp.to_c()
+    arr = (C.c_void_p * max(1, len(grads)))(*[_addr(g) for g in grads])
+    st = lib.zero_mean_grad_noalloc(C.byref(c_hp), arr, _addr(mean_out), _addr(sumsq_out),
+                                    _stream_handle(stream, mean_out if mean_out is not None
+                                                   else grads[0]))
     if st != ZERO_OK:
         _raise(st)
 

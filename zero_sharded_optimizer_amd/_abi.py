@@ -65,7 +65,7 @@ EXPORTED = ("zero_init_states", "zero_step", "zero_memory_bytes", "zero_shard_bo
             "zero_last_error", "zero_mean_grad_workspace_bytes", "zero_mean_grad",
             "zero_step_mean", "zero_step_clipped_workspace_bytes", "zero_step_clipped",
             "zero_step_range", "zero_step_scalars_fill", "zero_step_range_dev", "zero_min_stage",
-            "zero_step_buckets", "zero_step_with_mean")
+            "zero_step_buckets", "zero_step_with_mean", "zero_mean_grad_noalloc")
 
 _lib = None
 
@@ -121,6 +121,9 @@ def load(path=None):
     lib.zero_mean_grad.argtypes = [C.POINTER(zero_hparams), C.POINTER(C.c_void_p), C.c_void_p,
                                    C.c_void_p, C.c_void_p, C.c_size_t, C.c_void_p]
     lib.zero_mean_grad.restype = C.c_int
+    lib.zero_mean_grad_noalloc.argtypes = [C.POINTER(zero_hparams), C.POINTER(C.c_void_p),
+                                           C.c_void_p, C.c_void_p, C.c_void_p]
+    lib.zero_mean_grad_noalloc.restype = C.c_int
     lib.zero_step_mean.argtypes = [C.POINTER(zero_hparams), C.c_void_p, C.c_void_p,
                                    C.POINTER(zero_states), C.c_int64, C.c_void_p, C.c_double,
                                    C.c_void_p]

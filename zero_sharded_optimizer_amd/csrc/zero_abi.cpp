@@ -465,6 +465,79 @@ const char* launch_mean_pieces(const zlaunch::MeanArgs& ma, const Widths& wd, do
   return nullptr;
 }
 
+// zero_mean_grad and zero_mean_grad_noalloc: the partial sums of the squared
+// norm go to the caller's workspace, or (library_scratch) to the library's
+// static device scratch, whose address is looked up only after every argument
+// has been validated.
+zero_status mean_grad_impl(const zero_hparams* hp, const void* const* grads, void* mean_out,
+                           double* sumsq_out, void* workspace, size_t workspace_bytes,
+                           bool library_scratch, void* stream) {
+  Widths wd;
+  int64_t a = 0, b = 0;
+  zero_status s = check_hparams(hp, false, &wd, &a, &b);
+  if (s != ZERO_OK) return s;
+  const int64_t len = b - a;
+  const int N = hp->n_workers;
+  const int64_t count = partials_count(hp->mode, len);
+  const int64_t need = count * 8;
+  if (sumsq_out != nullptr) {
+    if (!aligned(sumsq_out, 8)) return fail(ZERO_EINVAL, "sumsq_out must be 8-byte aligned");
+    if (library_scratch) {
+      if (count > zlaunch::kScratchDoubles)
+        return fail(ZERO_EINVAL,
+                    "%lld elements need %lld partial sums of the squared norm; the library's "
+                    "scratch holds %lld (use zero_mean_grad with a workspace)",
+                    (long long)len, (long long)count, (long long)zlaunch::kScratchDoubles);
+    } else if (workspace == nullptr || !aligned(workspace, 16) ||
+               (int64_t)workspace_bytes < need) {
+      return fail(ZERO_EINVAL, "workspace must be 16-byte aligned and hold %lld bytes",
+                  (long long)need);
+    }
+  }
+  zlaunch::MeanArgs ma{};
+  ma.mode = hp->mode;
+  ma.n_workers = N;
+  ma.len = len;
+  ma.n_workers_value = (double)N;
+  if (len > 0) {
+    if (grads == nullptr) return fail(ZERO_EINVAL, "grads is NULL");
+    if (mean_out == nullptr || !aligned(mean_out, 16))
+      return fail(ZERO_EINVAL, "mean_out must be non-NULL and 16-byte aligned");
+    const Range rm{(uintptr_t)mean_out, (uintptr_t)mean_out + (uintptr_t)(len * wd.state), "mean_out"};
+    // the library's scratch is its own static allocation: it overlaps nothing
+    const bool ws_used = sumsq_out != nullptr && !library_scratch;
+    const Range rw{(uintptr_t)workspace,
+                   ws_used ? (uintptr_t)workspace + (uintptr_t)need : (uintptr_t)workspace,
+                   "workspace"};
+    const Range rs{(uintptr_t)sumsq_out, sumsq_out ? (uintptr_t)sumsq_out + 8 : 0, "sumsq_out"};
+    for (int k = 0; k < N; ++k) {
+      if (grads[k] == nullptr) return fail(ZERO_EINVAL, "grads[%d] is NULL", k);
+      if (!aligned(grads[k], 16)) return fail(ZERO_EINVAL, "grads[%d] must be 16-byte aligned", k);
+      const Range g{(uintptr_t)grads[k], (uintptr_t)grads[k] + (uintptr_t)(len * wd.grad), "grad"};
+      if (overlaps(rm, g) || overlaps(rw, g) || overlaps(rs, g))
+        return fail(ZERO_EINVAL, "an output overlaps grads[%d]", k);
+    }
+    if (overlaps(rm, rw) || overlaps(rm, rs) || overlaps(rw, rs))
+      return fail(ZERO_EINVAL, "mean_out, workspace and sumsq_out must not overlap");
+    ma.mean = mean_out;
+    for (int k = 0; k < N; ++k) ma.grads[k] = grads[k];
+  }
+  if (len == 0 && sumsq_out == nullptr) return ok();  // an empty shard: nothing to do
+  if (sumsq_out != nullptr) {
+    if (library_scratch) {
+      double* p = nullptr;
+      if (const char* err = zlaunch::scratch_address(stream, &p))
+        return fail(ZERO_EHIP, "scratch lookup failed: %s", err);
+      ma.partials = p;
+    } else {
+      ma.partials = static_cast<double*>(workspace);
+    }
+  }
+  const char* err = launch_mean_pieces(ma, wd, sumsq_out, stream);
+  if (err) return fail(ZERO_EHIP, "mean launch failed: %s", err);
+  return ok();
+}
+
 // Validation and launch arguments shared by zero_step_range and
 // zero_step_range_dev: the range [begin, end) of the call's index space as
 // offset views of the full-length buffers.
@@ -680,50 +753,12 @@ zero_status zero_mean_grad_workspace_bytes(const zero_hparams* hp, size_t* bytes
 zero_status zero_mean_grad(const zero_hparams* hp, const void* const* grads, void* mean_out,
                            double* sumsq_out, void* workspace, size_t workspace_bytes,
                            void* stream) {
-  Widths wd;
-  int64_t a = 0, b = 0;
-  zero_status s = check_hparams(hp, false, &wd, &a, &b);
-  if (s != ZERO_OK) return s;
-  const int64_t len = b - a;
-  const int N = hp->n_workers;
-  const int64_t need = partials_count(hp->mode, len) * 8;
-  if (sumsq_out != nullptr) {
-    if (!aligned(sumsq_out, 8)) return fail(ZERO_EINVAL, "sumsq_out must be 8-byte aligned");
-    if (workspace == nullptr || !aligned(workspace, 16) || (int64_t)workspace_bytes < need)
-      return fail(ZERO_EINVAL, "workspace must be 16-byte aligned and hold %lld bytes",
-                  (long long)need);
-  }
-  zlaunch::MeanArgs ma{};
-  ma.mode = hp->mode;
-  ma.n_workers = N;
-  ma.len = len;
-  ma.n_workers_value = (double)N;
-  ma.partials = sumsq_out ? static_cast<double*>(workspace) : nullptr;
-  if (len > 0) {
-    if (grads == nullptr) return fail(ZERO_EINVAL, "grads is NULL");
-    if (mean_out == nullptr || !aligned(mean_out, 16))
-      return fail(ZERO_EINVAL, "mean_out must be non-NULL and 16-byte aligned");
-    const Range rm{(uintptr_t)mean_out, (uintptr_t)mean_out + (uintptr_t)(len * wd.state), "mean_out"};
-    const Range rw{(uintptr_t)workspace,
-                   sumsq_out ? (uintptr_t)workspace + (uintptr_t)need : (uintptr_t)workspace,
-                   "workspace"};
-    const Range rs{(uintptr_t)sumsq_out, sumsq_out ? (uintptr_t)sumsq_out + 8 : 0, "sumsq_out"};
-    for (int k = 0; k < N; ++k) {
-      if (grads[k] == nullptr) return fail(ZERO_EINVAL, "grads[%d] is NULL", k);
-      if (!aligned(grads[k], 16)) return fail(ZERO_EINVAL, "grads[%d] must be 16-byte aligned", k);
-      const Range g{(uintptr_t)grads[k], (uintptr_t)grads[k] + (uintptr_t)(len * wd.grad), "grad"};
-      if (overlaps(rm, g) || overlaps(rw, g) || overlaps(rs, g))
-        return fail(ZERO_EINVAL, "an output overlaps grads[%d]", k);
-    }
-    if (overlaps(rm, rw) || overlaps(rm, rs) || overlaps(rw, rs))
-      return fail(ZERO_EINVAL, "mean_out, workspace and sumsq_out must not overlap");
-    ma.mean = mean_out;
-    for (int k = 0; k < N; ++k) ma.grads[k] = grads[k];
-  }
-  if (len == 0 && sumsq_out == nullptr) return ok();  // an empty shard: nothing to do
-  const char* err = launch_mean_pieces(ma, wd, sumsq_out, stream);
-  if (err) return fail(ZERO_EHIP, "mean launch failed: %s", err);
-  return ok();
+  return mean_grad_impl(hp, grads, mean_out, sumsq_out, workspace, workspace_bytes, false, stream);
+}
+
+zero_status zero_mean_grad_noalloc(const zero_hparams* hp, const void* const* grads,
+                                   void* mean_out, double* sumsq_out, void* stream) {
+  return mean_grad_impl(hp, grads, mean_out, sumsq_out, nullptr, 0, true, stream);
 }
 
 zero_status zero_step_mean(const zero_hparams* hp, void* param, const void* mean_grad,

@@ -32,6 +32,7 @@
 
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "zero_launch.h"
@@ -1000,7 +1001,42 @@ void launch_init_mode(const zlaunch::InitArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// Library-owned scratch for callers that cannot allocate device memory: the
+// squared norm's per-block partial sums of zero_mean_grad_noalloc. Each GPU the
+// library runs on holds its own copy until the process ends. In host code the
+// name is only a stand-in for the device symbol: its device address is looked
+// up once per device (scratch_address) and that address is what kernels get.
+static __device__ __align__(256) double scratch[zlaunch::kScratchDoubles];
+
 namespace zlaunch {
+
+const char* scratch_address(void* stream, double** out) {
+  // The device the stream belongs to (the null stream: the current device).
+  int dev = -1;
+  hipError_t e = stream != nullptr ? hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev)
+                                   : hipGetDevice(&dev);
+  if (e != hipSuccess) return hipGetErrorString(e);
+  constexpr int kMaxDevices = 64;
+  if (dev < 0 || dev >= kMaxDevices) return "device ordinal outside the scratch table";
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    // with that device current, once per device
+    int cur = -1;
+    if ((e = hipGetDevice(&cur)) != hipSuccess) return hipGetErrorString(e);
+    if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess) return hipGetErrorString(e);
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return hipGetErrorString(e);
+    if (back != hipSuccess) return hipGetErrorString(back);
+    if (p == nullptr) return "hipGetSymbolAddress returned NULL for the scratch array";
+    addr[dev] = p;
+  }
+  *out = static_cast<double*>(addr[dev]);
+  return nullptr;
+}
 
 const char* launch_step(const StepArgs& a, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);

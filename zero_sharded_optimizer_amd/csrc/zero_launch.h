@@ -90,5 +90,11 @@ const char* launch_sumsq_finalize(const double* partials, int64_t count, double*
 // Makes later work on `stream` wait for `event` (a hipEvent_t) to complete.
 const char* stream_wait(void* stream, void* event);
 
+// Size, in doubles, of the library's static device scratch (16 MiB per GPU):
+// the largest count of block partial sums zero_mean_grad_noalloc accepts.
+constexpr int64_t kScratchDoubles = INT64_C(1) << 21;
+// *out = the device address of the scratch on the device `stream` belongs to
+// (looked up once per device). Returns nullptr on success, else the error.
+const char* scratch_address(void* stream, double** out);
 
 }  // namespace zlaunch
