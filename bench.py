@@ -58,6 +58,12 @@ def bytes_per_param_clipped(wl):
     return bytes_per_param(wl) + 2 * s
 
 
+def bytes_per_param_with_mean(wl):
+    """The step that also stores the averaged gradient (zero_step_with_mean):
+    the fused step's bytes plus one value of the state type written."""
+    return bytes_per_param(wl) + (8 if wl.mode == 0 else 4)
+
+
 def kernel_hash():
     """Hash of the kernel source's code: comments and whitespace removed, so a
     comment-only edit does not mark the measured traffic as stale."""
@@ -102,7 +108,7 @@ def _pmc_rows(d):
     return out
 
 
-def pmc_summary(workload, fetch_dir, write_dir, cmd):
+def pmc_summary(workload, fetch_dir, write_dir, cmd, variant=None):
     """HBM bytes per step launch from two rocprofv3 --pmc passes (FETCH_SIZE,
     WRITE_SIZE; KiB per dispatch). Each counter is scaled by what it reads for
     the plain 4 GiB device copy run in the same process (known bytes / counter).
@@ -124,24 +130,27 @@ def pmc_summary(workload, fetch_dir, write_dir, cmd):
                      "copy_kib_median": statistics.median(copy), "copy_dispatches": len(copy),
                      "factor": factor,
                      "step_bytes": statistics.mean(step) * 1024 * factor}
-    algo = bytes_per_param(wl) * wl.length
+    bpp = bytes_per_param_with_mean(wl) if variant == "mean" else bytes_per_param(wl)
+    algo = bpp * wl.length
     total = res["FETCH_SIZE"]["step_bytes"] + res["WRITE_SIZE"]["step_bytes"]
     out = {"workload": workload, "kernel": STEP_KERNEL, "kernel_src_sha256_16": kernel_hash(),
            "bytes_per_launch": total, "algorithmic_bytes_per_launch": algo,
-           "traffic_over_algorithmic": total / algo, "counters": res, "command": cmd}
+           "traffic_over_algorithmic": total / algo, "counters": res, "command": cmd,
+           **({"variant": variant} if variant else {})}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    base = os.path.join(ROOT, "profiles", f"traffic_{workload}")
+    label = workload if not variant else f"{workload}_{variant}"
+    base = os.path.join(ROOT, "profiles", f"traffic_{label}")
     with open(base + ".json", "w") as f:
         json.dump(out, f, indent=2)
     with open(base + ".md", "w") as f:
-        f.write(f"# HBM traffic of {STEP_KERNEL}, workload {workload}\n\n")
+        f.write(f"# HBM traffic of {STEP_KERNEL}, workload {label}\n\n")
         f.write(f"Commands (run from the repository root on one MI355X):\n\n```\n{cmd}\n```\n\n")
         f.write("| counter | step kernel, KiB/dispatch | dispatches | 4 GiB copy, KiB | factor | bytes/launch |\n|---|---|---|---|---|---|\n")
         for k, v in res.items():
             f.write(f"| {k} | {v['step_kib_mean']:.1f} | {v['step_dispatches']} | {v['copy_kib_median']:.1f} | "
                     f"{v['factor']:.4f} | {v['step_bytes']:.4e} |\n")
         f.write(f"\nTraffic {total:.4e} B per launch against {algo:.4e} algorithmic bytes "
-                f"({bytes_per_param(wl)} B/param x {wl.length} params): ratio "
+                f"({bpp} B/param x {wl.length} params): ratio "
                 f"{total / algo:.4f}.\n")
     return out
 
@@ -165,8 +174,9 @@ def kt_summary(workload, kt_dir, cmd, variant=None, bench_json=None):
         fh.write(f"Command (run from the repository root on one MI355X):\n\n```\n{cmd}\n```\n\n")
         fh.write("Template arguments of `zero_step_kernel`: mode, fixed worker count (0: any "
                  "N), gradient-pointer capacity, threads per block, groups per thread, "
-                 "optimizer (0 Adam, 1 SGD), state loads issued with the gradient loads, "
-                 "groups 64 apart (wave-contiguous).\n\n")
+                 "optimizer (0 Adam, 1 SGD), load issue (0: state loads after the fold, 1: with "
+                 "the gradient loads, 2: one stream in flight per wave), groups 64 apart "
+                 "(wave-contiguous), averaged gradient stored.\n\n")
         fh.write("| kernel | calls | average ns | min ns | max ns | % of GPU time |\n|---|---|---|---|---|---|\n")
         for r in rows:
             name = r["Name"].replace("(anonymous namespace)::", "")
@@ -323,7 +333,7 @@ def copy_ceiling(nbytes=4 << 30, reps=10):
 
 
 CEIL_SHAPES = ("512x2", "512x2 wave-contiguous", "256x4 wave-contiguous", "256x1",
-               "128x8 wave-contiguous")
+               "128x8 wave-contiguous", "64x2 one stream in flight")
 
 
 def _zceil():
@@ -407,6 +417,167 @@ def stream_ceilings(wl):
     return out
 
 
+def bucket_edges(length, bucket_mib, gbytes):
+    """(begin, end) buckets of about bucket_mib MiB of one worker's gradient,
+    last bucket first (the order a backward pass finishes them); every begin a
+    multiple of 8 elements."""
+    size = max(8, int(bucket_mib * (1 << 20)) // gbytes // 8 * 8)
+    edges = list(range(0, length, size)) + [length]
+    return list(reversed(list(zip(edges[:-1], edges[1:]))))
+
+
+def run_overlap(args, wl, hp, param, st, grads):
+    """The bucketed step overlapped with the production of its gradients.
+
+    A producer stream stands in for backward: for each bucket, last first, it
+    runs one bf16 GEMM of gemm x gemm x gemm (compute, as backward's matrix
+    products are), then writes that bucket of every worker's gradient (one
+    strided device copy from a source of the same values: the gradients are
+    the rows of one N x L tensor) and records an event. As a backward hook
+    would, the host enqueues each bucket's step (zero_step_buckets with that one
+    bucket and its event) right after the bucket's producer work, on the step
+    stream, which waits on the device. Timed against the same producer work
+    followed by the one-shot zero_step (serialised), and against each alone.
+    Every step first waits for the previous one, so the producer never
+    overwrites gradients a step is still reading."""
+    import torch
+    import zero_sharded_optimizer_amd as z
+    gbytes = {0: 8, 1: 4, 2: 2, 3: 2}[wl.mode]
+    a, b = wl.shard
+    L = b - a
+    buckets = bucket_edges(L, args.bucket_mib or 25.0, gbytes)
+    N = wl.n_workers
+    rows = torch.empty(N, L, dtype=grads[0].dtype, device="cuda")
+    for k in range(N):
+        rows[k].copy_(grads[k])
+    grads[:] = [rows[k] for k in range(N)]  # the step reads the rows
+    torch.cuda.empty_cache()
+    src = rows.clone()
+    M = args.overlap_gemm
+    A = torch.randn(M, M, device="cuda").to(torch.bfloat16).contiguous() if M else None
+    B = torch.randn(M, M, device="cuda").to(torch.bfloat16).contiguous() if M else None
+    C = torch.empty(M, M, device="cuda", dtype=torch.bfloat16) if M else None
+    main_s = torch.cuda.current_stream()
+    prod = torch.cuda.Stream()
+
+    def produce_bucket(lo, hi):
+        with torch.cuda.stream(prod):
+            if M:
+                torch.matmul(A, B, out=C)
+            rows[:, lo:hi].copy_(src[:, lo:hi])
+
+    def overlapped(t):
+        prod.wait_stream(main_s)
+        for lo, hi in buckets:
+            produce_bucket(lo, hi)
+            ev = torch.cuda.Event()
+            ev.record(prod)
+            z.zero_step_buckets(hp, param, grads, st, t, [(lo, hi)], [ev], stream=main_s)
+
+    def serial(t):
+        prod.wait_stream(main_s)
+        for lo, hi in buckets:
+            produce_bucket(lo, hi)
+        main_s.wait_stream(prod)
+        z.zero_step(hp, param, grads, st, t, stream=main_s)
+
+    def producer_only(t):
+        prod.wait_stream(main_s)
+        for lo, hi in buckets:
+            produce_bucket(lo, hi)
+        main_s.wait_stream(prod)
+
+    def step_only(t):
+        z.zero_step(hp, param, grads, st, t, stream=main_s)
+
+    t = 0
+    res = {}
+    for name, fn in (("producer", producer_only), ("step", step_only), ("serial", serial),
+                     ("overlapped", overlapped)):
+        for _ in range(args.warmup):
+            t += 1
+            fn(t)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            t += 1
+            fn(t)
+        torch.cuda.synchronize()
+        res[name] = (time.perf_counter() - t0) * 1e3 / args.steps
+    hidden = (res["serial"] - res["overlapped"]) / res["step"]
+    return buckets, res, hidden
+
+
+def overlap_summary(workload, kt_dir, cmd, bench_json=None):
+    """From a rocprofv3 --kernel-trace run of bench.py --overlap: how much of
+    the step kernels' time ran while a producer kernel (GEMM or copy) was also
+    running, in the overlapped phase (the last zero_step_buckets launches).
+    Writes profiles/overlap_<workload>.md."""
+    import csv
+    import glob
+    if not cmd.strip():
+        raise SystemExit("--overlap-summary needs --cmd: the exact rocprofv3 command of the run")
+    f = glob.glob(os.path.join(kt_dir, "**", "*kernel_trace.csv"), recursive=True)[0]
+    rows = list(csv.DictReader(open(f)))
+    ks = sorted(((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"])
+                 for r in rows), key=lambda x: x[0])
+    steps = [k for k in ks if STEP_KERNEL in k[2]]
+    others = [k for k in ks if STEP_KERNEL not in k[2]]
+    with open(bench_json) as jf:
+        d = json.loads([ln for ln in jf.read().splitlines() if ln.startswith("{")][-1])
+    nb = d["config"]["buckets"]
+    per_phase = d["steps"] + d["warmup"]
+    # phases in order: producer (no step kernel), step (1 per step), serial (1 per
+    # step), overlapped (nb per step): the overlapped launches are the last ones
+    ovl = steps[-per_phase * nb:]
+    lo_t, hi_t = ovl[0][0], ovl[-1][1]
+    prod = [k for k in others if k[1] > lo_t and k[0] < hi_t]
+    busy = 0
+    overlap = 0
+    for s0, s1, _ in ovl:
+        busy += s1 - s0
+        cuts = sorted((max(s0, p0), min(s1, p1)) for p0, p1, _ in prod if p0 < s1 and p1 > s0)
+        cur_s = cur_e = None
+        for x0, x1 in cuts:  # union of the producer intervals inside this step kernel
+            if cur_e is None or x0 > cur_e:
+                if cur_e is not None:
+                    overlap += cur_e - cur_s
+                cur_s, cur_e = x0, x1
+            else:
+                cur_e = max(cur_e, x1)
+        if cur_e is not None:
+            overlap += cur_e - cur_s
+    path = os.path.join(ROOT, "profiles", f"overlap_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write(f"# Bucketed step overlapped with its gradient producer, workload {workload}\n\n")
+        fh.write(f"Command (run from the repository root on one MI355X):\n\n```\n{cmd}\n```\n\n")
+        ov = d["overlap"]
+        fh.write(f"{nb} buckets of {d['config']['bucket_mib']} MiB; producer per bucket: one bf16 "
+                 f"GEMM of {d['config']['overlap_gemm']}^3, then the bucket of every worker's "
+                 f"gradient written (one strided device copy); each bucket's step enqueued right "
+                 f"after, waiting on the device for the bucket's event.\n\n")
+        fh.write("| phase | ms per step (wall, the bench line) |\n|---|---|\n")
+        for k in ("producer", "step", "serial", "overlapped"):
+            fh.write(f"| {k} | {ov[k + '_ms']:.3f} |\n")
+        fh.write(f"\nHidden: (serial - overlapped) / step = {ov['hidden_fraction_of_step']:.3f} of "
+                 f"the step's time.\n\n")
+        fh.write(f"From the trace, overlapped phase: {len(ovl)} step-kernel launches over "
+                 f"{(hi_t - lo_t) / 1e6:.3f} ms, {busy / 1e6:.3f} ms of step-kernel time, of which "
+                 f"{overlap / 1e6:.3f} ms ({overlap / max(busy, 1):.3f}) ran while a producer "
+                 f"kernel was running ({len(prod)} producer kernels in the window).\n\n")
+        fh.write("The first 24 kernels of the last overlapped step, by start time (us from its "
+                 "first kernel; its producer starts once the previous step's last bucket has "
+                 "ended):\n\n| start | end | kernel |\n|---|---|---|\n")
+        t_begin = ovl[-nb - 1][1] if len(ovl) > nb else ovl[0][0]
+        win = [k for k in ks if k[0] >= t_begin][:24]
+        if win:
+            base = win[0][0]
+            for k0, k1, name in win:
+                short = name.replace("(anonymous namespace)::", "").split("(")[0][:90]
+                fh.write(f"| {(k0 - base) / 1e3:.1f} | {(k1 - base) / 1e3:.1f} | `{short}` |\n")
+    return path
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -431,6 +602,19 @@ def main():
     ap.add_argument("--bucket-mib", type=float, default=None, metavar="MIB",
                     help="time the bucketed step: zero_step_range over buckets of MIB MiB of "
                          "one worker's gradient, last bucket first")
+    ap.add_argument("--with-mean", action="store_true",
+                    help="time zero_step_with_mean: the step that also stores the averaged "
+                         "gradient (bytes model + sizeof(state) per parameter)")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time the bucketed step (zero_step_buckets, --bucket-mib, default 25) "
+                         "overlapped with a producer stream that writes each bucket's gradients, "
+                         "against producer then step serialised")
+    ap.add_argument("--overlap-gemm", type=int, default=4096, metavar="M",
+                    help="with --overlap: the producer's bf16 GEMM per bucket is M x M x M (0: "
+                         "gradient writes only)")
+    ap.add_argument("--overlap-summary", metavar="KT_DIR",
+                    help="summarise a rocprofv3 --kernel-trace run of --overlap (with "
+                         "--bench-json) into profiles/ and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarise two rocprofv3 --pmc runs into profiles/ and exit")
     ap.add_argument("--kt-summary", metavar="KT_DIR",
@@ -442,10 +626,13 @@ def main():
                     help="with --kt-summary: a suffix for the summary's name (e.g. clip)")
     args = ap.parse_args()
     if args.pmc_summary:
-        print(json.dumps(pmc_summary(args.workload, *args.pmc_summary, args.cmd)))
+        print(json.dumps(pmc_summary(args.workload, *args.pmc_summary, args.cmd, args.variant)))
         return
     if args.kt_summary:
         print(kt_summary(args.workload, args.kt_summary, args.cmd, args.variant, args.bench_json))
+        return
+    if args.overlap_summary:
+        print(overlap_summary(args.workload, args.overlap_summary, args.cmd, args.bench_json))
         return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (all logical workers live in one GPU's HBM); "
@@ -497,12 +684,40 @@ def main():
         del mean, ws
         ws = torch.empty(z.zero_step_clipped_workspace_bytes(hp), dtype=torch.uint8, device="cuda")
 
+    if args.overlap:
+        if args.clip is not None or args.graph:
+            print("--overlap takes neither --clip nor --graph", file=sys.stderr)
+            sys.exit(2)
+        buckets, ov, hidden = run_overlap(args, wl, hp, param, st, grads)
+        out = {
+            "metric": METRIC + " (bucketed, overlapped with the gradient producer)",
+            "value": L / (ov["overlapped"] * 1e-3), "unit": "params/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ov["overlapped"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": {0: "f64", 1: "f32", 2: "bf16+f32", 3: "f16+f32"}[wl.mode],
+            "data": "synthetic (seeded device-side draws; no dataset)",
+            "config": {"workload": wl.name, "params_updated_per_step": L,
+                       "n_workers": wl.n_workers, "bucket_mib": args.bucket_mib or 25.0,
+                       "buckets": len(buckets), "overlap_gemm": args.overlap_gemm,
+                       "parallelism": "1 GPU, N logical workers in one HBM"},
+            "overlap": {"producer_ms": ov["producer"], "step_ms": ov["step"],
+                        "serial_ms": ov["serial"], "overlapped_ms": ov["overlapped"],
+                        "hidden_fraction_of_step": hidden},
+        }
+        print(json.dumps(out), flush=True)
+        return
+
     buckets = None
     if args.bucket_mib is not None:
         gbytes = {0: 8, 1: 4, 2: 2, 3: 2}[wl.mode]
-        size = max(8, int(args.bucket_mib * (1 << 20)) // gbytes // 8 * 8)
-        edges = list(range(0, L, size)) + [L]
-        buckets = list(reversed(list(zip(edges[:-1], edges[1:]))))
+        buckets = bucket_edges(L, args.bucket_mib, gbytes)
+
+    mean_out = None
+    if args.with_mean:
+        if args.clip is not None or buckets is not None:
+            print("--with-mean takes neither --clip nor --bucket-mib", file=sys.stderr)
+            sys.exit(2)
+        mean_out = torch.empty(L, dtype=sdt, device="cuda")
 
     graph = None
     if args.graph:
@@ -534,6 +749,8 @@ def main():
         elif buckets is not None:
             for lo, hi in buckets:
                 z.zero_step_range(hp, param, grads, st, t, lo, hi, stream=stream)
+        elif mean_out is not None:
+            z.zero_step_with_mean(hp, param, grads, st, t, mean_out, stream=stream)
         elif max_norm is None:
             z.zero_step(hp, param, grads, st, t, stream=stream)
         else:
@@ -558,14 +775,23 @@ def main():
     kern_ms = [s.elapsed_time(e) for s, e in ev]
     avg_ms = sum(kern_ms) / len(kern_ms)
 
-    bpp = bytes_per_param(wl) if max_norm is None else bytes_per_param_clipped(wl)
+    if max_norm is not None:
+        bpp = bytes_per_param_clipped(wl)
+    elif mean_out is not None:
+        bpp = bytes_per_param_with_mean(wl)
+    else:
+        bpp = bytes_per_param(wl)
     algo_bytes = bpp * L
     achieved = algo_bytes / (avg_ms * 1e-3) / 1e9
-    traffic, traffic_src = (load_traffic(wl.name, algo_bytes) if max_norm is None and
-                            buckets is None else (None, None))
+    if max_norm is None and buckets is None:
+        traffic, traffic_src = load_traffic(wl.name + ("_mean" if mean_out is not None else ""),
+                                            algo_bytes)
+    else:
+        traffic, traffic_src = None, None
     dtype = {0: "f64", 1: "f32", 2: "bf16+f32", 3: "f16+f32"}[wl.mode]
 
-    del grads, param, st
+    with_mean = mean_out is not None
+    del grads, param, st, mean_out
     torch.cuda.empty_cache()
     copy_gbps = None if args.no_copy_ceiling else copy_ceiling()
     ceil = None if args.no_copy_ceiling or args.no_stream_ceilings else stream_ceilings(wl)
@@ -596,6 +822,7 @@ def main():
                    **({} if buckets is None else
                       {"bucket_mib": args.bucket_mib, "buckets": len(buckets)}),
                    **({"graph": True} if graph is not None else {}),
+                   **({"with_mean": True} if with_mean else {}),
                    **({"native_buckets": True} if buckets is not None and args.native_buckets
                       else {})},
         "achieved_GBps": achieved,

@@ -37,6 +37,20 @@ def test_traffic_summaries_match_the_current_kernel_source(workload):
     assert 0.999 <= d["bytes_per_launch"] / algo <= 1.002
 
 
+def test_mean_store_traffic_is_one_more_state_value_per_parameter():
+    """The counters of zero_step_with_mean on the 8B-model rank share: the fused
+    step's 42 B/param plus one fp32 mean written, 46 B/param, on the current
+    kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic_mixed-rank0-of-8B-n8_mean.json")
+    assert os.path.exists(path), path
+    d = json.load(open(path))
+    assert d["kernel_src_sha256_16"] == bench.kernel_hash(), "re-take the counters"
+    wl = synth.WORKLOADS["mixed-rank0-of-8B-n8"]
+    assert bench.bytes_per_param_with_mean(wl) == 46
+    assert d["algorithmic_bytes_per_launch"] == pytest.approx(46 * wl.length)
+    assert 0.999 <= d["bytes_per_launch"] / (46 * wl.length) <= 1.002
+
+
 def test_every_profile_summary_records_its_command():
     """Every committed profile summary gives the full command that made it (the
     rocprofv3 invocation, with the program after --), so each figure can be
@@ -94,10 +108,31 @@ def test_bench_line_on_the_gpu():
 
 
 @pytest.mark.gpu
+def test_bench_overlap_line_on_the_gpu():
+    """--overlap prints one line whose phases are consistent: the serialised run
+    is at least as long as the producer and the step each, and the hidden
+    fraction is (serial - overlapped) / step."""
+    print("[case] bench.py --overlap on fp32-320M-n8", flush=True)
+    res = subprocess.run([sys.executable, "-u", os.path.join(ROOT, "bench.py"), "--steps", "3",
+                          "--warmup", "1", "--workload", "fp32-320M-n8", "--overlap",
+                          "--overlap-gemm", "1024"],
+                         capture_output=True, text=True, timeout=600, cwd=ROOT)
+    assert res.returncode == 0, res.stderr[-3000:]
+    lines = [ln for ln in res.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, lines
+    d = json.loads(lines[0])
+    ov = d["overlap"]
+    assert d["config"]["buckets"] > 1 and d["value"] > 0
+    assert ov["serial_ms"] >= 0.9 * max(ov["producer_ms"], ov["step_ms"])
+    assert ov["hidden_fraction_of_step"] == pytest.approx(
+        (ov["serial_ms"] - ov["overlapped_ms"]) / ov["step_ms"])
+
+
+@pytest.mark.gpu
 @pytest.mark.parametrize("flags", [["--clip", "0.5"], ["--bucket-mib", "25"],
                                    ["--bucket-mib", "25", "--native-buckets"],
-                                   ["--bucket-mib", "25", "--graph"]],
-                         ids=["clip", "buckets", "native-buckets", "graph"])
+                                   ["--bucket-mib", "25", "--graph"], ["--with-mean"]],
+                         ids=["clip", "buckets", "native-buckets", "graph", "with-mean"])
 def test_bench_variants_on_the_gpu(flags):
     """The variant runs behind the committed kernel-trace summaries still print
     one valid line (a few steps, no baselines or ceilings)."""
@@ -111,8 +146,11 @@ def test_bench_variants_on_the_gpu(flags):
     assert len(lines) == 1, lines
     d = json.loads(lines[0])
     assert d["value"] > 0 and d["roofline"]["achieved"] > 0
-    assert d["roofline"]["traffic"] is None  # counters exist for the one-shot step only
+    if "--with-mean" not in flags:
+        assert d["roofline"]["traffic"] is None  # no counters for these variants
     if "--clip" in flags:
         assert d["config"]["clipped"] is True
+    elif "--with-mean" in flags:
+        assert d["config"]["with_mean"] is True and d["config"]["bytes_per_param"] == 60
     else:
         assert d["config"]["bucket_mib"] == 25 and d["config"]["buckets"] > 1

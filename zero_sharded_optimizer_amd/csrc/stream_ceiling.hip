@@ -23,8 +23,9 @@ constexpr int kMaxIn = 16;       // streams held in registers all at once
 constexpr int kMaxWideIn = 128;  // streams loaded in batches of kBatch
 constexpr int kBatch = 8;
 constexpr int kMaxOut = 4;
-constexpr int kShapes = 5;  // shape 0: 512 x 2, 512 apart; 1: 512 x 2, 64 apart;
-                            // 2: 256 x 4, 64 apart; 3: 256 x 1; 4: 128 x 8, 64 apart
+constexpr int kShapes = 6;  // shape 0: 512 x 2, 512 apart; 1: 512 x 2, 64 apart;
+                            // 2: 256 x 4, 64 apart; 3: 256 x 1; 4: 128 x 8, 64 apart;
+                            // 5: 64 x 2, 64 apart, one stream in flight per wave
 
 struct Streams {
   const void* in[kMaxWideIn];
@@ -102,6 +103,65 @@ __global__ void __launch_bounds__(BLOCK)
   }
 }
 
+// A zero that exists only once `word` (just loaded) and the previous token have
+// arrived; adding it to the next load's index makes that load wait for this one.
+__device__ __forceinline__ uint32_t after(uint32_t word, uint32_t prev) {
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z) : "v"(word), "v"(prev));
+  return z;
+}
+
+// Shape 5, the fused step's issue mode for the mixed precisions: 64 threads x 2
+// groups 64 apart; the inputs are loaded one stream at a time, each stream's two
+// loads waiting for the previous stream's to return.
+template <int NOUT>
+__global__ void __launch_bounds__(64)
+    ceiling_serial_kernel(Streams s, int nin, uint32_t out_wide, int64_t ngroups) {
+  constexpr int C = 2;
+  const int64_t g0 = (int64_t)blockIdx.x * (64 * C) + threadIdx.x;
+  u32x4 acc[C];
+#pragma unroll
+  for (int u = 0; u < C; ++u) acc[u] = u32x4{0u, 0u, 0u, 0u};
+  uint32_t tok = 0;
+  for (int i = 0; i < nin; ++i) {
+    u32x4 r[C];
+#pragma unroll
+    for (int u = 0; u < C; ++u) {
+      const int64_t g = g0 + (int64_t)u * 64;
+      r[u] = g < ngroups ? load_group(s, i, g + tok) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < C; ++u) {
+      tok = after(r[u].x, tok);
+      acc[u] ^= r[u];
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < C; ++u) {
+    const int64_t g = g0 + (int64_t)u * 64;
+    if (g < ngroups) store_group<NOUT>(s, out_wide, g, acc[u]);
+  }
+}
+
+template <int NOUT>
+hipError_t launch_serial(const Streams& s, int nin, uint32_t ow, int64_t ngroups,
+                         hipStream_t st) {
+  const int64_t blocks = (ngroups + 127) / 128;
+  hipLaunchKernelGGL((ceiling_serial_kernel<NOUT>), dim3((unsigned)blocks), dim3(64), 0, st, s,
+                     nin, ow, ngroups);
+  return hipGetLastError();
+}
+
+hipError_t launch_serial_out(int nout, const Streams& s, int nin, uint32_t ow, int64_t ng,
+                             hipStream_t st) {
+  switch (nout) {
+    case 1: return launch_serial<1>(s, nin, ow, ng, st);
+    case 2: return launch_serial<2>(s, nin, ow, ng, st);
+    case 3: return launch_serial<3>(s, nin, ow, ng, st);
+    default: return launch_serial<4>(s, nin, ow, ng, st);
+  }
+}
+
 template <int NIN, int NOUT, int BLOCK, int C, bool WC>
 hipError_t launch(const Streams& s, int nin, uint32_t out_wide, int64_t ngroups, hipStream_t st) {
   const int64_t per_block = (int64_t)BLOCK * C;
@@ -157,9 +217,10 @@ extern "C" {
 // holds ngroups * in_width[i] bytes. Device pointers, aligned to their width;
 // 1 <= nin <= 128, 1 <= nout <= 4, ngroups >= 0; shape selects the launch
 // shape: 0 = 512 threads x 2 groups 512 apart, 1 = 512 x 2 groups 64 apart,
-// 2 = 256 x 4 groups 64 apart, 3 = 256 x 1, 4 = 128 x 8 groups 64 apart. Up
-// to 16 inputs (shapes 0-3) are loaded all at once; more, or shape 4, in
-// batches of 8. Launches on `stream` (a
+// 2 = 256 x 4 groups 64 apart, 3 = 256 x 1, 4 = 128 x 8 groups 64 apart,
+// 5 = 64 x 2 groups 64 apart with one input stream in flight per wave. Up to 16
+// inputs (shapes 0-3) are loaded all at once; more, or shape 4, in batches of
+// 8. Launches on `stream` (a
 // hipStream_t, or NULL) and returns at once. Returns 0, -1 for an invalid
 // argument (nothing launched), or -3 for a HIP launch error.
 int zceil_streams(const void* const* in, const int32_t* in_width, int32_t nin, void* const* out,
@@ -170,6 +231,7 @@ int zceil_streams(const void* const* in, const int32_t* in_width, int32_t nin, v
   if (shape < 0 || shape >= kShapes) return -1;
   if (ngroups == 0) return 0;
   if (ngroups > (int64_t)0x7FFFFFFF * 256) return -1;
+  if (shape == 5 && ngroups > (int64_t)0x7FFFFFFF) return -1;  // 64-thread blocks
   Streams s{};
   uint32_t ow = 0;
   for (int i = 0; i < nin; ++i) {
@@ -185,7 +247,8 @@ int zceil_streams(const void* const* in, const int32_t* in_width, int32_t nin, v
     if (out_width[o] == 16) ow |= 1u << o;
   }
   const hipError_t e =
-      launch_in<1>(nin, nout, shape, s, ow, ngroups, static_cast<hipStream_t>(stream));
+      shape == 5 ? launch_serial_out(nout, s, nin, ow, ngroups, static_cast<hipStream_t>(stream))
+                 : launch_in<1>(nin, nout, shape, s, ow, ngroups, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? 0 : -3;
 }
 

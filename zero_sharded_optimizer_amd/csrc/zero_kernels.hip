@@ -48,9 +48,9 @@ namespace {
 // so the window of in-flight requests sweeps each stream front to back. Within
 // the tile a thread takes C groups, BLOCK or 64 groups apart (WC below), so
 // every load instruction of a wave covers 512 B or 1 KiB of one stream. A
-// thread issues the gradient loads of all its C groups before it adds any.
-// Measured on MI355X, this beats a grid-stride persistent loop by about 25 % on
-// the many-stream mix of the step.
+// thread either issues all its loads before it adds any, or one stream at a
+// time (ISSUE below). Measured on MI355X, the tiled grid beats a grid-stride
+// persistent loop by about 25 % on the many-stream mix of the step.
 #ifndef ZERO_STEP_NT_LOAD
 #define ZERO_STEP_NT_LOAD 1
 #endif
@@ -60,19 +60,26 @@ namespace {
 // Any-N path (N not 1, 2, 4 or 8): gradient loads issued per batch (4, 8 and
 // 16 measured the same on MI355X).
 constexpr int kWideBatch = 8;
-// Launch shape per mode: BLOCK threads, C groups per thread, PRELOAD, WC;
-// overridable at build time for tuning. PRELOAD 1: a thread issues its state
-// loads together with its gradient loads, before it waits on any; 0: after the
-// gradients are folded. WC 1: the C groups of a thread are 64 groups apart, so
-// each wave covers C * 64 consecutive groups; 0: BLOCK groups apart. F32W is
-// the fp32 shape for any N (not 1, 2, 4 or 8). Chosen by interleaved sweeps on
-// MI355X (same process, same buffers):
-//   fp32, N = 8:       512 x 2, PRELOAD, strided groups (WC and 4 groups lose
-//                      up to 1 %; 1024 threads lose 5 %);
-//   mixed, N = 8:      512 x 2, PRELOAD, WC: 4 % over 256 x 1 (PRELOAD alone at
-//                      256 x 1 loses 6 %);
-//   fp32, N = 64:      128 x 8, WC, no PRELOAD: 3 % over 512 x 2 (314 registers,
+// Launch shape per mode: BLOCK threads, C groups per thread, ISSUE, WC;
+// overridable at build time for tuning. ISSUE 0: a thread issues its gradient
+// loads, folds them, then loads its state words; 1: the state loads go out
+// together with the gradient loads, before the thread waits on any; 2: every
+// load waits for the one before it (one stream in flight per wave; the many
+// small blocks provide the parallelism). WC 1: the C groups of a thread are 64
+// groups apart, so each wave covers C * 64 consecutive groups; 0: BLOCK groups
+// apart. F32W is the fp32 shape for any N (not 1, 2, 4 or 8). Chosen by
+// interleaved A/B runs on MI355X (same process, same buffers; placement moves
+// every shape by several percent between processes):
+//   mixed, N = 8:      64 x 2, ISSUE 2: 0 to 9 % over 512 x 2 with ISSUE 1 on
+//                      the 10^9-element rank share (0.74-0.77 of 8 TB/s against
+//                      0.70-0.78), equal on the 10^9-element full-mode vector;
+//                      64 x 1, 64 x 4, 128 x 2 and 256 x 2 with ISSUE 2 lose
+//                      1-3 %, 64 x 2 with ISSUE 1 loses 5 %;
+//   fp32, N = 8:       512 x 2, ISSUE 1, strided groups (ISSUE 2 shapes lose
+//                      1-2 %; WC and 4 groups lose up to 1 %; 1024 threads 5 %);
+//   fp32, N = 64:      128 x 8, WC, ISSUE 0: 3 % over 512 x 2 (314 registers,
 //                      one wave per SIMD, 64 loads of 1 KiB in flight per wave);
+//                      ISSUE 2 shapes lose 2-10 %;
 //   fp64 (1 M params): 256 x 1; launch-bound, every shape within noise.
 #ifndef ZERO_F64_BLOCK
 #define ZERO_F64_BLOCK 256
@@ -80,8 +87,8 @@ constexpr int kWideBatch = 8;
 #ifndef ZERO_F64_GROUPS
 #define ZERO_F64_GROUPS 1
 #endif
-#ifndef ZERO_F64_PRELOAD
-#define ZERO_F64_PRELOAD 0
+#ifndef ZERO_F64_ISSUE
+#define ZERO_F64_ISSUE 0
 #endif
 #ifndef ZERO_F64_WC
 #define ZERO_F64_WC 0
@@ -92,8 +99,8 @@ constexpr int kWideBatch = 8;
 #ifndef ZERO_F32_GROUPS
 #define ZERO_F32_GROUPS 2
 #endif
-#ifndef ZERO_F32_PRELOAD
-#define ZERO_F32_PRELOAD 1
+#ifndef ZERO_F32_ISSUE
+#define ZERO_F32_ISSUE 1
 #endif
 #ifndef ZERO_F32_WC
 #define ZERO_F32_WC 0
@@ -104,20 +111,20 @@ constexpr int kWideBatch = 8;
 #ifndef ZERO_F32W_GROUPS
 #define ZERO_F32W_GROUPS 8
 #endif
-#ifndef ZERO_F32W_PRELOAD
-#define ZERO_F32W_PRELOAD 0
+#ifndef ZERO_F32W_ISSUE
+#define ZERO_F32W_ISSUE 0
 #endif
 #ifndef ZERO_F32W_WC
 #define ZERO_F32W_WC 1
 #endif
 #ifndef ZERO_MIX_BLOCK
-#define ZERO_MIX_BLOCK 512
+#define ZERO_MIX_BLOCK 64
 #endif
 #ifndef ZERO_MIX_GROUPS
 #define ZERO_MIX_GROUPS 2
 #endif
-#ifndef ZERO_MIX_PRELOAD
-#define ZERO_MIX_PRELOAD 1
+#ifndef ZERO_MIX_ISSUE
+#define ZERO_MIX_ISSUE 2
 #endif
 #ifndef ZERO_MIX_WC
 #define ZERO_MIX_WC 1
@@ -145,6 +152,22 @@ __device__ __forceinline__ void st_stream(T* p, T v) {
 #else
   *p = v;
 #endif
+}
+
+// A zero that exists only once `word` (a value just loaded) has arrived, and
+// once the previous token `prev` has: adding it to the next load's index makes
+// that load wait for this one, in hardware (the asm reads the loaded register,
+// so the load must have returned) and in the compiler (the next address depends
+// on the asm's result, so no load can be moved above it). Used by the issue
+// mode that keeps one load in flight per wave.
+__device__ __forceinline__ uint32_t after(uint32_t word, uint32_t prev) {
+  uint32_t z;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(z) : "v"(word), "v"(prev));
+  return z;
+}
+__device__ __forceinline__ uint32_t first_word(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ uint32_t first_word(double x) {
+  return (uint32_t)__double_as_longlong(x);
 }
 
 template <int CAP>
@@ -242,6 +265,7 @@ struct GradRaw;
 template <>
 struct GradRaw<ModeF64> {
   f64x2 r;
+  __device__ __forceinline__ uint32_t word0() const { return first_word(r.x); }
   __device__ __forceinline__ void load(const void* base, int64_t g) {
     r = ld_stream(reinterpret_cast<const f64x2*>(base) + g);
   }
@@ -254,6 +278,7 @@ struct GradRaw<ModeF64> {
 template <>
 struct GradRaw<ModeF32> {
   f32x4 r;
+  __device__ __forceinline__ uint32_t word0() const { return first_word(r.x); }
   __device__ __forceinline__ void load(const void* base, int64_t g) {
     r = ld_stream(reinterpret_cast<const f32x4*>(base) + g);
   }
@@ -270,6 +295,7 @@ struct GradRaw<ModeF32> {
 template <>
 struct GradRaw<ModeMixed> {
   u32x2 r;
+  __device__ __forceinline__ uint32_t word0() const { return r.x; }
   __device__ __forceinline__ void load(const void* base, int64_t g) {
     r = ld_stream(reinterpret_cast<const u32x2*>(base) + g);
   }
@@ -290,6 +316,7 @@ struct GradRaw<ModeMixed> {
 template <>
 struct GradRaw<ModeMixedF16> {
   u32x2 r;
+  __device__ __forceinline__ uint32_t word0() const { return r.x; }
   __device__ __forceinline__ void load(const void* base, int64_t g) {
     r = ld_stream(reinterpret_cast<const u32x2*>(base) + g);
   }
@@ -505,13 +532,17 @@ __device__ __forceinline__ void load_states(typename M::S* __restrict__ w,
   }
 }
 
-// The C groups of one thread: the gradient loads of all groups are issued
-// first (with the state loads too when PRE), then the gradients are folded in
-// rank order, then each group is updated and stored. GUARD: some of the
-// thread's groups may lie past the end (only in the last block of the grid);
-// otherwise no load is predicated, so the loads form one straight run with no
-// branches between them.
-template <class M, int NFIX, int CAP, int GS, int C, int OPT, bool PRE, bool MEAN, bool GUARD>
+// The C groups of one thread. ISSUE 0 or 1: the gradient loads of all groups
+// are issued first (with the state loads too when ISSUE is 1), then the
+// gradients are folded in rank order, then each group is updated and stored.
+// ISSUE 2: every load is issued alone, after the previous one has returned:
+// worker 0's group, then worker 1's, ... (each added as it arrives), then the
+// master, m and v words. One load is in flight per wave, and the many waves of
+// a small-block launch provide the parallelism; the arithmetic and its order
+// are the same in every mode. GUARD: some of the thread's groups may lie past
+// the end (only in the last block of the grid); otherwise no load is
+// predicated.
+template <class M, int NFIX, int CAP, int GS, int C, int OPT, int ISSUE, bool MEAN, bool GUARD>
 __device__ __forceinline__ void step_groups(
     const GradSet<CAP>& gs, int N, typename M::S* __restrict__ w, typename M::S* __restrict__ m,
     typename M::S* __restrict__ v, typename M::P* __restrict__ out, int out_vec,
@@ -527,7 +558,52 @@ __device__ __forceinline__ void step_groups(
 
   S s[C][VEC];
   S wv[C][VEC], mv[C][VEC], vv[C][VEC];
-  if constexpr (NFIX > 0) {
+  constexpr bool PRE = ISSUE == 1;
+  if constexpr (ISSUE == 2) {
+    // each load's index carries the token of the load before it
+    uint32_t tok = 0;
+    {
+      GradRaw<M> raw[C];
+#pragma unroll
+      for (int u = 0; u < C; ++u)
+        if (live[u]) raw[u].load(gs.p[0], g0 + (int64_t)u * GS + tok);
+#pragma unroll
+      for (int u = 0; u < C; ++u) {
+        tok = after(raw[u].word0(), tok);
+        raw[u].widen(s[u]);
+      }
+    }
+    constexpr int kUnroll = NFIX > 0 ? NFIX : 1;
+#pragma unroll kUnroll
+    for (int k = 1; k < N; ++k) {
+      GradRaw<M> raw[C];
+#pragma unroll
+      for (int u = 0; u < C; ++u)
+        if (live[u]) raw[u].load(gs.p[k], g0 + (int64_t)u * GS + tok);
+#pragma unroll
+      for (int u = 0; u < C; ++u) {
+        tok = after(raw[u].word0(), tok);
+        raw[u].add(s[u]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < C; ++u)
+      if (live[u]) StateIO<M>::load(w, g0 + (int64_t)u * GS + tok, wv[u]);
+#pragma unroll
+    for (int u = 0; u < C; ++u) tok = after(first_word(wv[u][0]), tok);
+    if (use_m) {
+#pragma unroll
+      for (int u = 0; u < C; ++u)
+        if (live[u]) StateIO<M>::load(m, g0 + (int64_t)u * GS + tok, mv[u]);
+#pragma unroll
+      for (int u = 0; u < C; ++u) tok = after(first_word(mv[u][0]), tok);
+    }
+    if constexpr (OPT == 0) {
+#pragma unroll
+      for (int u = 0; u < C; ++u)
+        if (live[u]) StateIO<M>::load(v, g0 + (int64_t)u * GS + tok, vv[u]);
+    }
+  } else if constexpr (NFIX > 0) {
     GradRaw<M> raw[C][NFIX];
 #pragma unroll
     for (int u = 0; u < C; ++u)
@@ -571,7 +647,7 @@ __device__ __forceinline__ void step_groups(
   for (int u = 0; u < C; ++u) {
     if (!live[u]) continue;
     const int64_t g = g0 + (int64_t)u * GS;
-    if constexpr (!PRE) {
+    if constexpr (ISSUE == 0) {
       StateIO<M>::load(w, g, wv[u]);
       if (use_m) StateIO<M>::load(m, g, mv[u]);
       if (OPT == 0) StateIO<M>::load(v, g, vv[u]);
@@ -608,7 +684,7 @@ __device__ __forceinline__ void step_groups(
 
 // The fused step. NFIX > 0: exactly NFIX workers; NFIX == 0: any N <= CAP,
 // loaded in batches of 8 workers. Each thread handles C groups of one tile.
-template <class M, int NFIX, int CAP, int BLOCK, int C, int OPT, bool PRE, bool WC, bool MEAN>
+template <class M, int NFIX, int CAP, int BLOCK, int C, int OPT, int ISSUE, bool WC, bool MEAN>
 __global__ void __launch_bounds__(BLOCK)
     zero_step_kernel(GradSet<CAP> gs, int nw, typename M::S* __restrict__ w,
                      typename M::S* __restrict__ m, typename M::S* __restrict__ v,
@@ -633,11 +709,11 @@ __global__ void __launch_bounds__(BLOCK)
   const S coef = clip ? clip_coef<S>(clip_sumsq, max_norm) : S(1);
   const int N = NFIX > 0 ? NFIX : nw;
   if (g0 + (int64_t)(C - 1) * GS < ngroups)
-    step_groups<M, NFIX, CAP, GS, C, OPT, PRE, MEAN, false>(gs, N, w, m, v, out, out_vec,
+    step_groups<M, NFIX, CAP, GS, C, OPT, ISSUE, MEAN, false>(gs, N, w, m, v, out, out_vec,
                                                                mean_out, g0, ngroups, c, mask,
                                                                mask_off, decay_kind, clip, coef);
   else if (g0 < ngroups)
-    step_groups<M, NFIX, CAP, GS, C, OPT, PRE, MEAN, true>(gs, N, w, m, v, out, out_vec,
+    step_groups<M, NFIX, CAP, GS, C, OPT, ISSUE, MEAN, true>(gs, N, w, m, v, out, out_vec,
                                                               mean_out, g0, ngroups, c, mask,
                                                               mask_off, decay_kind, clip, coef);
 
@@ -850,17 +926,20 @@ struct Shape;
 template <>
 struct Shape<ModeF64> {
   static constexpr int BLOCK = ZERO_F64_BLOCK, C = ZERO_F64_GROUPS;
-  static constexpr bool PRE = ZERO_F64_PRELOAD, WC = ZERO_F64_WC;
+  static constexpr int ISSUE = ZERO_F64_ISSUE;
+  static constexpr bool WC = ZERO_F64_WC;
 };
 template <>
 struct Shape<ModeF32> {
   static constexpr int BLOCK = ZERO_F32_BLOCK, C = ZERO_F32_GROUPS;
-  static constexpr bool PRE = ZERO_F32_PRELOAD, WC = ZERO_F32_WC;
+  static constexpr int ISSUE = ZERO_F32_ISSUE;
+  static constexpr bool WC = ZERO_F32_WC;
 };
 template <>
 struct Shape<ModeMixed> {
   static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
-  static constexpr bool PRE = ZERO_MIX_PRELOAD, WC = ZERO_MIX_WC;
+  static constexpr int ISSUE = ZERO_MIX_ISSUE;
+  static constexpr bool WC = ZERO_MIX_WC;
 };
 template <>
 struct Shape<ModeMixedF16> : Shape<ModeMixed> {};
@@ -870,12 +949,13 @@ struct StepShape : Shape<M> {};
 template <>
 struct StepShape<ModeF32, 0> {
   static constexpr int BLOCK = ZERO_F32W_BLOCK, C = ZERO_F32W_GROUPS;
-  static constexpr bool PRE = ZERO_F32W_PRELOAD, WC = ZERO_F32W_WC;
+  static constexpr int ISSUE = ZERO_F32W_ISSUE;
+  static constexpr bool WC = ZERO_F32W_WC;
 };
 
-// Launches the step in the shape (BLOCK, C, PRE, WC): one tile of BLOCK * C
+// Launches the step in the shape (BLOCK, C, ISSUE, WC): one tile of BLOCK * C
 // groups per block, and at least one block for the leftover elements.
-template <class M, int NFIX, int CAP, int BLOCK, int C, bool PRE, bool WC, bool MEAN>
+template <class M, int NFIX, int CAP, int BLOCK, int C, int ISSUE, bool WC, bool MEAN>
 void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP>& gs,
                    int out_vec) {
   typedef typename M::S S;
@@ -885,14 +965,14 @@ void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP
   int64_t blocks = (ngroups + per_block - 1) / per_block;
   if (blocks < 1) blocks = 1;
   if (a.optimizer == 0)
-    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0, PRE, WC, MEAN>),
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0, ISSUE, WC, MEAN>),
                        dim3((unsigned)blocks), dim3(BLOCK), 0, st, gs, a.n_workers,
                        static_cast<S*>(a.w), static_cast<S*>(a.m), static_cast<S*>(a.v),
                        static_cast<P*>(a.out), out_vec, static_cast<S*>(a.mean_out), a.len,
                        round_consts<S>(a), a.mask, a.mask_bit_offset, a.decay_kind,
                        a.clip_sumsq, a.max_norm, static_cast<const zlaunch::DynScalars*>(a.dyn));
   else
-    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, PRE, WC, MEAN>),
+    hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, ISSUE, WC, MEAN>),
                        dim3((unsigned)blocks), dim3(BLOCK), 0, st, gs, a.n_workers,
                        static_cast<S*>(a.w), static_cast<S*>(a.m), static_cast<S*>(a.v),
                        static_cast<P*>(a.out), out_vec, static_cast<S*>(a.mean_out), a.len,
@@ -904,7 +984,14 @@ void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP
 // own shape would give fewer than two blocks per CU: the launch then spreads
 // over every CU instead of a quarter of them (1 MiB fp32 bucket, 8 workers:
 // 4.3 us against 5.8-6.3 us on MI355X). The arithmetic is the same.
-constexpr int kSmallBlock = 256;
+#ifndef ZERO_SMALL_BLOCK
+#define ZERO_SMALL_BLOCK 256
+#endif
+#ifndef ZERO_SMALL_ISSUE
+#define ZERO_SMALL_ISSUE 0
+#endif
+constexpr int kSmallBlock = ZERO_SMALL_BLOCK;
+constexpr int kSmallIssue = ZERO_SMALL_ISSUE;
 
 template <class M, int NFIX, int CAP, bool MEAN>
 void launch_mode_nm(const zlaunch::StepArgs& a, hipStream_t st) {
@@ -917,11 +1004,11 @@ void launch_mode_nm(const zlaunch::StepArgs& a, hipStream_t st) {
     const int64_t per_block = (int64_t)SH::BLOCK * SH::C;
     const int64_t blocks = (a.len / M::VEC + per_block - 1) / per_block;
     if (blocks < 2 * (int64_t)device_cus()) {
-      launch_shaped<M, NFIX, CAP, kSmallBlock, 1, false, false, MEAN>(a, st, gs, out_vec);
+      launch_shaped<M, NFIX, CAP, kSmallBlock, 1, kSmallIssue, false, MEAN>(a, st, gs, out_vec);
       return;
     }
   }
-  launch_shaped<M, NFIX, CAP, SH::BLOCK, SH::C, SH::PRE, SH::WC, MEAN>(a, st, gs, out_vec);
+  launch_shaped<M, NFIX, CAP, SH::BLOCK, SH::C, SH::ISSUE, SH::WC, MEAN>(a, st, gs, out_vec);
 }
 
 // The step, with the averaged gradient also stored when a.mean_out is set (the
@@ -949,14 +1036,27 @@ void launch_mode(const zlaunch::StepArgs& a, hipStream_t st) {
 template <>
 struct Shape<ModeMixedMean> {
   static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
-  static constexpr bool PRE = ZERO_MIX_PRELOAD, WC = ZERO_MIX_WC;
+  static constexpr int ISSUE = ZERO_MIX_ISSUE;
+  static constexpr bool WC = ZERO_MIX_WC;
 };
 template <>
 struct Shape<ModeMixedF16Mean> : Shape<ModeMixedMean> {};
 
+// The materialised mean's own launch shape (its block count is the number of
+// partial sums of the squared norm, which the workspace queries and the
+// library's static scratch are sized by): 512 x 2 groups, 256 x 1 in fp64.
+template <class M>
+struct MeanShape {
+  static constexpr int BLOCK = 512, C = 2;
+};
+template <>
+struct MeanShape<ModeF64> {
+  static constexpr int BLOCK = 256, C = 1;
+};
+
 template <class M>
 int64_t mean_blocks(int64_t len) {
-  const int64_t per_block = (int64_t)Shape<M>::BLOCK * Shape<M>::C;
+  const int64_t per_block = (int64_t)MeanShape<M>::BLOCK * MeanShape<M>::C;
   const int64_t b = (len / M::VEC + per_block - 1) / per_block;
   return b < 1 ? 1 : b;
 }
@@ -964,7 +1064,7 @@ int64_t mean_blocks(int64_t len) {
 template <class M, int NFIX, int CAP>
 void launch_mean_n(const zlaunch::MeanArgs& a, hipStream_t st) {
   typedef typename M::S S;
-  constexpr int BLOCK = Shape<M>::BLOCK, C = Shape<M>::C;
+  constexpr int BLOCK = MeanShape<M>::BLOCK, C = MeanShape<M>::C;
   const int64_t blocks = mean_blocks<M>(a.len);
   GradSet<CAP> gs;
   for (int k = 0; k < CAP; ++k) gs.p[k] = k < a.n_workers ? a.grads[k] : nullptr;
