@@ -333,7 +333,8 @@ def copy_ceiling(nbytes=4 << 30, reps=10):
 
 
 CEIL_SHAPES = ("512x2", "512x2 wave-contiguous", "256x4 wave-contiguous", "256x1",
-               "128x8 wave-contiguous", "64x2 one stream in flight")
+               "128x8 wave-contiguous", "64x2 one stream in flight",
+               "64x2 one stream in flight, 16 blocks per CU")
 
 
 def _zceil():

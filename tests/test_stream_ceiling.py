@@ -44,12 +44,12 @@ def test_exports_and_rejects_bad_arguments_before_any_launch():
     assert _call(lib, [fake[0] + 8], [16], fake[1:], [16], 10) == -1    # misaligned
     assert _call(lib, [0], [16], fake[1:], [16], 10) == -1              # NULL stream pointer
     assert _call(lib, fake[:1], [16], fake[1:], [16], -1) == -1         # negative size
-    assert _call(lib, fake[:1], [16], fake[1:], [16], 10, shape=6) == -1  # no such shape
+    assert _call(lib, fake[:1], [16], fake[1:], [16], 10, shape=7) == -1  # no such shape
     assert _call(lib, fake[:1], [16], fake[1:], [16], 0) == 0           # empty: nothing to do
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5])
+@pytest.mark.parametrize("shape", [0, 1, 2, 3, 4, 5, 6])
 @pytest.mark.parametrize("nin", [5, 21, 40])
 @pytest.mark.parametrize("ngroups", [1, 1023, 1024 * 3 + 517])
 def test_xor_of_the_inputs_reaches_every_output(ngroups, nin, shape):

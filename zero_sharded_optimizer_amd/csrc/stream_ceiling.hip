@@ -23,9 +23,10 @@ constexpr int kMaxIn = 16;       // streams held in registers all at once
 constexpr int kMaxWideIn = 128;  // streams loaded in batches of kBatch
 constexpr int kBatch = 8;
 constexpr int kMaxOut = 4;
-constexpr int kShapes = 6;  // shape 0: 512 x 2, 512 apart; 1: 512 x 2, 64 apart;
+constexpr int kShapes = 7;  // shape 0: 512 x 2, 512 apart; 1: 512 x 2, 64 apart;
                             // 2: 256 x 4, 64 apart; 3: 256 x 1; 4: 128 x 8, 64 apart;
-                            // 5: 64 x 2, 64 apart, one stream in flight per wave
+                            // 5: 64 x 2, 64 apart, one stream in flight per wave;
+                            // 6: shape 5 with at most 16 blocks per CU
 
 struct Streams {
   const void* in[kMaxWideIn];
@@ -143,22 +144,37 @@ __global__ void __launch_bounds__(64)
   }
 }
 
+// Dynamic LDS bytes that let at most `cu_blocks` blocks reside on a CU at once
+// (the kernel never touches LDS; 0 if the device does not report its LDS size).
+size_t cap_lds(int cu_blocks) {
+  int dev = 0, lds = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+          hipSuccess ||
+      lds <= 0)
+    return 0;
+  int bytes = lds / cu_blocks;
+  bytes -= bytes % 512;
+  if (bytes <= 0 || bytes > 65536 || (int64_t)bytes * (cu_blocks + 1) <= lds) return 0;
+  return (size_t)bytes;
+}
+
 template <int NOUT>
-hipError_t launch_serial(const Streams& s, int nin, uint32_t ow, int64_t ngroups,
+hipError_t launch_serial(const Streams& s, int nin, uint32_t ow, int64_t ngroups, size_t lds,
                          hipStream_t st) {
   const int64_t blocks = (ngroups + 127) / 128;
-  hipLaunchKernelGGL((ceiling_serial_kernel<NOUT>), dim3((unsigned)blocks), dim3(64), 0, st, s,
+  hipLaunchKernelGGL((ceiling_serial_kernel<NOUT>), dim3((unsigned)blocks), dim3(64), lds, st, s,
                      nin, ow, ngroups);
   return hipGetLastError();
 }
 
 hipError_t launch_serial_out(int nout, const Streams& s, int nin, uint32_t ow, int64_t ng,
-                             hipStream_t st) {
+                             size_t lds, hipStream_t st) {
   switch (nout) {
-    case 1: return launch_serial<1>(s, nin, ow, ng, st);
-    case 2: return launch_serial<2>(s, nin, ow, ng, st);
-    case 3: return launch_serial<3>(s, nin, ow, ng, st);
-    default: return launch_serial<4>(s, nin, ow, ng, st);
+    case 1: return launch_serial<1>(s, nin, ow, ng, lds, st);
+    case 2: return launch_serial<2>(s, nin, ow, ng, lds, st);
+    case 3: return launch_serial<3>(s, nin, ow, ng, lds, st);
+    default: return launch_serial<4>(s, nin, ow, ng, lds, st);
   }
 }
 
@@ -218,7 +234,9 @@ extern "C" {
 // 1 <= nin <= 128, 1 <= nout <= 4, ngroups >= 0; shape selects the launch
 // shape: 0 = 512 threads x 2 groups 512 apart, 1 = 512 x 2 groups 64 apart,
 // 2 = 256 x 4 groups 64 apart, 3 = 256 x 1, 4 = 128 x 8 groups 64 apart,
-// 5 = 64 x 2 groups 64 apart with one input stream in flight per wave. Up to 16
+// 5 = 64 x 2 groups 64 apart with one input stream in flight per wave, 6 = shape 5
+// with at most 16 blocks resident per CU (the fused step's mixed-precision
+// launch). Up to 16
 // inputs (shapes 0-3) are loaded all at once; more, or shape 4, in batches of
 // 8. Launches on `stream` (a
 // hipStream_t, or NULL) and returns at once. Returns 0, -1 for an invalid
@@ -231,7 +249,7 @@ int zceil_streams(const void* const* in, const int32_t* in_width, int32_t nin, v
   if (shape < 0 || shape >= kShapes) return -1;
   if (ngroups == 0) return 0;
   if (ngroups > (int64_t)0x7FFFFFFF * 256) return -1;
-  if (shape == 5 && ngroups > (int64_t)0x7FFFFFFF) return -1;  // 64-thread blocks
+  if (shape >= 5 && ngroups > (int64_t)0x7FFFFFFF) return -1;  // 64-thread blocks
   Streams s{};
   uint32_t ow = 0;
   for (int i = 0; i < nin; ++i) {
@@ -246,9 +264,10 @@ int zceil_streams(const void* const* in, const int32_t* in_width, int32_t nin, v
     s.out[o] = out[o];
     if (out_width[o] == 16) ow |= 1u << o;
   }
-  const hipError_t e =
-      shape == 5 ? launch_serial_out(nout, s, nin, ow, ngroups, static_cast<hipStream_t>(stream))
-                 : launch_in<1>(nin, nout, shape, s, ow, ngroups, static_cast<hipStream_t>(stream));
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  const hipError_t e = shape >= 5 ? launch_serial_out(nout, s, nin, ow, ngroups,
+                                                      shape == 6 ? cap_lds(16) : 0, st)
+                                  : launch_in<1>(nin, nout, shape, s, ow, ngroups, st);
   return e == hipSuccess ? 0 : -3;
 }
 

@@ -60,19 +60,26 @@ namespace {
 // Any-N path (N not 1, 2, 4 or 8): gradient loads issued per batch (4, 8 and
 // 16 measured the same on MI355X).
 constexpr int kWideBatch = 8;
-// Launch shape per mode: BLOCK threads, C groups per thread, ISSUE, WC;
-// overridable at build time for tuning. ISSUE 0: a thread issues its gradient
-// loads, folds them, then loads its state words; 1: the state loads go out
-// together with the gradient loads, before the thread waits on any; 2: every
-// load waits for the one before it (one stream in flight per wave; the many
-// small blocks provide the parallelism). WC 1: the C groups of a thread are 64
-// groups apart, so each wave covers C * 64 consecutive groups; 0: BLOCK groups
-// apart. F32W is the fp32 shape for any N (not 1, 2, 4 or 8). Chosen by
-// interleaved A/B runs on MI355X (same process, same buffers; placement moves
-// every shape by several percent between processes):
-//   mixed, N = 8:      64 x 2, ISSUE 2: 0 to 9 % over 512 x 2 with ISSUE 1 on
-//                      the 10^9-element rank share (0.74-0.77 of 8 TB/s against
-//                      0.70-0.78), equal on the 10^9-element full-mode vector;
+// Launch shape per mode: BLOCK threads, C groups per thread, ISSUE, WC, and
+// CU_BLOCKS; overridable at build time for tuning. ISSUE 0: a thread issues its
+// gradient loads, folds them, then loads its state words; 1: the state loads
+// go out together with the gradient loads, before the thread waits on any; 2:
+// every load waits for the one before it (one stream in flight per wave; the
+// many small blocks provide the parallelism). WC 1: the C groups of a thread
+// are 64 groups apart, so each wave covers C * 64 consecutive groups; 0: BLOCK
+// groups apart. CU_BLOCKS > 0: at most that many blocks reside on a CU at once
+// (a dynamic LDS allocation the kernel never touches enforces it), which sets
+// the loads in flight chip-wide (0: as many as registers allow). F32W is the
+// fp32 shape for any N (not 1, 2, 4 or 8). Chosen by interleaved A/B runs on
+// MI355X (same process, same buffers; placement moves every shape by several
+// percent between processes):
+//   mixed, N = 8:      64 x 2, ISSUE 2, 16 blocks per CU (4 waves per SIMD,
+//                      1 KiB of one stream in flight per wave): 2-4 % over
+//                      the same shape at its register-bound 5 waves, 10-12 %
+//                      over 8 waves; 14, 17, 18 and 20 blocks lose 0-1.5 %,
+//                      12 blocks (3 waves) 10 %, 8 blocks 25 %. Against
+//                      512 x 2 with ISSUE 1: 2-9 % on the 10^9-element rank
+//                      share (0.77-0.79 of 8 TB/s against 0.70-0.78);
 //                      64 x 1, 64 x 4, 128 x 2 and 256 x 2 with ISSUE 2 lose
 //                      1-3 %, 64 x 2 with ISSUE 1 loses 5 %;
 //   fp32, N = 8:       512 x 2, ISSUE 1, strided groups (ISSUE 2 shapes lose
@@ -129,6 +136,9 @@ constexpr int kWideBatch = 8;
 #ifndef ZERO_MIX_WC
 #define ZERO_MIX_WC 1
 #endif
+#ifndef ZERO_MIX_CU_BLOCKS
+#define ZERO_MIX_CU_BLOCKS 16
+#endif
 
 constexpr int kInitBlock = 256;
 
@@ -168,6 +178,17 @@ __device__ __forceinline__ uint32_t after(uint32_t word, uint32_t prev) {
 __device__ __forceinline__ uint32_t first_word(float x) { return __float_as_uint(x); }
 __device__ __forceinline__ uint32_t first_word(double x) {
   return (uint32_t)__double_as_longlong(x);
+}
+// A token that exists only once every element of x has been computed. Chaining
+// the next gradient load on the running sums (not on the raw loaded word) makes
+// each group's add happen as its load arrives, so the raw groups are not kept
+// in registers until the end of the fold.
+template <class T, int V>
+__device__ __forceinline__ uint32_t after_all(const T (&x)[V], uint32_t prev) {
+  uint32_t t = prev;
+#pragma unroll
+  for (int e = 0; e < V; ++e) t = after(first_word(x[e]), t);
+  return t;
 }
 
 template <int CAP>
@@ -569,8 +590,8 @@ __device__ __forceinline__ void step_groups(
         if (live[u]) raw[u].load(gs.p[0], g0 + (int64_t)u * GS + tok);
 #pragma unroll
       for (int u = 0; u < C; ++u) {
-        tok = after(raw[u].word0(), tok);
         raw[u].widen(s[u]);
+        tok = after_all(s[u], tok);
       }
     }
     constexpr int kUnroll = NFIX > 0 ? NFIX : 1;
@@ -582,8 +603,8 @@ __device__ __forceinline__ void step_groups(
         if (live[u]) raw[u].load(gs.p[k], g0 + (int64_t)u * GS + tok);
 #pragma unroll
       for (int u = 0; u < C; ++u) {
-        tok = after(raw[u].word0(), tok);
         raw[u].add(s[u]);
+        tok = after_all(s[u], tok);
       }
     }
 #pragma unroll
@@ -928,18 +949,21 @@ struct Shape<ModeF64> {
   static constexpr int BLOCK = ZERO_F64_BLOCK, C = ZERO_F64_GROUPS;
   static constexpr int ISSUE = ZERO_F64_ISSUE;
   static constexpr bool WC = ZERO_F64_WC;
+  static constexpr int CU_BLOCKS = 0;
 };
 template <>
 struct Shape<ModeF32> {
   static constexpr int BLOCK = ZERO_F32_BLOCK, C = ZERO_F32_GROUPS;
   static constexpr int ISSUE = ZERO_F32_ISSUE;
   static constexpr bool WC = ZERO_F32_WC;
+  static constexpr int CU_BLOCKS = 0;
 };
 template <>
 struct Shape<ModeMixed> {
   static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
   static constexpr int ISSUE = ZERO_MIX_ISSUE;
   static constexpr bool WC = ZERO_MIX_WC;
+  static constexpr int CU_BLOCKS = ZERO_MIX_CU_BLOCKS;
 };
 template <>
 struct Shape<ModeMixedF16> : Shape<ModeMixed> {};
@@ -951,11 +975,46 @@ struct StepShape<ModeF32, 0> {
   static constexpr int BLOCK = ZERO_F32W_BLOCK, C = ZERO_F32W_GROUPS;
   static constexpr int ISSUE = ZERO_F32W_ISSUE;
   static constexpr bool WC = ZERO_F32W_WC;
+  static constexpr int CU_BLOCKS = 0;
 };
 
+// LDS bytes per CU of the current device (one query per device, as device_cus).
+int device_lds_per_cu() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int lds = cached[dev].load(std::memory_order_relaxed);
+  if (lds == 0) {
+    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) !=
+            hipSuccess ||
+        lds <= 0)
+      lds = -1;
+    cached[dev].store(lds, std::memory_order_relaxed);
+  }
+  return lds > 0 ? lds : 0;
+}
+
+// Dynamic LDS bytes that let at most `cu_blocks` blocks of a launch reside on
+// one CU at a time (0: no cap). The step kernel does not touch LDS: the
+// allocation only limits how many blocks the hardware places on a CU, and so
+// how many loads are in flight chip-wide. Whole 512-byte granules; no cap if
+// the device does not report its LDS size or the bytes would pass the
+// per-block limit.
+size_t occupancy_cap_lds(int cu_blocks) {
+  if (cu_blocks <= 0) return 0;
+  const int lds = device_lds_per_cu();
+  if (lds <= 0) return 0;
+  int bytes = lds / cu_blocks;
+  bytes -= bytes % 512;
+  if (bytes <= 0 || bytes > 65536 || (int64_t)bytes * (cu_blocks + 1) <= lds) return 0;
+  return (size_t)bytes;
+}
+
 // Launches the step in the shape (BLOCK, C, ISSUE, WC): one tile of BLOCK * C
-// groups per block, and at least one block for the leftover elements.
-template <class M, int NFIX, int CAP, int BLOCK, int C, int ISSUE, bool WC, bool MEAN>
+// groups per block, and at least one block for the leftover elements; at most
+// CU_BLOCKS blocks per CU at a time when CU_BLOCKS > 0.
+template <class M, int NFIX, int CAP, int BLOCK, int C, int ISSUE, bool WC, bool MEAN,
+          int CU_BLOCKS>
 void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP>& gs,
                    int out_vec) {
   typedef typename M::S S;
@@ -964,16 +1023,17 @@ void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP
   const int64_t per_block = (int64_t)BLOCK * C;
   int64_t blocks = (ngroups + per_block - 1) / per_block;
   if (blocks < 1) blocks = 1;
+  const size_t lds = occupancy_cap_lds(CU_BLOCKS);
   if (a.optimizer == 0)
     hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 0, ISSUE, WC, MEAN>),
-                       dim3((unsigned)blocks), dim3(BLOCK), 0, st, gs, a.n_workers,
+                       dim3((unsigned)blocks), dim3(BLOCK), lds, st, gs, a.n_workers,
                        static_cast<S*>(a.w), static_cast<S*>(a.m), static_cast<S*>(a.v),
                        static_cast<P*>(a.out), out_vec, static_cast<S*>(a.mean_out), a.len,
                        round_consts<S>(a), a.mask, a.mask_bit_offset, a.decay_kind,
                        a.clip_sumsq, a.max_norm, static_cast<const zlaunch::DynScalars*>(a.dyn));
   else
     hipLaunchKernelGGL((zero_step_kernel<M, NFIX, CAP, BLOCK, C, 1, ISSUE, WC, MEAN>),
-                       dim3((unsigned)blocks), dim3(BLOCK), 0, st, gs, a.n_workers,
+                       dim3((unsigned)blocks), dim3(BLOCK), lds, st, gs, a.n_workers,
                        static_cast<S*>(a.w), static_cast<S*>(a.m), static_cast<S*>(a.v),
                        static_cast<P*>(a.out), out_vec, static_cast<S*>(a.mean_out), a.len,
                        round_consts<S>(a), a.mask, a.mask_bit_offset, a.decay_kind,
@@ -1004,11 +1064,13 @@ void launch_mode_nm(const zlaunch::StepArgs& a, hipStream_t st) {
     const int64_t per_block = (int64_t)SH::BLOCK * SH::C;
     const int64_t blocks = (a.len / M::VEC + per_block - 1) / per_block;
     if (blocks < 2 * (int64_t)device_cus()) {
-      launch_shaped<M, NFIX, CAP, kSmallBlock, 1, kSmallIssue, false, MEAN>(a, st, gs, out_vec);
+      launch_shaped<M, NFIX, CAP, kSmallBlock, 1, kSmallIssue, false, MEAN, 0>(a, st, gs,
+                                                                                out_vec);
       return;
     }
   }
-  launch_shaped<M, NFIX, CAP, SH::BLOCK, SH::C, SH::ISSUE, SH::WC, MEAN>(a, st, gs, out_vec);
+  launch_shaped<M, NFIX, CAP, SH::BLOCK, SH::C, SH::ISSUE, SH::WC, MEAN, SH::CU_BLOCKS>(
+      a, st, gs, out_vec);
 }
 
 // The step, with the averaged gradient also stored when a.mean_out is set (the
@@ -1038,6 +1100,7 @@ struct Shape<ModeMixedMean> {
   static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
   static constexpr int ISSUE = ZERO_MIX_ISSUE;
   static constexpr bool WC = ZERO_MIX_WC;
+  static constexpr int CU_BLOCKS = ZERO_MIX_CU_BLOCKS;
 };
 template <>
 struct Shape<ModeMixedF16Mean> : Shape<ModeMixedMean> {};
