@@ -60,7 +60,7 @@ namespace {
 // Any-N path (N not 1, 2, 4 or 8): gradient loads issued per batch (4, 8 and
 // 16 measured the same on MI355X).
 constexpr int kWideBatch = 8;
-// Launch shape per mode: BLOCK threads, C groups per thread, ISSUE, WC, and
+// Launch shapes per mode: BLOCK threads, C groups per thread, ISSUE, WC, and
 // CU_BLOCKS; overridable at build time for tuning. ISSUE 0: a thread issues its
 // gradient loads, folds them, then loads its state words; 1: the state loads
 // go out together with the gradient loads, before the thread waits on any; 2:
@@ -69,25 +69,37 @@ constexpr int kWideBatch = 8;
 // are 64 groups apart, so each wave covers C * 64 consecutive groups; 0: BLOCK
 // groups apart. CU_BLOCKS > 0: at most that many blocks reside on a CU at once
 // (a dynamic LDS allocation the kernel never touches enforces it), which sets
-// the loads in flight chip-wide (0: as many as registers allow). F32W is the
-// fp32 shape for any N (not 1, 2, 4 or 8). Chosen by interleaved A/B runs on
-// MI355X (same process, same buffers; placement moves every shape by several
-// percent between processes):
-//   mixed, N = 8:      64 x 2, ISSUE 2, 16 blocks per CU (4 waves per SIMD,
-//                      1 KiB of one stream in flight per wave): 2-4 % over
-//                      the same shape at its register-bound 5 waves, 10-12 %
-//                      over 8 waves; 14, 17, 18 and 20 blocks lose 0-1.5 %,
-//                      12 blocks (3 waves) 10 %, 8 blocks 25 %. Against
-//                      512 x 2 with ISSUE 1: 2-9 % on the 10^9-element rank
-//                      share (0.77-0.79 of 8 TB/s against 0.70-0.78);
-//                      64 x 1, 64 x 4, 128 x 2 and 256 x 2 with ISSUE 2 lose
-//                      1-3 %, 64 x 2 with ISSUE 1 loses 5 %;
-//   fp32, N = 8:       512 x 2, ISSUE 1, strided groups (ISSUE 2 shapes lose
-//                      1-2 %; WC and 4 groups lose up to 1 %; 1024 threads 5 %);
+// the loads in flight chip-wide (0: as many as registers allow). The fp32 and
+// mixed modes have a bulk shape (serial issue under a cap), used from ROUNDS
+// full rounds of resident blocks up, and a wide shape below that (a bucket of
+// a few MiB); F32W is the fp32 shape for any N (not 1, 2, 4 or 8). Chosen by
+// interleaved A/B runs on MI355X (same process, same buffers; placement moves
+// every shape by several percent between processes):
+//   mixed, N = 8:      bulk 64 x 2, ISSUE 2, 16 blocks per CU (4 waves per
+//                      SIMD, 1 KiB of one stream in flight per wave): 2-4 %
+//                      over the same shape at its register-bound 5 waves,
+//                      10-12 % over 8 waves; 14, 17, 18 and 20 blocks lose
+//                      0-1.5 %, 12 blocks (3 waves) 10 %, 8 blocks 25 %.
+//                      Against the wide 512 x 2 with ISSUE 1: 2-9 % on the
+//                      10^9-element rank share (0.77-0.79 of 8 TB/s against
+//                      0.70-0.78). 64 x 1, 64 x 4, 128 x 2 and 256 x 2 lose
+//                      1-3 %, 128 x 2 and 256 x 1 under the same 4-wave cap
+//                      4-5 %. Bulk from 6 rounds: below 4 rounds (buckets of
+//                      up to 4 M elements) the wide shape is 2-10 % faster,
+//                      from 4 to 8 rounds the two are within 1 %;
+//   fp32, N = 8:       bulk 64 x 2, ISSUE 2, 12 blocks per CU (3 waves per
+//                      SIMD, 2 KiB in flight per wave): 5-13 % over the wide
+//                      512 x 2, ISSUE 1, strided groups (0.79-0.80 of 8 TB/s
+//                      against 0.70-0.76 on 320 M elements); 10, 11, 13, 14,
+//                      16 and 20 blocks lose 1-5 %, 64 x 1 and 64 x 4 2-6 %.
+//                      Bulk from 8 rounds: below 4 rounds the wide shape is
+//                      2-13 % faster, from 4 to 8 rounds 1-4 % either way;
 //   fp32, N = 64:      128 x 8, WC, ISSUE 0: 3 % over 512 x 2 (314 registers,
 //                      one wave per SIMD, 64 loads of 1 KiB in flight per wave);
-//                      ISSUE 2 shapes lose 2-10 %;
+//                      ISSUE 2 shapes lose 2-10 % with or without a cap;
 //   fp64 (1 M params): 256 x 1; launch-bound, every shape within noise.
+// Tile order: running tile b on block b beat giving each XCD a contiguous
+// share of the tiles by 1-7 %.
 #ifndef ZERO_F64_BLOCK
 #define ZERO_F64_BLOCK 256
 #endif
@@ -101,16 +113,34 @@ constexpr int kWideBatch = 8;
 #define ZERO_F64_WC 0
 #endif
 #ifndef ZERO_F32_BLOCK
-#define ZERO_F32_BLOCK 512
+#define ZERO_F32_BLOCK 64
 #endif
 #ifndef ZERO_F32_GROUPS
 #define ZERO_F32_GROUPS 2
 #endif
 #ifndef ZERO_F32_ISSUE
-#define ZERO_F32_ISSUE 1
+#define ZERO_F32_ISSUE 2
 #endif
 #ifndef ZERO_F32_WC
-#define ZERO_F32_WC 0
+#define ZERO_F32_WC 1
+#endif
+#ifndef ZERO_F32_CU_BLOCKS
+#define ZERO_F32_CU_BLOCKS 12
+#endif
+#ifndef ZERO_F32_ROUNDS
+#define ZERO_F32_ROUNDS 8
+#endif
+#ifndef ZERO_F32_WIDE_BLOCK
+#define ZERO_F32_WIDE_BLOCK 512
+#endif
+#ifndef ZERO_F32_WIDE_GROUPS
+#define ZERO_F32_WIDE_GROUPS 2
+#endif
+#ifndef ZERO_F32_WIDE_ISSUE
+#define ZERO_F32_WIDE_ISSUE 1
+#endif
+#ifndef ZERO_F32_WIDE_WC
+#define ZERO_F32_WIDE_WC 0
 #endif
 #ifndef ZERO_F32W_BLOCK
 #define ZERO_F32W_BLOCK 128
@@ -138,6 +168,27 @@ constexpr int kWideBatch = 8;
 #endif
 #ifndef ZERO_MIX_CU_BLOCKS
 #define ZERO_MIX_CU_BLOCKS 16
+#endif
+#ifndef ZERO_MIX_ROUNDS
+#define ZERO_MIX_ROUNDS 6
+#endif
+#ifndef ZERO_MIX_WIDE_BLOCK
+#define ZERO_MIX_WIDE_BLOCK 512
+#endif
+#ifndef ZERO_MIX_WIDE_GROUPS
+#define ZERO_MIX_WIDE_GROUPS 2
+#endif
+#ifndef ZERO_MIX_WIDE_ISSUE
+#define ZERO_MIX_WIDE_ISSUE 1
+#endif
+#ifndef ZERO_MIX_WIDE_WC
+#define ZERO_MIX_WIDE_WC 1
+#endif
+#ifndef ZERO_MIXMEAN_CU_BLOCKS
+#define ZERO_MIXMEAN_CU_BLOCKS 12
+#endif
+#ifndef ZERO_MIXMEAN_ROUNDS
+#define ZERO_MIXMEAN_ROUNDS 8
 #endif
 
 constexpr int kInitBlock = 256;
@@ -942,40 +993,59 @@ Consts<S> round_consts(const zlaunch::StepArgs& a) {
   return c;
 }
 
+// A launch shape: BLOCK threads, C groups per thread, ISSUE, WC, CU_BLOCKS (as
+// in the shape table at the top of this file).
+template <int BLOCK_, int C_, int ISSUE_, bool WC_, int CU_BLOCKS_ = 0>
+struct LaunchShape {
+  static constexpr int BLOCK = BLOCK_, C = C_, ISSUE = ISSUE_, CU_BLOCKS = CU_BLOCKS_;
+  static constexpr bool WC = WC_;
+};
+// Per mode: the bulk shape, used when the launch has at least ROUNDS full
+// rounds of resident blocks (ROUNDS * CU_BLOCKS blocks per CU), and the wide
+// shape below that. A serial-issue bulk shape keeps few loads in flight per
+// wave and relies on many resident waves over many rounds: on a launch that
+// fills the chip only once or twice, the chain of dependent loads of each
+// wave is the critical path, and the wide shape (every load of a thread in
+// flight at once) is faster. A mode with no bulk shape has ROUNDS = 0 and the
+// same shape twice.
 template <class M>
 struct Shape;
 template <>
 struct Shape<ModeF64> {
-  static constexpr int BLOCK = ZERO_F64_BLOCK, C = ZERO_F64_GROUPS;
-  static constexpr int ISSUE = ZERO_F64_ISSUE;
-  static constexpr bool WC = ZERO_F64_WC;
-  static constexpr int CU_BLOCKS = 0;
+  typedef LaunchShape<ZERO_F64_BLOCK, ZERO_F64_GROUPS, ZERO_F64_ISSUE, ZERO_F64_WC> Bulk;
+  typedef Bulk Wide;
+  static constexpr int ROUNDS = 0;
 };
 template <>
 struct Shape<ModeF32> {
-  static constexpr int BLOCK = ZERO_F32_BLOCK, C = ZERO_F32_GROUPS;
-  static constexpr int ISSUE = ZERO_F32_ISSUE;
-  static constexpr bool WC = ZERO_F32_WC;
-  static constexpr int CU_BLOCKS = 0;
+  typedef LaunchShape<ZERO_F32_BLOCK, ZERO_F32_GROUPS, ZERO_F32_ISSUE, ZERO_F32_WC,
+                      ZERO_F32_CU_BLOCKS>
+      Bulk;
+  typedef LaunchShape<ZERO_F32_WIDE_BLOCK, ZERO_F32_WIDE_GROUPS, ZERO_F32_WIDE_ISSUE,
+                      ZERO_F32_WIDE_WC>
+      Wide;
+  static constexpr int ROUNDS = ZERO_F32_ROUNDS;
 };
 template <>
 struct Shape<ModeMixed> {
-  static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
-  static constexpr int ISSUE = ZERO_MIX_ISSUE;
-  static constexpr bool WC = ZERO_MIX_WC;
-  static constexpr int CU_BLOCKS = ZERO_MIX_CU_BLOCKS;
+  typedef LaunchShape<ZERO_MIX_BLOCK, ZERO_MIX_GROUPS, ZERO_MIX_ISSUE, ZERO_MIX_WC,
+                      ZERO_MIX_CU_BLOCKS>
+      Bulk;
+  typedef LaunchShape<ZERO_MIX_WIDE_BLOCK, ZERO_MIX_WIDE_GROUPS, ZERO_MIX_WIDE_ISSUE,
+                      ZERO_MIX_WIDE_WC>
+      Wide;
+  static constexpr int ROUNDS = ZERO_MIX_ROUNDS;
 };
 template <>
 struct Shape<ModeMixedF16> : Shape<ModeMixed> {};
-// the step kernel's shape for NFIX fixed workers (0: any N)
+// the step kernel's shapes for NFIX fixed workers (0: any N)
 template <class M, int NFIX>
 struct StepShape : Shape<M> {};
 template <>
 struct StepShape<ModeF32, 0> {
-  static constexpr int BLOCK = ZERO_F32W_BLOCK, C = ZERO_F32W_GROUPS;
-  static constexpr int ISSUE = ZERO_F32W_ISSUE;
-  static constexpr bool WC = ZERO_F32W_WC;
-  static constexpr int CU_BLOCKS = 0;
+  typedef LaunchShape<ZERO_F32W_BLOCK, ZERO_F32W_GROUPS, ZERO_F32W_ISSUE, ZERO_F32W_WC> Bulk;
+  typedef Bulk Wide;
+  static constexpr int ROUNDS = 0;
 };
 
 // LDS bytes per CU of the current device (one query per device, as device_cus).
@@ -1053,15 +1123,13 @@ void launch_shaped(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP
 constexpr int kSmallBlock = ZERO_SMALL_BLOCK;
 constexpr int kSmallIssue = ZERO_SMALL_ISSUE;
 
-template <class M, int NFIX, int CAP, bool MEAN>
-void launch_mode_nm(const zlaunch::StepArgs& a, hipStream_t st) {
-  typedef StepShape<M, NFIX> SH;
-  GradSet<CAP> gs;
-  for (int k = 0; k < CAP; ++k) gs.p[k] = k < a.n_workers ? a.grads[k] : nullptr;
-  const int out_vec =
-      a.out != nullptr && (reinterpret_cast<uintptr_t>(a.out) % OutIO<M>::kAlign == 0);
-  if constexpr (SH::BLOCK * SH::C > kSmallBlock) {
-    const int64_t per_block = (int64_t)SH::BLOCK * SH::C;
+// The wide shape W, or 256 x 1 tiles when W would give fewer than two blocks
+// per CU.
+template <class M, int NFIX, int CAP, bool MEAN, class W>
+void launch_wide(const zlaunch::StepArgs& a, hipStream_t st, const GradSet<CAP>& gs,
+                 int out_vec) {
+  if constexpr (W::BLOCK * W::C > kSmallBlock) {
+    const int64_t per_block = (int64_t)W::BLOCK * W::C;
     const int64_t blocks = (a.len / M::VEC + per_block - 1) / per_block;
     if (blocks < 2 * (int64_t)device_cus()) {
       launch_shaped<M, NFIX, CAP, kSmallBlock, 1, kSmallIssue, false, MEAN, 0>(a, st, gs,
@@ -1069,8 +1137,28 @@ void launch_mode_nm(const zlaunch::StepArgs& a, hipStream_t st) {
       return;
     }
   }
-  launch_shaped<M, NFIX, CAP, SH::BLOCK, SH::C, SH::ISSUE, SH::WC, MEAN, SH::CU_BLOCKS>(
-      a, st, gs, out_vec);
+  launch_shaped<M, NFIX, CAP, W::BLOCK, W::C, W::ISSUE, W::WC, MEAN, W::CU_BLOCKS>(a, st, gs,
+                                                                                    out_vec);
+}
+
+template <class M, int NFIX, int CAP, bool MEAN>
+void launch_mode_nm(const zlaunch::StepArgs& a, hipStream_t st) {
+  typedef StepShape<M, NFIX> SH;
+  typedef typename SH::Bulk B;
+  GradSet<CAP> gs;
+  for (int k = 0; k < CAP; ++k) gs.p[k] = k < a.n_workers ? a.grads[k] : nullptr;
+  const int out_vec =
+      a.out != nullptr && (reinterpret_cast<uintptr_t>(a.out) % OutIO<M>::kAlign == 0);
+  if constexpr (SH::ROUNDS > 0) {
+    const int64_t per_block = (int64_t)B::BLOCK * B::C;
+    const int64_t blocks = (a.len / M::VEC + per_block - 1) / per_block;
+    if (blocks >= (int64_t)SH::ROUNDS * B::CU_BLOCKS * device_cus()) {
+      launch_shaped<M, NFIX, CAP, B::BLOCK, B::C, B::ISSUE, B::WC, MEAN, B::CU_BLOCKS>(a, st, gs,
+                                                                                      out_vec);
+      return;
+    }
+  }
+  launch_wide<M, NFIX, CAP, MEAN, typename SH::Wide>(a, st, gs, out_vec);
 }
 
 // The step, with the averaged gradient also stored when a.mean_out is set (the
@@ -1095,12 +1183,15 @@ void launch_mode(const zlaunch::StepArgs& a, hipStream_t st) {
   }
 }
 
+// The step from a materialised fp32 mean reads only 16-byte groups, as the
+// fp32 step does, and takes the fp32 step's residency cap and rounds.
 template <>
 struct Shape<ModeMixedMean> {
-  static constexpr int BLOCK = ZERO_MIX_BLOCK, C = ZERO_MIX_GROUPS;
-  static constexpr int ISSUE = ZERO_MIX_ISSUE;
-  static constexpr bool WC = ZERO_MIX_WC;
-  static constexpr int CU_BLOCKS = ZERO_MIX_CU_BLOCKS;
+  typedef LaunchShape<ZERO_MIX_BLOCK, ZERO_MIX_GROUPS, ZERO_MIX_ISSUE, ZERO_MIX_WC,
+                      ZERO_MIXMEAN_CU_BLOCKS>
+      Bulk;
+  typedef Shape<ModeMixed>::Wide Wide;
+  static constexpr int ROUNDS = ZERO_MIXMEAN_ROUNDS;
 };
 template <>
 struct Shape<ModeMixedF16Mean> : Shape<ModeMixedMean> {};
