@@ -50,7 +50,7 @@ def _loss(model, x, y):
 
 
 @pytest.mark.parametrize("stage", [1, 2, 3])
-@pytest.mark.parametrize("N", [2, 4])
+@pytest.mark.parametrize("N", [2, 4, 5])
 def test_zero_matches_single_process(oracle, stage, N):
     """4 AdamW steps with decay on the 2-D weights only: the sharded optimizer's
     parameters equal one process's torch AdamW driven by the averaged gradient
@@ -89,6 +89,9 @@ def test_zero_matches_single_process(oracle, stage, N):
         p_o, _, m_o, v_o = oracle.zero_step(MODE_F64, p_before, grads, None, m_o, v_o, t, lr,
                                             betas[0], betas[1], eps, wd, flags)
         got = host(zo.flat)
+        if stage == 1:  # the averaged gradient kept by the step (N = 5: the split path)
+            mean_o, _ = oracle.mean_grad(MODE_F64, n, N, grads)
+            compare_bits("averaged grad", host(zo.averaged_grad()), mean_o, "exact")
         compare_bits("param", got, p_o, "exact")
         compare_bits("m", host(zo.states.m), m_o, "exact")
         compare_bits("v", host(zo.states.v), v_o, "exact")
