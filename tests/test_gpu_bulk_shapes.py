@@ -6,7 +6,9 @@ about 12.6 M elements up, the wide shape below. The other parity tests run
 either far below that (a few M elements, every element) or at full size
 (sampled). Here the bulk shape runs at sizes every element of which the oracle
 can check: 13 M elements plus a ragged tail, so the last tile is partial and a
-few elements sit past the last whole group. The same vector stepped as two
+few elements sit past the last whole group; AdamW with and without the decay
+bitmask, momentum SGD, a rank share, the mean store and the clipped step from
+the materialised mean. The same vector stepped as two
 buckets (each below the threshold, so in the wide shape) must match the
 one-shot bulk launch bit for bit.
 """
@@ -25,6 +27,7 @@ import zero_sharded_optimizer_amd as z  # noqa: E402
 from zero_sharded_optimizer_amd import synth  # noqa: E402
 from oracle import MODE_F32, MODE_MIXED, MODE_MIXED_F16  # noqa: E402
 from gpu_cases import check_all, compare_bits, host, kinds, run_full, say, setup  # noqa: E402
+from test_gpu_sgd import run_sgd  # noqa: E402
 
 W = synth.WORKLOADS
 BASE = {MODE_F32: W["fp32-320M-n8"], MODE_MIXED: W["mixed-1B-n8"],
@@ -42,6 +45,25 @@ def test_bulk_shape_rank_share(oracle):
     """Rank 3's share of 13 M elements: shard-local master/m/v, chunk gradients,
     the bf16 slot written at an unaligned offset of the gathered buffer."""
     run_full(oracle, synth.scaled(W["mixed-rank0-of-8B-n8"], 8 * N_BULK + 5, rank=3), steps=2)
+
+
+# a GPT-2-shaped tensor list of 13,962,240 elements: 2-D tensors decay, the rest not
+MASKED_SHAPES = synth.gpt2_small_shapes(vocab=20000, ctx=512, d=320, layers=6)
+
+
+@pytest.mark.parametrize("mode", [MODE_F32, MODE_MIXED])
+def test_bulk_shape_with_decay_mask(oracle, mode):
+    """AdamW with the 2-D decay bitmask read inside the bulk shape's serial loads."""
+    wl = synth.scaled(BASE[mode], 0, shapes=MASKED_SHAPES, decay="2d", weight_decay=0.1)
+    assert wl.n > N_BULK - 1_000_000
+    run_full(oracle, wl, steps=2)
+
+
+@pytest.mark.parametrize("mode", [MODE_F32, MODE_MIXED])
+def test_bulk_shape_momentum_sgd(oracle, mode):
+    """The SGD kernel variant (no v stream) in the bulk shape."""
+    run_sgd(oracle, synth.scaled(BASE[mode], N_BULK, decay="all", worker_scale=None),
+            "nesterov+decay", 3)
 
 
 @pytest.mark.parametrize("mode", [MODE_F32, MODE_MIXED])
