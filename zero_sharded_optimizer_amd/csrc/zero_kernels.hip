@@ -13,9 +13,11 @@
 // elementwise optimizer on a chunk reproduces the unsharded result for those
 // elements). So the
 // kernel streams the flat index space: each byte of every input is read from
-// HBM once and each output byte written once. No LDS, no atomics, no MFMA:
-// there is no contraction and no reuse, so the design is all about keeping
-// enough wide loads in flight per CU.
+// HBM once and each output byte written once. No atomics, no MFMA and no use of
+// LDS (on some shapes a dynamic LDS allocation that no thread touches caps the
+// blocks resident on a CU): there is no contraction and no reuse, so the design
+// is all about the amount of wide loads in flight per CU. Too few starve the
+// memory system; on this chip, too many slow it down.
 //
 // Layout: a group is the elements of one gradient stream that one thread
 // loads at once: 2 fp64, 4 fp32 (16 bytes) or 4 bf16 (8 bytes); the matching
