@@ -109,3 +109,32 @@ def test_noalloc_mean_grad_inside_a_captured_graph(oracle):
         torch.cuda.synchronize()
         assert torch.equal(mean.view(torch.int32), ref.view(torch.int32)), rep
         assert ss.item() == ss_ref.item(), rep
+
+
+def test_noalloc_clipped_step_composition(oracle):
+    """A caller that cannot allocate composes the clipped step from the
+    no-allocation mean (into its own mean buffer) and zero_step_mean; it must
+    equal zero_step_clipped (workspace) bit for bit, with clipping active."""
+    n, N = 700_001, 8
+    wl = synth.scaled(BASE[MODE_MIXED], n, n_workers=N, weight_decay=0.1, decay="all")
+    say("[case] clipped step from zero_mean_grad_noalloc + zero_step_mean")
+    from gpu_cases import setup
+    hp, p_a, s_a, _ = setup(wl)
+    _, p_b, s_b, _ = setup(wl)
+    mean = torch.empty(n, device="cuda")
+    ss_a = torch.zeros(1, dtype=torch.float64, device="cuda")
+    ss_b = torch.zeros(1, dtype=torch.float64, device="cuda")
+    ws = torch.empty(z.zero_step_clipped_workspace_bytes(hp), dtype=torch.uint8, device="cuda")
+    for t in (1, 2, 3):
+        grads = synth.make_grads(wl, t, "cuda")
+        _, ss_h = oracle.mean_grad(wl.mode, n, N, [host(g) for g in grads])
+        max_norm = 0.5 * math.sqrt(ss_h)
+        z.zero_mean_grad_noalloc(hp, grads, mean, ss_a)
+        z.zero_step_mean(hp, p_a, mean, s_a, t, ss_a, max_norm)
+        z.zero_step_clipped(hp, p_b, grads, s_b, t, max_norm, ws, sumsq_out=ss_b)
+    torch.cuda.synchronize()
+    assert ss_a.item() == ss_b.item()
+    for name, x, y in (("param", p_a, p_b), ("master", s_a.master, s_b.master), ("m", s_a.m, s_b.m),
+                       ("v", s_a.v, s_b.v)):
+        kind = "bf16" if x.dtype == torch.bfloat16 else "exact"
+        compare_bits(name, host(x), host(y), kind)
