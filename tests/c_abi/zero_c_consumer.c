@@ -16,7 +16,11 @@
  *                          and a clipped fp32 step (zero_step_clipped): its
  *                          squared norm within the summation-order bound of
  *                          the oracle's, and the step equal to the oracle's
- *                          step from the mean clipped by the device's norm.
+ *                          step from the mean clipped by the device's norm;
+ *                          then a bf16 step that stores the averaged gradient
+ *                          (zero_step_with_mean) and the no-allocation mean
+ *                          (zero_mean_grad_noalloc), bit for bit against the
+ *                          oracle's mean and step.
  * Exit status 0 when every check holds.
  */
 #include <hip/hip_runtime_api.h>
@@ -420,6 +424,105 @@ static void run_clipped(void) {
   free(dv);
 }
 
+/* The fused step that also stores the averaged gradient (bf16 mixed
+ * precision), and the no-allocation mean with its squared norm, each against
+ * the oracle: the stored mean and every state bit for bit, the norm within the
+ * summation-order bound. */
+static void run_with_mean_and_noalloc(void) {
+  const int mode = ZERO_MODE_MIXED_BF16, N = 4;
+  const int64_t n = 40009;
+  printf("[case] step with mean store and no-allocation mean: bf16 n %lld N %d\n", (long long)n,
+         N);
+  fflush(stdout);
+  uint16_t *p_h = malloc(n * 2), *g_h[4];
+  for (int64_t i = 0; i < n; ++i) p_h[i] = random_bf16(115, 124);
+  void *p_d, *ms_d, *m_d, *v_d, *g_d[4], *mean_d, *mean2_d;
+  double* ss_d;
+  for (int k = 0; k < N; ++k) {
+    g_h[k] = malloc(n * 2);
+    for (int64_t i = 0; i < n; ++i) g_h[k][i] = random_bf16(110, 121);
+    HIP(hipMalloc(&g_d[k], n * 2));
+    HIP(hipMemcpy(g_d[k], g_h[k], n * 2, hipMemcpyHostToDevice));
+  }
+  HIP(hipMalloc(&p_d, n * 2));
+  HIP(hipMalloc(&ms_d, n * 4));
+  HIP(hipMalloc(&m_d, n * 4));
+  HIP(hipMalloc(&v_d, n * 4));
+  HIP(hipMalloc(&mean_d, n * 4));
+  HIP(hipMalloc(&mean2_d, n * 4));
+  HIP(hipMalloc((void**)&ss_d, sizeof(double)));
+  HIP(hipMemcpy(p_d, p_h, n * 2, hipMemcpyHostToDevice));
+  zero_hparams hp;
+  memset(&hp, 0, sizeof hp);
+  hp.n = n;
+  hp.n_workers = N;
+  hp.rank = -1;
+  hp.mode = mode;
+  hp.lr = 1e-3;
+  hp.beta1 = 0.9;
+  hp.beta2 = 0.95;
+  hp.eps = 1e-8;
+  hp.weight_decay = 0.05;
+  zero_states st = {ms_d, m_d, v_d};
+  CHECK(zero_init_states(&hp, p_d, &st, NULL) == ZERO_OK);
+  const void* gp[4];
+  for (int k = 0; k < N; ++k) gp[k] = g_d[k];
+  CHECK(zero_step_with_mean(&hp, p_d, gp, &st, 1, mean_d, NULL) == ZERO_OK);
+  CHECK(zero_mean_grad_noalloc(&hp, gp, mean2_d, ss_d, NULL) == ZERO_OK);
+  HIP(hipDeviceSynchronize());
+  float *mean_o = malloc(n * 4), *oms = malloc(n * 4), *om = malloc(n * 4), *ov = malloc(n * 4);
+  float *nms = malloc(n * 4), *nm = malloc(n * 4), *nv = malloc(n * 4);
+  uint16_t* np_ = malloc(n * 2);
+  double ss_o = 0.0;
+  CHECK(orc_mean_grad(mode, n, N, -1, (const void* const*)g_h, mean_o, &ss_o) == 0);
+  orc_init_states(mode, n, p_h, oms, om, ov);
+  CHECK(orc_zero_step(mode, n, N, p_h, (const void* const*)g_h, oms, om, ov, np_, nms, nm, nv, 1,
+                      hp.lr, hp.beta1, hp.beta2, hp.eps, hp.weight_decay, NULL) == 0);
+  float *dmean = malloc(n * 4), *dmean2 = malloc(n * 4), *dms = malloc(n * 4);
+  float *dm = malloc(n * 4), *dv = malloc(n * 4);
+  uint16_t* dp = malloc(n * 2);
+  double ss_dev = 0.0;
+  HIP(hipMemcpy(dmean, mean_d, n * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(dmean2, mean2_d, n * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(dp, p_d, n * 2, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(dms, ms_d, n * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(dm, m_d, n * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(dv, v_d, n * 4, hipMemcpyDeviceToHost));
+  HIP(hipMemcpy(&ss_dev, ss_d, sizeof(double), hipMemcpyDeviceToHost));
+  CHECK(memcmp(dmean, mean_o, n * 4) == 0);
+  CHECK(memcmp(dmean2, mean_o, n * 4) == 0);
+  CHECK(fabs(ss_dev - ss_o) <= 2.0 * (double)n * ldexp(1.0, -53) * ss_o);
+  CHECK(compare("param", 2, dp, np_, n) == 0);
+  CHECK(memcmp(dms, nms, n * 4) == 0 && memcmp(dm, nm, n * 4) == 0 && memcmp(dv, nv, n * 4) == 0);
+  printf("  mean (stored and no-allocation), master, m and v bit-exact\n");
+  for (int k = 0; k < N; ++k) {
+    HIP(hipFree(g_d[k]));
+    free(g_h[k]);
+  }
+  HIP(hipFree(p_d));
+  HIP(hipFree(ms_d));
+  HIP(hipFree(m_d));
+  HIP(hipFree(v_d));
+  HIP(hipFree(mean_d));
+  HIP(hipFree(mean2_d));
+  HIP(hipFree(ss_d));
+  free(p_h);
+  free(mean_o);
+  free(oms);
+  free(om);
+  free(ov);
+  free(nms);
+  free(nm);
+  free(nv);
+  free(np_);
+  free(dmean);
+  free(dmean2);
+  free(dms);
+  free(dm);
+  free(dv);
+  free(dp);
+}
+
 int main(int argc, char** argv) {
   if (argc != 2 || (strcmp(argv[1], "host") != 0 && strcmp(argv[1], "gpu") != 0)) {
     fprintf(stderr, "usage: %s host|gpu\n", argv[0]);
@@ -432,6 +535,7 @@ int main(int argc, char** argv) {
   run_mode(ZERO_MODE_MIXED_F16, 30011, 5);
   run_buckets();
   run_clipped();
+  run_with_mean_and_noalloc();
   printf("gpu run: %d failures\n", g_fail);
   return g_fail == 0 ? 0 : 1;
 }

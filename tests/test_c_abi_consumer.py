@@ -2,7 +2,8 @@
 On the host it checks shard bounds, the memory model, rejection with a message
 and the step scalars; on the GPU it allocates with the HIP runtime, runs
 init_states and three fused steps in fp64, fp32 and mixed precision, then two
-bucketed steps released by events from a producer stream and one clipped step,
+bucketed steps released by events from a producer stream, one clipped step, and
+a step that stores the averaged gradient plus the no-allocation mean,
 and compares with the oracle library on the same inputs."""
 import os
 import subprocess
